@@ -1,0 +1,17 @@
+"""CPU oracle for the W4A16 verify linear -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never calls it and
+shares no code with it.
+"""
+from .w4a16_ref import (  # noqa: F401
+    CONTRACT_RTOL,
+    bf16_bits_to_f64,
+    check_contract,
+    dequant64,
+    linear64,
+    linear64_columns,
+    scales_to_f64,
+    unpack_qweight,
+    unpack_zeros,
+)
