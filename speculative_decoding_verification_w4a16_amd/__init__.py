@@ -1,0 +1,224 @@
+"""Python binding of libw4a16.so, the MI355X W4A16 verify-linear library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/w4a16.h``.  The functions
+here carry the C names, take torch tensors (device memory from PyTorch-ROCm)
+or raw integer addresses, pass the current HIP stream of the tensor's
+device, and raise ``W4Error`` on a nonzero status.  Importing the package
+fails loudly when the built library is missing; there is no fallback path.
+
+Build the library with ``python speculative_decoding_verification_w4a16_amd/build.py``
+(or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4a16.so")
+
+W4_OK, W4_ERR_INVALID, W4_ERR_UNSUPPORTED, W4_ERR_HIP = 0, 1, 2, 3
+W4_KERNEL_AUTO, W4_KERNEL_GEMV, W4_KERNEL_MFMA = 0, 1, 2
+GROUP = 128
+MAX_M = 64
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python speculative_decoding_verification_w4a16_amd/build.py`")
+
+# PyTorch-ROCm ships its own libamdhip64 (same soname as /opt/rocm's, but
+# loaded under another file name).  Loading this library first would bring in
+# /opt/rocm's runtime and torch would then load a second one, which cannot
+# open the device.  Importing torch first makes both use torch's runtime.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # pragma: no cover - the library itself does not need torch
+    _torch = None
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+
+
+class W4LinearDesc(ctypes.Structure):
+    _fields_ = [("x", _vp), ("qweight_t", _vp), ("scales_t", _vp), ("zeros_t", _vp), ("y", _vp), ("N", _i),
+                ("K", _i)]
+
+
+def _sig(name, args, res=_i):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_c = {
+    "w4_status_str": _sig("w4_status_str", [_i], ctypes.c_char_p),
+    "w4_init": _sig("w4_init", []),
+    "w4_last_error": _sig("w4_last_error", [], ctypes.c_char_p),
+    "w4_repacked_sizes": _sig("w4_repacked_sizes", [_i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                                    ctypes.POINTER(_sz)]),
+    "w4_repack": _sig("w4_repack", [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "w4a16_linear": _sig("w4a16_linear", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "w4a16_linear_cfg": _sig("w4a16_linear_cfg", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _vp]),
+    "w4a16_plan": _sig("w4a16_plan", [_i, _i, _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 5),
+    "w4a16_verify_pass": _sig("w4a16_verify_pass", [ctypes.POINTER(W4LinearDesc), _i, _i, _i, _vp]),
+    "w4_unpack": _sig("w4_unpack", [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "w4_bench_read": _sig("w4_bench_read", [_vp, _sz, _vp, _vp]),
+    "w4_bench_read_blocks": _sig("w4_bench_read_blocks", []),
+    "w4_bench_copy": _sig("w4_bench_copy", [_vp, _vp, _sz, _vp]),
+}
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        detail = f" [{w4_last_error()}]" if status == W4_ERR_HIP else ""
+        super().__init__(f"{where}: {w4_status_str(status)}{detail}")
+        self.status = status
+
+
+def exported_symbols():
+    """Names of the C entry points this binding wraps (all must be exported)."""
+    return sorted(_c)
+
+
+def _ptr(t):
+    """Device address of a tensor (or an int address, or None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+
+    dev = None
+    for t in tensors:
+        if t is not None and not isinstance(t, int) and t.is_cuda:
+            dev = t.device
+            break
+    if dev is None:
+        return None
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(rc, where):
+    if rc != W4_OK:
+        raise W4Error(rc, where)
+
+
+def w4_status_str(status: int) -> str:
+    return _c["w4_status_str"](status).decode()
+
+
+def w4_last_error() -> str:
+    return _c["w4_last_error"]().decode()
+
+
+def w4_init() -> None:
+    _check(_c["w4_init"](), "w4_init")
+
+
+def w4_repacked_sizes(N: int, K: int, group: int = GROUP):
+    q, s, z = _sz(), _sz(), _sz()
+    _check(_c["w4_repacked_sizes"](N, K, group, ctypes.byref(q), ctypes.byref(s), ctypes.byref(z)),
+           "w4_repacked_sizes")
+    return q.value, s.value, z.value
+
+
+def w4_repack(qweight, scales, zeros, N, K, group, qweight_t, scales_t, zeros_t, stream=None):
+    st = _stream(stream, qweight, qweight_t)
+    _check(_c["w4_repack"](_ptr(qweight), _ptr(scales), _ptr(zeros), N, K, group, _ptr(qweight_t), _ptr(scales_t),
+                           _ptr(zeros_t), st), "w4_repack")
+
+
+def w4a16_linear(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, stream=None):
+    st = _stream(stream, x, y)
+    _check(_c["w4a16_linear"](_ptr(x), _ptr(qweight_t), _ptr(scales_t), _ptr(zeros_t), M, N, K, group, _ptr(y), st),
+           "w4a16_linear")
+
+
+def w4a16_linear_cfg(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, kernel=W4_KERNEL_AUTO, splits=0,
+                     stream=None):
+    st = _stream(stream, x, y)
+    _check(_c["w4a16_linear_cfg"](_ptr(x), _ptr(qweight_t), _ptr(scales_t), _ptr(zeros_t), M, N, K, group, _ptr(y),
+                                  kernel, splits, st), "w4a16_linear_cfg")
+
+
+def w4a16_plan(M, N, K, group=GROUP, kernel=W4_KERNEL_AUTO, splits=0) -> dict:
+    outs = [_i() for _ in range(5)]
+    _check(_c["w4a16_plan"](M, N, K, group, kernel, splits, *[ctypes.byref(o) for o in outs]), "w4a16_plan")
+    return dict(zip(("kernel", "splits", "grid", "block", "lds"), (o.value for o in outs)))
+
+
+def w4a16_verify_pass(linears, M, group=GROUP, stream=None):
+    """`linears`: sequence of dicts with x, qweight_t, scales_t, zeros_t, y, N, K."""
+    arr = (W4LinearDesc * max(1, len(linears)))()
+    for i, d in enumerate(linears):
+        arr[i] = W4LinearDesc(_ptr(d["x"]), _ptr(d["qweight_t"]), _ptr(d["scales_t"]), _ptr(d["zeros_t"]),
+                              _ptr(d["y"]), d["N"], d["K"])
+    first = linears[0]["y"] if linears else None
+    st = _stream(stream, first)
+    _check(_c["w4a16_verify_pass"](arr, len(linears), M, group, st), "w4a16_verify_pass")
+
+
+def w4_unpack(qweight_t, zeros_t, N, K, group, q_out, z_out, stream=None):
+    st = _stream(stream, qweight_t, q_out)
+    _check(_c["w4_unpack"](_ptr(qweight_t), _ptr(zeros_t), N, K, group, _ptr(q_out), _ptr(z_out), st), "w4_unpack")
+
+
+def w4_bench_read_blocks() -> int:
+    return int(_c["w4_bench_read_blocks"]())
+
+
+def w4_bench_read(buf, nbytes, sink, stream=None):
+    st = _stream(stream, buf)
+    _check(_c["w4_bench_read"](_ptr(buf), nbytes, _ptr(sink), st), "w4_bench_read")
+
+
+def w4_bench_copy(dst, src, nbytes, stream=None):
+    st = _stream(stream, dst)
+    _check(_c["w4_bench_copy"](_ptr(dst), _ptr(src), nbytes, st), "w4_bench_copy")
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor conveniences (allocation + the calls above)
+# ---------------------------------------------------------------------------
+
+class PackedLinear:
+    """Tile-layout weights of one (N, K) linear on a device."""
+
+    def __init__(self, qweight_t, scales_t, zeros_t, N, K, group=GROUP):
+        self.qweight_t, self.scales_t, self.zeros_t = qweight_t, scales_t, zeros_t
+        self.N, self.K, self.group = N, K, group
+
+    @property
+    def nbytes(self) -> int:
+        return self.qweight_t.numel() * 4 + self.scales_t.numel() * 2 + self.zeros_t.numel() * 2
+
+
+def repack(qweight, scales, zeros, N, K, group=GROUP, stream=None) -> PackedLinear:
+    """Device canonical tensors (int32, int16/uint16 bits, int32) -> PackedLinear."""
+    import torch
+
+    qb, sb, zb = w4_repacked_sizes(N, K, group)
+    dev = qweight.device
+    qt = torch.empty(qb // 4, dtype=torch.int32, device=dev)
+    st = torch.empty(sb // 2, dtype=torch.int16, device=dev)
+    zt = torch.empty(zb // 2, dtype=torch.int16, device=dev)
+    w4_repack(qweight, scales, zeros, N, K, group, qt, st, zt, stream)
+    return PackedLinear(qt, st, zt, N, K, group)
+
+
+def linear(x, w: PackedLinear, y=None, kernel=W4_KERNEL_AUTO, splits=0, stream=None):
+    """y[M, N] fp32 = x[M, K] (bf16 tensor or int16 bf16 bits) . dequant(w)."""
+    import torch
+
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    w4a16_linear_cfg(x, w.qweight_t, w.scales_t, w.zeros_t, M, w.N, w.K, w.group, y, kernel, splits, stream)
+    return y

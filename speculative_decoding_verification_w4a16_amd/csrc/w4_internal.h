@@ -1,0 +1,67 @@
+// Internal interface between the C ABI (w4a16_api.cpp) and the kernels
+// (w4a16_kernels.hip).  Not installed; the public ABI is include/w4a16.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4 {
+
+constexpr int kChunkN = 64;   // output columns per chunk (4 MFMA n-tiles of 16)
+constexpr int kKBlock = 32;   // k per MFMA k-block (one 16x16x32 bf16 MFMA)
+constexpr int kGroup = 128;   // quantisation group along k
+constexpr int kWaves = 4;     // waves per workgroup (one chunk each)
+constexpr int kThreads = kWaves * 64;
+constexpr int kTileN = kWaves * kChunkN;  // output columns per workgroup
+
+enum KernelId { kAuto = 0, kGemv = 1, kMfma = 2 };
+
+struct Plan {
+    int kernel;   // kGemv or kMfma
+    int mb;       // m-blocks of 16 rows (MFMA)
+    int splits;   // K splits (workgroups per column tile)
+    int gps;      // groups per split
+    int ntiles;   // column tiles of kTileN
+    int grid;     // workgroups
+    int block;    // threads per workgroup
+    int lds;      // dynamic LDS bytes per workgroup
+    int row_stride;  // LDS bytes per staged x row
+};
+
+struct Workspace {
+    float* partial;      // split-K partial sums
+    size_t partial_bytes;
+    int* counters;       // per column tile, self-resetting
+    int n_counters;
+};
+
+// LDS budget per workgroup for the staged activation tile.
+constexpr int kLdsLimit = 160 * 1024 - 256;  // room for the small static LDS
+
+// Workspace sizes (per device).
+constexpr size_t kWorkspaceBytes = size_t(64) << 20;
+constexpr int kCounters = 1 << 16;
+
+int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Plan* p);
+
+hipError_t set_kernel_attributes();
+
+hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* zeros, int N, int K,
+                         uint32_t* qweight_t, uint16_t* scales_t, uint16_t* zeros_t, hipStream_t stream);
+
+hipError_t launch_unpack(const uint32_t* qweight_t, const uint16_t* zeros_t, int N, int K, uint8_t* q_out,
+                         uint8_t* z_out, hipStream_t stream);
+
+hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                         const uint16_t* zeros_t, int M, int N, int K, float* y, const Workspace& ws,
+                         hipStream_t stream);
+
+hipError_t launch_zero(float* y, size_t n, hipStream_t stream);
+
+hipError_t launch_bench_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
+hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+constexpr int kBenchReadBlocks = 256 * 8;
+
+}  // namespace w4

@@ -1,0 +1,275 @@
+// C ABI of the W4A16 verify linear (declared in include/w4a16.h and
+// include/w4a16_bench.h): argument validation, launch planning, the per-device
+// split-K workspace, and dispatch to the kernels in w4a16_kernels.hip.
+//
+// Every check runs before the first HIP call, so a rejected call touches no
+// device state; that is what lets the host tests exercise every error path
+// without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <mutex>
+
+#include "../../include/w4a16.h"
+#include "../../include/w4a16_bench.h"
+#include "w4_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+    bool ready = false;
+    w4::Workspace ws{};
+};
+
+std::mutex g_mutex;
+DeviceState g_dev[kMaxDevices];
+thread_local char g_last_error[256] = "";
+
+// Records the failing HIP call for w4_last_error and maps it to W4_ERR_HIP.
+int hip_fail(const char* what, hipError_t e) {
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what, hipGetErrorName(e), (int)e);
+    return W4_ERR_HIP;
+}
+
+int hip_status(const char* what, hipError_t e) { return e == hipSuccess ? W4_OK : hip_fail(what, e); }
+
+// Workspace and kernel attributes of the current device, created once.
+int device_state(w4::Workspace* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    if (dev < 0 || dev >= kMaxDevices) return hip_fail("device index", hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceState& st = g_dev[dev];
+    if (!st.ready) {
+        e = w4::set_kernel_attributes();
+        if (e != hipSuccess) return hip_fail("hipFuncSetAttribute", e);
+        void* p = nullptr;
+        void* c = nullptr;
+        e = hipMalloc(&p, w4::kWorkspaceBytes);
+        if (e != hipSuccess) return hip_fail("hipMalloc(workspace)", e);
+        e = hipMalloc(&c, sizeof(int) * w4::kCounters);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail("hipMalloc(counters)", e);
+        }
+        // counters start at zero; kernels re-arm them after every use
+        e = hipMemset(c, 0, sizeof(int) * w4::kCounters);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            (void)hipFree(c);
+            return hip_fail("hipMemset(counters)", e);
+        }
+        st.ws.partial = (float*)p;
+        st.ws.partial_bytes = w4::kWorkspaceBytes;
+        st.ws.counters = (int*)c;
+        st.ws.n_counters = w4::kCounters;
+        st.ready = true;
+    }
+    if (out) *out = st.ws;
+    return W4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b || an == 0 || bn == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+// Shape checks shared by every entry point.
+int check_shape(int N, int K, int group) {
+    if (N < 0 || K < 0) return W4_ERR_INVALID;
+    if (group != w4::kGroup) return W4_ERR_UNSUPPORTED;
+    if (N > W4_MAX_N || K > W4_MAX_K) return W4_ERR_UNSUPPORTED;
+    if (K % w4::kGroup != 0 || N % 8 != 0) return W4_ERR_UNSUPPORTED;
+    return W4_OK;
+}
+
+size_t chunks(int N) { return ((size_t)N + w4::kChunkN - 1) / w4::kChunkN; }
+
+void tile_sizes(int N, int K, size_t* qb, size_t* sb, size_t* zb) {
+    const size_t npad = chunks(N) * w4::kChunkN;
+    *qb = npad * (size_t)K / 2;
+    *sb = npad * (size_t)(K / w4::kGroup) * 2;
+    *zb = npad * (size_t)(K / w4::kGroup) / 2;
+}
+
+// Validation of one linear call; fills the plan on success.
+int check_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, const uint16_t* zt, int M, int N, int K,
+                 int group, const float* y, int kernel, int splits, w4::Plan* plan) {
+    if (M < 0) return W4_ERR_INVALID;
+    int rc = check_shape(N, K, group);
+    if (rc != W4_OK) return rc;
+    if (M > W4_MAX_M) return W4_ERR_UNSUPPORTED;
+    if (kernel < W4_KERNEL_AUTO || kernel > W4_KERNEL_MFMA || splits < 0) return W4_ERR_INVALID;
+    if (kernel == W4_KERNEL_GEMV && M > 1) return W4_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return W4_OK;  // nothing to compute
+    if (!y) return W4_ERR_INVALID;
+    if (!aligned(y, 4)) return W4_ERR_INVALID;
+    const size_t ybytes = (size_t)M * N * 4;
+    if (K == 0) return W4_OK;  // y = 0
+    if (!x || !qt || !st || !zt) return W4_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(qt, 16) || !aligned(st, 8) || !aligned(zt, 2)) return W4_ERR_INVALID;
+    size_t qb, sb, zb;
+    tile_sizes(N, K, &qb, &sb, &zb);
+    if (overlap(y, ybytes, x, (size_t)M * K * 2) || overlap(y, ybytes, qt, qb) || overlap(y, ybytes, st, sb) ||
+        overlap(y, ybytes, zt, zb))
+        return W4_ERR_INVALID;
+    if (plan) {
+        if (w4::plan_linear(M, N, K, kernel, splits, w4::kWorkspaceBytes, plan) != 0) return W4_ERR_UNSUPPORTED;
+    }
+    return W4_OK;
+}
+
+int run_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, const uint16_t* zt, int M, int N, int K,
+               float* y, const w4::Plan& plan, hipStream_t stream) {
+    if (M == 0 || N == 0) return W4_OK;
+    if (K == 0) return hip_status("zero_kernel launch", w4::launch_zero(y, (size_t)M * N, stream));
+    w4::Workspace ws{};
+    if (plan.splits > 1) {
+        int rc = device_state(&ws);
+        if (rc != W4_OK) return rc;
+    } else {
+        int rc = device_state(nullptr);  // kernel attributes
+        if (rc != W4_OK) return rc;
+    }
+    return hip_status("verify-linear launch", w4::launch_linear(plan, x, qt, st, zt, M, N, K, y, ws, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4_status_str(int status) {
+    switch (status) {
+        case W4_OK: return "W4_OK";
+        case W4_ERR_INVALID: return "W4_ERR_INVALID: invalid argument (null, negative, misaligned or overlapping)";
+        case W4_ERR_UNSUPPORTED: return "W4_ERR_UNSUPPORTED: unsupported shape or group size";
+        case W4_ERR_HIP: return "W4_ERR_HIP: a HIP runtime call failed";
+        default: return "W4_ERR_UNKNOWN: unknown status code";
+    }
+}
+
+const char* w4_last_error(void) { return g_last_error; }
+
+int w4_init(void) { return device_state(nullptr); }
+
+int w4_repacked_sizes(int N, int K, int group, size_t* qweight_bytes, size_t* scales_bytes, size_t* zeros_bytes) {
+    if (!qweight_bytes || !scales_bytes || !zeros_bytes) return W4_ERR_INVALID;
+    int rc = check_shape(N, K, group);
+    if (rc != W4_OK) return rc;
+    tile_sizes(N, K, qweight_bytes, scales_bytes, zeros_bytes);
+    return W4_OK;
+}
+
+int w4_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* zeros, int N, int K, int group,
+              uint32_t* qweight_t, uint16_t* scales_t, uint16_t* zeros_t, void* stream) {
+    int rc = check_shape(N, K, group);
+    if (rc != W4_OK) return rc;
+    if (N == 0 || K == 0) return W4_OK;
+    if (!qweight || !scales || !zeros || !qweight_t || !scales_t || !zeros_t) return W4_ERR_INVALID;
+    if (!aligned(qweight, 4) || !aligned(scales, 2) || !aligned(zeros, 4) || !aligned(qweight_t, 16) ||
+        !aligned(scales_t, 8) || !aligned(zeros_t, 2))
+        return W4_ERR_INVALID;
+    size_t qb, sb, zb;
+    tile_sizes(N, K, &qb, &sb, &zb);
+    const size_t cq = (size_t)N * K / 2, cs = (size_t)N * (K / w4::kGroup) * 2, cz = cs / 4;
+    const void* ins[3] = {qweight, scales, zeros};
+    const size_t inb[3] = {cq, cs, cz};
+    const void* outs[3] = {qweight_t, scales_t, zeros_t};
+    const size_t outb[3] = {qb, sb, zb};
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            if (overlap(outs[i], outb[i], ins[j], inb[j])) return W4_ERR_INVALID;
+            if (i != j && overlap(outs[i], outb[i], outs[j], outb[j])) return W4_ERR_INVALID;
+        }
+    return hip_status("repack launch", w4::launch_repack(qweight, scales, zeros, N, K, qweight_t, scales_t, zeros_t,
+                                                          (hipStream_t)stream));
+}
+
+int w4a16_linear_cfg(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                     const uint16_t* zeros_t, int M, int N, int K, int group, float* y, int kernel, int splits,
+                     void* stream) {
+    w4::Plan plan{};
+    int rc = check_linear(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, kernel, splits, &plan);
+    if (rc != W4_OK) return rc;
+    return run_linear(x, qweight_t, scales_t, zeros_t, M, N, K, y, plan, (hipStream_t)stream);
+}
+
+int w4a16_linear(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t, const uint16_t* zeros_t,
+                 int M, int N, int K, int group, float* y, void* stream) {
+    return w4a16_linear_cfg(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, W4_KERNEL_AUTO, 0, stream);
+}
+
+int w4a16_plan(int M, int N, int K, int group, int kernel, int splits, int* kernel_out, int* splits_out,
+               int* grid_out, int* block_out, int* lds_out) {
+    if (M <= 0 || N <= 0 || K <= 0) return W4_ERR_INVALID;
+    int rc = check_shape(N, K, group);
+    if (rc != W4_OK) return rc;
+    if (M > W4_MAX_M) return W4_ERR_UNSUPPORTED;
+    if (kernel < W4_KERNEL_AUTO || kernel > W4_KERNEL_MFMA || splits < 0) return W4_ERR_INVALID;
+    if (kernel == W4_KERNEL_GEMV && M > 1) return W4_ERR_UNSUPPORTED;
+    w4::Plan p{};
+    if (w4::plan_linear(M, N, K, kernel, splits, w4::kWorkspaceBytes, &p) != 0) return W4_ERR_UNSUPPORTED;
+    if (kernel_out) *kernel_out = p.kernel;
+    if (splits_out) *splits_out = p.splits;
+    if (grid_out) *grid_out = p.grid;
+    if (block_out) *block_out = p.block;
+    if (lds_out) *lds_out = p.lds;
+    return W4_OK;
+}
+
+int w4a16_verify_pass(const w4_linear_desc* linears, int n, int M, int group, void* stream) {
+    if (n < 0 || (n > 0 && !linears)) return W4_ERR_INVALID;
+    // validate everything first so a bad entry launches nothing
+    for (int i = 0; i < n; ++i) {
+        const w4_linear_desc& d = linears[i];
+        int rc = check_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, group, d.y, W4_KERNEL_AUTO, 0,
+                              nullptr);
+        if (rc != W4_OK) return rc;
+    }
+    for (int i = 0; i < n; ++i) {
+        const w4_linear_desc& d = linears[i];
+        w4::Plan plan{};
+        if (M > 0 && d.N > 0 && d.K > 0 &&
+            w4::plan_linear(M, d.N, d.K, W4_KERNEL_AUTO, 0, w4::kWorkspaceBytes, &plan) != 0)
+            return W4_ERR_UNSUPPORTED;
+        int rc = run_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, d.y, plan, (hipStream_t)stream);
+        if (rc != W4_OK) return rc;
+    }
+    return W4_OK;
+}
+
+int w4_unpack(const uint32_t* qweight_t, const uint16_t* zeros_t, int N, int K, int group, uint8_t* q_out,
+              uint8_t* z_out, void* stream) {
+    int rc = check_shape(N, K, group);
+    if (rc != W4_OK) return rc;
+    if (N == 0 || K == 0) return W4_OK;
+    if (!qweight_t || !zeros_t || !q_out || !z_out) return W4_ERR_INVALID;
+    if (!aligned(qweight_t, 16) || !aligned(zeros_t, 2)) return W4_ERR_INVALID;
+    return hip_status("unpack launch", w4::launch_unpack(qweight_t, zeros_t, N, K, q_out, z_out, (hipStream_t)stream));
+}
+
+int w4_bench_read_blocks(void) { return w4::kBenchReadBlocks; }
+
+int w4_bench_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink || bytes % 16 != 0 || !aligned(buf, 16) || !aligned(sink, 4)) return W4_ERR_INVALID;
+    if (bytes == 0) return W4_OK;
+    return hip_status("bench_read launch",
+                      w4::launch_bench_read(buf, bytes, sink, w4::kBenchReadBlocks, (hipStream_t)stream));
+}
+
+int w4_bench_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!dst || !src || bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16)) return W4_ERR_INVALID;
+    if (overlap(dst, bytes, src, bytes)) return W4_ERR_INVALID;
+    if (bytes == 0) return W4_OK;
+    return hip_status("bench_copy launch", w4::launch_bench_copy(dst, src, bytes, (hipStream_t)stream));
+}
+
+}  // extern "C"

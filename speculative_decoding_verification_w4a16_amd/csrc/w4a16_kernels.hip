@@ -1,0 +1,795 @@
+// HIP kernels of the W4A16 verify linear for gfx950 (CDNA4).
+//
+// The operation (a weight-only 4-bit linear evaluated over the M tokens of a
+// speculative-decoding verify pass; "Speculative Decoding Meets
+// Quantization", Abstract, and the ordoresearch.ai review, "Research
+// Landscape") is
+//     y[m, n] = sum_G s[G, n] * sum_{k in G} x[m, k] * (q[k, n] - z[G, n]).
+// The pages call this inference memory-bound; at M <= 64 the 0.52 bytes of
+// packed weight per multiply-add dominate every other stream, so every kernel
+// here is built around one coalesced pass over the packed weights.
+//
+// Tile layout (written by w4_repack): a chunk is 64 output columns; for each
+// chunk c and k-block kb (32 k) the 64 lanes of a wave read 1 KB, 16 bytes
+// per lane.  Lane l's word j carries the 8 codes of column 64c + 16j + l%16
+// at k = 32kb + 8(l/16) + e.  That is exactly the B operand of a
+// v_mfma_f32_16x16x32_bf16 for n-tile j, so one 128-bit load feeds four
+// MFMAs that share one A operand (the activation tile).
+//
+// Exact operands.  Code e sits at nibble e/2 (even e) or 4 + (e-1)/2 (odd e),
+// so  (word >> 4d) & 0x000F000F | 0x43004300  is the bf16 pair
+// (128 + q[2d], 128 + q[2d+1]) -- exact integers in bf16.  The kernels
+// accumulate x . (128 + q) per group in fp32 and subtract (128 + z) * sum(x)
+// per group before the fp32 group scale, so no weight is ever rounded.
+#include "w4_internal.h"
+
+#include <algorithm>
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+namespace w4 {
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+
+// 8 packed codes -> 4 bf16 pairs (128 + q): dword d holds k offsets 2d, 2d+1.
+// `mask` (0x000F000F) and `magic` (0x43004300) arrive as kernel arguments so
+// that the compiler keeps them in registers and forms one v_and_or_b32 per
+// pair (with literal constants it emits a separate AND and OR).  Plain C, not
+// inline asm, so the compiler's MFMA operand hazard checks see every write.
+__device__ __forceinline__ u32x4 unpack_biased(uint32_t w, uint32_t mask, uint32_t magic) {
+    u32x4 r;
+    r[0] = (w & mask) | magic;
+    r[1] = ((w >> 4) & mask) | magic;
+    r[2] = ((w >> 8) & mask) | magic;
+    r[3] = ((w >> 12) & mask) | magic;
+    return r;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// 128 + z for nibble j of a packed zero word, exact in fp32.
+__device__ __forceinline__ float biased_zero(uint32_t zw, int j) {
+    return (float)(128u + ((zw >> (4 * j)) & 15u));
+}
+
+// a . b + acc over one bf16 pair each, fp32 accumulation (v_dot2_f32_bf16).
+// Arguments are plain dwords: hipcc miscompiles __builtin_bit_cast applied
+// directly to an element of an ext_vector (it reads element 0), so vector
+// elements are always copied into a scalar first.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// sum of the 8 bf16 values in a 16-byte vector, fp32, via dot2 with ones.
+__device__ __forceinline__ float sum8_bf16(u32x4 v, float acc) {
+    const uint32_t v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+    acc = dot2(v0, 0x3F803F80u, acc);
+    acc = dot2(v1, 0x3F803F80u, acc);
+    acc = dot2(v2, 0x3F803F80u, acc);
+    return dot2(v3, 0x3F803F80u, acc);
+}
+
+// ---------------------------------------------------------------------------
+// repack: canonical -> tile layout (offline, not timed)
+// ---------------------------------------------------------------------------
+
+// Moves canonical nibble e (k offset e) to tile nibble e/2 (even e) or
+// 4 + (e-1)/2 (odd e).
+__device__ __forceinline__ uint32_t to_tile_nibbles(uint32_t w) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int p = (e & 1) ? 4 + (e >> 1) : (e >> 1);
+        out |= ((w >> (4 * e)) & 15u) << (4 * p);
+    }
+    return out;
+}
+
+// One thread per tile word.  Thread order (c, kb, o, j, t) keeps canonical
+// reads coalesced along n.
+__global__ void repack_qweight_kernel(const int32_t* __restrict__ qweight, int N, int K, uint32_t* __restrict__ out,
+                                      size_t total) {
+    const int KB = K / kKBlock;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const int t = (int)(idx & 15);
+        const int j = (int)((idx >> 4) & 3);
+        const int o = (int)((idx >> 6) & 3);
+        const size_t rest = idx >> 8;
+        const int kb = (int)(rest % KB);
+        const size_t c = rest / KB;
+        const size_t n = c * kChunkN + 16 * j + t;
+        uint32_t w = 0;
+        if (n < (size_t)N) w = (uint32_t)qweight[(size_t)(4 * kb + o) * N + n];
+        const int lane = o * 16 + t;
+        out[((c * KB + kb) * 64 + lane) * 4 + j] = to_tile_nibbles(w);
+    }
+}
+
+__global__ void repack_scales_kernel(const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N,
+                                     int K, uint16_t* __restrict__ s_out, uint16_t* __restrict__ z_out,
+                                     size_t total) {
+    const int G = K / kGroup;
+    // one thread per (c, G, t)
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const int t = (int)(idx & 15);
+        const size_t rest = idx >> 4;
+        const int g = (int)(rest % G);
+        const size_t c = rest / G;
+        uint32_t zw = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const size_t n = c * kChunkN + 16 * j + t;
+            uint16_t s = 0;
+            uint32_t z = 0;
+            if (n < (size_t)N) {
+                s = scales[(size_t)g * N + n];
+                z = ((uint32_t)zeros[(size_t)g * (N / 8) + n / 8] >> (4 * (n % 8))) & 15u;
+            }
+            s_out[idx * 4 + j] = s;
+            zw |= z << (4 * j);
+        }
+        z_out[idx] = (uint16_t)zw;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// unpack (test only): tile layout -> canonical bytes through unpack_biased
+// ---------------------------------------------------------------------------
+
+__global__ void unpack_qweight_kernel(const uint32_t* __restrict__ qt, int N, int K, uint8_t* __restrict__ q_out,
+                                      size_t total, uint32_t mask, uint32_t magic) {
+    const int KB = K / kKBlock;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const int j = (int)(idx & 3);
+        const int lane = (int)((idx >> 2) & 63);
+        const size_t rest = idx >> 8;
+        const int kb = (int)(rest % KB);
+        const size_t c = rest / KB;
+        const size_t n = c * kChunkN + 16 * j + (lane & 15);
+        if (n >= (size_t)N) continue;
+        const u32x4 b = unpack_biased(qt[idx], mask, magic);
+        const size_t k0 = (size_t)kb * kKBlock + 8 * (lane >> 4);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const float lo = bf16_bits_to_f32(b[d] & 0xFFFFu) - 128.0f;
+            const float hi = bf16_bits_to_f32(b[d] >> 16) - 128.0f;
+            q_out[(k0 + 2 * d) * N + n] = (uint8_t)lo;
+            q_out[(k0 + 2 * d + 1) * N + n] = (uint8_t)hi;
+        }
+    }
+}
+
+__global__ void unpack_zeros_kernel(const uint16_t* __restrict__ zt, int N, int K, uint8_t* __restrict__ z_out,
+                                    size_t total) {
+    const int G = K / kGroup;
+    for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const int t = (int)(idx & 15);
+        const size_t rest = idx >> 4;
+        const int g = (int)(rest % G);
+        const size_t c = rest / G;
+        const uint32_t zw = zt[idx];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const size_t n = c * kChunkN + 16 * j + t;
+            if (n < (size_t)N) z_out[(size_t)g * N + n] = (uint8_t)(biased_zero(zw, j) - 128.0f);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// verify linear: shared pieces
+// ---------------------------------------------------------------------------
+
+struct LinearArgs {
+    const uint16_t* x;
+    const u32x4* qt;
+    const uint2* st;
+    const uint16_t* zt;
+    float* y;
+    float* ws;
+    int* counters;
+    int M, N, K;
+    int NC, KB, G;
+    int gps, splits, ntiles;
+    int row_stride;  // LDS bytes per staged x row
+    int xs_off;      // LDS byte offset of the per-group x sums
+    uint32_t mask;   // 0x000F000F (see unpack_biased)
+    uint32_t magic;  // 0x43004300: bf16 128.0 in both halves
+};
+
+// Stage x[0:M, g0*128 : g1*128] into LDS rows of `row_stride` bytes, then a
+// 64-byte zero line (the A operand of padded rows).
+__device__ __forceinline__ void stage_x(const LinearArgs& a, char* smem, int g0, int ng) {
+    const int per_row = ng * (kGroup / 8);  // 16-byte pieces per row
+    const int total = a.M * per_row;
+    for (int p = threadIdx.x; p < total; p += kThreads) {
+        const int m = p / per_row;
+        const int q = p - m * per_row;
+        const u32x4 v = *(const u32x4*)(a.x + (size_t)m * a.K + (size_t)g0 * kGroup + 8 * q);
+        *(u32x4*)(smem + m * a.row_stride + 16 * q) = v;
+    }
+    if (threadIdx.x < 4) *(u32x4*)(smem + a.M * a.row_stride + 16 * threadIdx.x) = u32x4{0, 0, 0, 0};
+}
+
+// Split-K epilogue: the last workgroup of a column tile sums the partials in
+// split order (deterministic) and writes y; it then re-arms the counter.
+__device__ void splitk_fixup(const LinearArgs& a, int tile) {
+    __shared__ int last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last = (old == a.splits - 1);
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    const size_t npad = (size_t)a.NC * kChunkN;
+    const int n0 = tile * kTileN;
+    for (int idx = threadIdx.x; idx < a.M * kTileN; idx += kThreads) {
+        const int m = idx / kTileN;
+        const int n = n0 + (idx - m * kTileN);
+        if (n >= a.N) continue;
+        float acc = 0.0f;
+        for (int s = 0; s < a.splits; ++s) acc += a.ws[((size_t)s * a.M + m) * npad + n];
+        a.y[(size_t)m * a.N + n] = acc;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Ring of weight loads: D groups (4 x 16 B per lane each) in flight.
+constexpr int kRing = 3;
+
+// ---------------------------------------------------------------------------
+// M = 1: VALU GEMV (bf16 dot2, fp32 accumulation, cross-lane shuffles)
+// ---------------------------------------------------------------------------
+//
+// Lane (o = l/16, t = l%16) accumulates, for its 4 columns 64c + 16j + t, the
+// k of octet o in every k-block; the four octet lanes of a column are summed
+// with two xor-shuffles at the end.
+
+__global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int split = blockIdx.x / a.ntiles;
+    const int tile = blockIdx.x - split * a.ntiles;
+    const int g0 = split * a.gps;
+    const int ng = min(a.G, g0 + a.gps) - g0;
+    const int c = tile * kWaves + wave;
+    const int o = lane >> 4, t = lane & 15;
+
+    stage_x(a, smem, g0, ng);
+    __syncthreads();
+    // per (group, octet) sums of x: 32 values each
+    for (int p = threadIdx.x; p < ng * 4; p += kThreads) {
+        const int gl = p >> 2, oo = p & 3;
+        float acc = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = sum8_bf16(*(const u32x4*)(smem + (gl * kGroup + kk * kKBlock + 8 * oo) * 2), acc);
+        *(float*)(smem + a.xs_off + p * 4) = acc;
+    }
+    __syncthreads();
+
+    float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c < a.NC) {
+        const uint32_t mask = a.mask, magic = a.magic;
+        const u32x4* wp = a.qt + ((size_t)c * a.KB + (size_t)g0 * 4) * 64 + lane;
+        const uint2* sp = a.st + ((size_t)c * a.G + g0) * 16 + t;
+        const uint16_t* zp = a.zt + ((size_t)c * a.G + g0) * 16 + t;
+
+        u32x4 wr[kRing][4];
+        uint2 sr[kRing];
+        uint32_t zr[kRing];
+#pragma unroll
+        for (int d = 0; d < kRing; ++d) {
+            if (d < ng) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) wr[d][kk] = wp[(d * 4 + kk) * 64];
+                sr[d] = sp[d * 16];
+                zr[d] = zp[d * 16];
+            }
+        }
+        for (int gb = 0; gb < ng; gb += kRing) {
+#pragma unroll
+            for (int d = 0; d < kRing; ++d) {
+                const int gl = gb + d;
+                if (gl < ng) {
+                    float acc[4];
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const u32x4 xa = *(const u32x4*)(smem + (gl * kGroup + kk * kKBlock + 8 * o) * 2);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const u32x4 b = unpack_biased(wr[d][kk][j], mask, magic);
+                            float s0 = kk == 0 ? 0.0f : acc[j];
+                            s0 = dot2(b[0], xa[0], s0);
+                            s0 = dot2(b[1], xa[1], s0);
+                            s0 = dot2(b[2], xa[2], s0);
+                            s0 = dot2(b[3], xa[3], s0);
+                            acc[j] = s0;
+                        }
+                    }
+                    const float xs = *(const float*)(smem + a.xs_off + (gl * 4 + o) * 4);
+                    const uint2 sv = sr[d];
+                    const uint32_t zw = zr[d];
+                    const float sj[4] = {f16_bits_to_f32(sv.x & 0xFFFFu), f16_bits_to_f32(sv.x >> 16),
+                                         f16_bits_to_f32(sv.y & 0xFFFFu), f16_bits_to_f32(sv.y >> 16)};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) yv[j] = fmaf(sj[j], fmaf(-biased_zero(zw, j), xs, acc[j]), yv[j]);
+                    if (gl + kRing < ng) {
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) wr[d][kk] = wp[((gl + kRing) * 4 + kk) * 64];
+                        sr[d] = sp[(gl + kRing) * 16];
+                        zr[d] = zp[(gl + kRing) * 16];
+                    }
+                }
+            }
+        }
+    }
+    // sum the four octet lanes of each column
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        yv[j] += __shfl_xor(yv[j], 16);
+        yv[j] += __shfl_xor(yv[j], 32);
+    }
+    if (c < a.NC && o == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = c * kChunkN + 16 * j + t;
+            if (n < a.N) {
+                if (a.splits == 1)
+                    a.y[n] = yv[j];
+                else
+                    a.ws[(size_t)split * a.NC * kChunkN + n] = yv[j];
+            }
+        }
+    }
+    if (a.splits > 1) splitk_fixup(a, tile);
+}
+
+// ---------------------------------------------------------------------------
+// M = 2..64: bf16 MFMA, split-K, activations streamed through an LDS ring
+// ---------------------------------------------------------------------------
+//
+// A operand (activations, 16 rows x 32 k per m-block) comes from a
+// double-buffered LDS ring of kStage groups per stage; B operand (weights,
+// 32 k x 16 columns) is unpacked in registers from the 128-bit weight load.
+// Lane l of a 16x16 fp32 MFMA result holds rows 4(l/16) + r, r = 0..3, of
+// column l%16.  While a stage is computed the next stage's activations are
+// loaded into registers; at the end of the stage they are written to the
+// other LDS buffer together with their per-(row, group) sums, reduced over
+// the 16 lanes that hold one row-group (fixed order, deterministic).
+
+constexpr int kStage = 2;  // groups per LDS stage
+
+struct MfmaLds {
+    int row_stride;  // bytes per staged row (kStage groups + 16 bytes of skew)
+    int xs_off;      // offset of the x sums inside a buffer
+    int buf;         // bytes per buffer
+    int zero_off;    // offset of the 64-byte zero line
+    int total;
+};
+
+__host__ __device__ inline MfmaLds mfma_lds(int M, int mb) {
+    MfmaLds l;
+    l.row_stride = kStage * kGroup * 2 + 16;
+    l.xs_off = M * l.row_stride;
+    l.buf = (l.xs_off + kStage * 16 * mb * 4 + 15) & ~15;
+    l.zero_off = 2 * l.buf;
+    l.total = l.zero_off + 64;
+    return l;
+}
+
+// Load the activation pieces of stage `st` (16 bytes of one row-group each).
+template <int MB>
+__device__ __forceinline__ void mfma_load_x(const LinearArgs& a, int g0, int ng, int st, u32x4 (&xr)[MB * kStage]) {
+#pragma unroll
+    for (int i = 0; i < MB * kStage; ++i) {
+        const int p = threadIdx.x + kThreads * i;
+        const int m = p / (kStage * 16);
+        const int rem = p - m * (kStage * 16);
+        const int gl = st * kStage + (rem >> 4);
+        const int q = rem & 15;
+        xr[i] = u32x4{0, 0, 0, 0};
+        if (m < a.M && gl < ng) xr[i] = *(const u32x4*)(a.x + (size_t)m * a.K + (size_t)(g0 + gl) * kGroup + 8 * q);
+    }
+}
+
+template <int MB>
+__device__ __forceinline__ void mfma_store_x(const LinearArgs& a, const MfmaLds& L, char* buf, int g_in_stage_max,
+                                             const u32x4 (&xr)[MB * kStage]) {
+    constexpr int XSW = 16 * MB;
+#pragma unroll
+    for (int i = 0; i < MB * kStage; ++i) {
+        const int p = threadIdx.x + kThreads * i;
+        const int m = p / (kStage * 16);
+        const int rem = p - m * (kStage * 16);
+        const int gs = rem >> 4;
+        const int q = rem & 15;
+        const bool valid = m < a.M && gs < g_in_stage_max;
+        if (valid) *(u32x4*)(buf + m * L.row_stride + gs * kGroup * 2 + 16 * q) = xr[i];
+        float s = sum8_bf16(xr[i], 0.0f);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 8);
+        if (valid && q == 0) *(float*)(buf + L.xs_off + (gs * XSW + m) * 4) = s;
+    }
+}
+
+template <int MB>
+__global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(LinearArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    constexpr int XSW = 16 * MB;  // x sums per group (rows, padded to the m-blocks)
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int split = blockIdx.x / a.ntiles;
+    const int tile = blockIdx.x - split * a.ntiles;
+    const int g0 = split * a.gps;
+    const int ng = min(a.G, g0 + a.gps) - g0;
+    const int nst = (ng + kStage - 1) / kStage;
+    const int c = tile * kWaves + wave;
+    const bool active = c < a.NC;
+    const int o = lane >> 4, t = lane & 15;
+    const MfmaLds L = mfma_lds(a.M, MB);
+
+    // sums of padded rows stay zero; the zero line feeds padded A rows
+    for (int p = threadIdx.x; p < 2 * kStage * XSW; p += kThreads) {
+        const int b = p / (kStage * XSW), r = p - b * (kStage * XSW);
+        *(float*)(smem + b * L.buf + L.xs_off + r * 4) = 0.0f;
+    }
+    if (threadIdx.x < 4) *(u32x4*)(smem + L.zero_off + 16 * threadIdx.x) = u32x4{0, 0, 0, 0};
+    __syncthreads();
+    {
+        u32x4 xr[MB * kStage];
+        mfma_load_x<MB>(a, g0, ng, 0, xr);
+        mfma_store_x<MB>(a, L, smem, min(kStage, ng), xr);
+    }
+    __syncthreads();
+
+    f32x4 yv[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yv[mb][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const uint32_t mask = a.mask, magic = a.magic;
+    const u32x4* wp = a.qt + ((size_t)(active ? c : 0) * a.KB + (size_t)g0 * 4) * 64 + lane;
+    const uint2* sp = a.st + ((size_t)(active ? c : 0) * a.G + g0) * 16 + t;
+    const uint16_t* zp = a.zt + ((size_t)(active ? c : 0) * a.G + g0) * 16 + t;
+    int aoff[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int row = 16 * mb + t;
+        aoff[mb] = (row < a.M ? row * L.row_stride : L.zero_off) + 16 * o;
+    }
+    const int xs_lane = L.xs_off + 4 * (4 * o);
+
+    // weight ring: kStage groups in flight ahead of the one being computed
+    constexpr int R = 2 * kStage;
+    u32x4 wr[R][4];
+    uint2 sr[R];
+    uint32_t zr[R];
+    if (active) {
+#pragma unroll
+        for (int d = 0; d < R; ++d) {
+            if (d < ng) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) wr[d][kk] = wp[(d * 4 + kk) * 64];
+                sr[d] = sp[d * 16];
+                zr[d] = zp[d * 16];
+            }
+        }
+    }
+
+    u32x4 xr[MB * kStage];  // next stage's activations, in flight during a stage
+    for (int gb = 0; gb < ng; gb += R) {
+#pragma unroll
+        for (int d = 0; d < R; ++d) {
+            const int gl = gb + d;
+            if (gl < ng) {
+                const int st = gl / kStage;
+                const int gs = gl - st * kStage;
+                if (gs == 0 && st + 1 < nst) mfma_load_x<MB>(a, g0, ng, st + 1, xr);
+                const char* buf = smem + (st & 1) * L.buf;
+                if (active) {
+                    f32x4 acc[MB][4];
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        bf16x8 av[MB];
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) {
+                            const int off = 16 * mb + t < a.M ? (st & 1) * L.buf + aoff[mb] + (gs * kGroup + kk * kKBlock) * 2
+                                                              : aoff[mb];
+                            av[mb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + off));
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const bf16x8 bv = __builtin_bit_cast(bf16x8, unpack_biased(wr[d][kk][j], mask, magic));
+#pragma unroll
+                            for (int mb = 0; mb < MB; ++mb)
+                                acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    av[mb], bv, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][j], 0, 0, 0);
+                        }
+                    }
+                    const uint2 sv = sr[d];
+                    const uint32_t zw = zr[d];
+                    const float sj[4] = {f16_bits_to_f32(sv.x & 0xFFFFu), f16_bits_to_f32(sv.x >> 16),
+                                         f16_bits_to_f32(sv.y & 0xFFFFu), f16_bits_to_f32(sv.y >> 16)};
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const f32x4 xs = *(const f32x4*)(buf + xs_lane + (gs * XSW + 16 * mb) * 4);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float cz = biased_zero(zw, j);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                yv[mb][j][r] = fmaf(sj[j], fmaf(-cz, xs[r], acc[mb][j][r]), yv[mb][j][r]);
+                        }
+                    }
+                    if (gl + R < ng) {
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) wr[d][kk] = wp[((gl + R) * 4 + kk) * 64];
+                        sr[d] = sp[(gl + R) * 16];
+                        zr[d] = zp[(gl + R) * 16];
+                    }
+                }
+                if (gs == kStage - 1 || gl == ng - 1) {
+                    if (st + 1 < nst) {
+                        // everyone finished stage st-1, whose buffer this is
+                        mfma_store_x<MB>(a, L, smem + ((st + 1) & 1) * L.buf, min(kStage, ng - (st + 1) * kStage),
+                                         xr);
+                    }
+                    __syncthreads();
+                }
+            }
+        }
+    }
+
+    if (active) {
+        const size_t npad = (size_t)a.NC * kChunkN;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = c * kChunkN + 16 * j + t;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 16 * mb + 4 * o + r;
+                    if (m < a.M && n < a.N) {
+                        if (a.splits == 1)
+                            a.y[(size_t)m * a.N + n] = yv[mb][j][r];
+                        else
+                            a.ws[((size_t)split * a.M + m) * npad + n] = yv[mb][j][r];
+                    }
+                }
+            }
+    }
+    if (a.splits > 1) splitk_fixup(a, tile);
+}
+
+// ---------------------------------------------------------------------------
+// small kernels
+// ---------------------------------------------------------------------------
+
+__global__ void zero_kernel(float* __restrict__ y, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) y[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void bench_read_kernel(const u32x4* __restrict__ buf, size_t n16,
+                                                         uint32_t* __restrict__ sink) {
+    uint32_t acc = 0;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 v0 = __builtin_nontemporal_load(buf + i);
+        const u32x4 v1 = __builtin_nontemporal_load(buf + i + stride);
+        const u32x4 v2 = __builtin_nontemporal_load(buf + i + 2 * stride);
+        const u32x4 v3 = __builtin_nontemporal_load(buf + i + 3 * stride);
+        acc ^= v0[0] ^ v0[1] ^ v0[2] ^ v0[3] ^ v1[0] ^ v1[1] ^ v1[2] ^ v1[3];
+        acc ^= v2[0] ^ v2[1] ^ v2[2] ^ v2[3] ^ v3[0] ^ v3[1] ^ v3[2] ^ v3[3];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = buf[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    // xor-reduce the workgroup
+    for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
+    __shared__ uint32_t part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+__global__ __launch_bounds__(256) void bench_copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                         size_t n16) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// planning and launches
+// ---------------------------------------------------------------------------
+
+static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// LDS bytes of the GEMV kernel with `gps` groups per split (the whole
+// K-range of x is staged once).
+static int gemv_lds(int gps, int* row_stride, int* xs_off) {
+    const int rs = gps * kGroup * 2 + 16;
+    if (row_stride) *row_stride = rs;
+    if (xs_off) *xs_off = rs + 64;
+    return rs + 64 + gps * 4 * 4;
+}
+
+int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Plan* p) {
+    if (kernel == kAuto) kernel = (M == 1) ? kGemv : kMfma;
+    if (kernel == kGemv && M != 1) return -1;
+    const int NC = ceil_div(N, kChunkN);
+    const int G = K / kGroup;
+    const int ntiles = ceil_div(NC, kWaves);
+    const int mb = ceil_div(M, 16);
+    // GEMV stages its whole K-range of x; the MFMA kernel streams it
+    int gmax = G;
+    if (kernel == kGemv)
+        while (gmax > 1 && gemv_lds(gmax, nullptr, nullptr) > kLdsLimit) --gmax;
+    int S;
+    if (splits > 0) {
+        S = splits;
+    } else {
+        // aim for ~2 workgroups per CU (256 CUs), fewer splits when the
+        // partial sums would be a large fraction of the weight bytes
+        const int target = 512;
+        S = ceil_div(target, ntiles);
+        const long weight_bytes = (long)NC * kChunkN * K / 2;
+        const long partial_per_split = (long)M * NC * kChunkN * 4;
+        const int s_traffic = (int)std::max<long>(1, weight_bytes / (4 * partial_per_split));
+        S = std::min(S, s_traffic);
+    }
+    S = std::max(1, std::min(S, G));
+    int gps = ceil_div(G, S);
+    if (gps > gmax) gps = gmax;
+    S = ceil_div(G, gps);
+    // the split-K workspace must hold S partial [M][NC*64] tiles
+    while (S > 1 && (size_t)S * M * NC * kChunkN * 4 > ws_bytes) {
+        if (gps >= gmax) return -2;
+        ++gps;
+        S = ceil_div(G, gps);
+    }
+    if (S > 1 && ntiles > kCounters) return -2;
+    p->kernel = kernel;
+    p->mb = mb;
+    p->splits = S;
+    p->gps = gps;
+    p->ntiles = ntiles;
+    p->grid = ntiles * S;
+    p->block = kThreads;
+    if (kernel == kGemv) {
+        p->lds = gemv_lds(gps, &p->row_stride, nullptr);
+    } else {
+        const MfmaLds L = mfma_lds(M, mb);
+        p->lds = L.total;
+        p->row_stride = L.row_stride;
+    }
+    return 0;
+}
+
+hipError_t set_kernel_attributes() {
+    hipError_t e;
+    e = hipFuncSetAttribute((const void*)w4a16_gemv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)w4a16_mfma_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)w4a16_mfma_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)w4a16_mfma_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute((const void*)w4a16_mfma_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kLdsLimit);
+}
+
+static constexpr uint32_t kNibbleMask = 0x000F000Fu;
+static constexpr uint32_t kBiasMagic = 0x43004300u;
+
+static int grid_for(size_t total, int block) {
+    size_t g = (total + block - 1) / block;
+    if (g > 65535 * 4) g = 65535 * 4;
+    return (int)std::max<size_t>(g, 1);
+}
+
+// Launch through hipLaunchKernel so the status returned is this launch's own
+// (hipGetLastError could report an earlier, unrelated failure).
+template <typename... Args>
+static hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                         Args... args) {
+    void* argv[] = {(void*)&args...};
+    return hipLaunchKernel((const void*)kernel, grid, block, argv, lds, stream);
+}
+
+hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* zeros, int N, int K,
+                         uint32_t* qweight_t, uint16_t* scales_t, uint16_t* zeros_t, hipStream_t stream) {
+    const size_t NC = (size_t)ceil_div(N, kChunkN);
+    const size_t words = NC * (K / kKBlock) * 256;
+    hipError_t e = launch(repack_qweight_kernel, dim3(grid_for(words, 256)), dim3(256), 0, stream, qweight, N, K,
+                          qweight_t, words);
+    if (e != hipSuccess) return e;
+    const size_t sz = NC * (K / kGroup) * 16;
+    return launch(repack_scales_kernel, dim3(grid_for(sz, 256)), dim3(256), 0, stream, scales, zeros, N, K, scales_t,
+                  zeros_t, sz);
+}
+
+hipError_t launch_unpack(const uint32_t* qweight_t, const uint16_t* zeros_t, int N, int K, uint8_t* q_out,
+                         uint8_t* z_out, hipStream_t stream) {
+    const size_t NC = (size_t)ceil_div(N, kChunkN);
+    const size_t words = NC * (K / kKBlock) * 256;
+    hipError_t e = launch(unpack_qweight_kernel, dim3(grid_for(words, 256)), dim3(256), 0, stream, qweight_t, N, K,
+                          q_out, words, kNibbleMask, kBiasMagic);
+    if (e != hipSuccess) return e;
+    const size_t sz = NC * (K / kGroup) * 16;
+    return launch(unpack_zeros_kernel, dim3(grid_for(sz, 256)), dim3(256), 0, stream, zeros_t, N, K, z_out, sz);
+}
+
+hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                         const uint16_t* zeros_t, int M, int N, int K, float* y, const Workspace& ws,
+                         hipStream_t stream) {
+    LinearArgs a;
+    a.x = x;
+    a.qt = (const u32x4*)qweight_t;
+    a.st = (const uint2*)scales_t;
+    a.zt = zeros_t;
+    a.y = y;
+    a.ws = ws.partial;
+    a.counters = ws.counters;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.NC = ceil_div(N, kChunkN);
+    a.KB = K / kKBlock;
+    a.G = K / kGroup;
+    a.gps = p.gps;
+    a.splits = p.splits;
+    a.ntiles = p.ntiles;
+    a.row_stride = 0;
+    a.xs_off = 0;
+    a.mask = kNibbleMask;
+    a.magic = kBiasMagic;
+    if (p.kernel == kGemv) gemv_lds(p.gps, &a.row_stride, &a.xs_off);
+    const dim3 grid(p.grid), block(p.block);
+    if (p.kernel == kGemv) return launch(w4a16_gemv_kernel, grid, block, p.lds, stream, a);
+    switch (p.mb) {
+        case 1: return launch(w4a16_mfma_kernel<1>, grid, block, p.lds, stream, a);
+        case 2: return launch(w4a16_mfma_kernel<2>, grid, block, p.lds, stream, a);
+        case 3: return launch(w4a16_mfma_kernel<3>, grid, block, p.lds, stream, a);
+        default: return launch(w4a16_mfma_kernel<4>, grid, block, p.lds, stream, a);
+    }
+}
+
+hipError_t launch_zero(float* y, size_t n, hipStream_t stream) {
+    return launch(zero_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, y, n);
+}
+
+hipError_t launch_bench_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream) {
+    return launch(bench_read_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4*)buf, bytes / 16, sink);
+}
+
+hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    const size_t n16 = bytes / 16;
+    return launch(bench_copy_kernel, dim3(grid_for(n16, 256)), dim3(256), 0, stream, (u32x4*)dst, (const u32x4*)src,
+                  n16);
+}
+
+}  // namespace w4

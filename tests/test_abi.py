@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+headers declare, and rejects bad arguments before any HIP call.
+
+Nothing here launches a kernel, so it runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("w4a16.h", "w4a16_bench.h")]
+
+w4 = pytest.importorskip("speculative_decoding_verification_w4a16_amd")
+
+
+def _declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(w4\w*)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 12, names
+    lib = ctypes.CDLL(w4.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the binding wraps every one of them under the same name
+    assert set(names) <= set(w4.exported_symbols())
+    for n in names:
+        assert callable(getattr(w4, n))
+
+
+def test_status_strings():
+    assert w4.w4_status_str(0) == "W4_OK"
+    for s in (1, 2, 3):
+        assert w4.w4_status_str(s).startswith("W4_ERR_")
+    assert "UNKNOWN" in w4.w4_status_str(99)
+
+
+def test_repacked_sizes():
+    assert w4.w4_repacked_sizes(8192, 8192) == (8192 * 8192 // 2, 8192 * 8192 // 64, 8192 * 8192 // 256)
+    # N padded to 64 columns
+    assert w4.w4_repacked_sizes(200, 256) == (256 * 256 // 2, 256 * 2 * 2, 256 * 2 // 2)
+    for args, code in [((8192, 8192, 64), w4.W4_ERR_UNSUPPORTED), ((8192, 100, 128), w4.W4_ERR_UNSUPPORTED),
+                       ((12, 128, 128), w4.W4_ERR_UNSUPPORTED), ((-8, 128, 128), w4.W4_ERR_INVALID)]:
+        with pytest.raises(w4.W4Error) as e:
+            w4.w4_repacked_sizes(*args)
+        assert e.value.status == code
+
+
+def _lin(x=0x1000, q=0x2000, s=0x3000, z=0x4000, M=4, N=256, K=512, g=128, y=0x100000, kernel=0, splits=0):
+    return w4.w4a16_linear_cfg(x, q, s, z, M, N, K, g, y, kernel, splits, stream=0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), 1), (dict(N=-8), 1), (dict(K=-128), 1),
+    (dict(M=65), 2), (dict(g=64), 2), (dict(K=500), 2), (dict(N=12), 2),
+    (dict(kernel=1, M=2), 2), (dict(kernel=7), 1), (dict(splits=-1), 1),
+    (dict(x=0), 1), (dict(q=0), 1), (dict(s=0), 1), (dict(z=0), 1), (dict(y=0), 1),
+    (dict(x=0x1008), 1), (dict(q=0x2004), 1), (dict(s=0x3002), 1), (dict(z=0x4001), 1), (dict(y=0x100002), 1),
+    (dict(y=0x1000), 1),            # y overlaps x
+    (dict(y=0x2000 + 64), 1),       # y overlaps the weights
+])
+def test_linear_argument_errors(kw, code):
+    with pytest.raises(w4.W4Error) as e:
+        _lin(**kw)
+    assert e.value.status == code
+
+
+def test_empty_calls_are_noops():
+    # nothing to compute: returns OK without touching memory or the GPU
+    _lin(M=0, x=0, q=0, s=0, z=0, y=0)
+    _lin(N=0, x=0, q=0, s=0, z=0, y=0)
+
+
+def test_repack_and_unpack_argument_errors():
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_repack(0, 0x3000, 0x4000, 256, 512, 128, 0x10000, 0x20000, 0x30000, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(w4.W4Error) as e:  # output overlaps input
+        w4.w4_repack(0x10000, 0x90000, 0xA0000, 256, 512, 128, 0x10000 + 256, 0xB0000, 0xC0000, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_unpack(0x10004, 0x20000, 256, 512, 128, 0x30000, 0x40000, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_unpack(0x10000, 0x20000, 256, 512, 96, 0x30000, 0x40000, stream=0)
+    assert e.value.status == 2
+
+
+def test_verify_pass_validates_every_entry_first():
+    good = dict(x=0x1000, qweight_t=0x2000, scales_t=0x3000, zeros_t=0x4000, y=0x100000, N=256, K=512)
+    bad = dict(good, K=500)
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4a16_verify_pass([good, bad], M=2, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4a16_verify_pass([good], M=70, stream=0)
+    assert e.value.status == 2
+
+
+def test_bench_argument_errors():
+    with pytest.raises(w4.W4Error):
+        w4.w4_bench_read(0x1000, 100, 0x2000, stream=0)
+    with pytest.raises(w4.W4Error):
+        w4.w4_bench_copy(0x1000, 0x1000 + 16, 64, stream=0)
+    assert w4.w4_bench_read_blocks() > 0
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 16, 17, 33, 64])
+@pytest.mark.parametrize("N,K", [(256, 512), (8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672),
+                                 (128256, 8192), (200, 384)])
+def test_plans_fit_the_hardware(M, N, K):
+    p = w4.w4a16_plan(M, N, K)
+    assert p["kernel"] == (w4.W4_KERNEL_GEMV if M == 1 else w4.W4_KERNEL_MFMA)
+    assert p["block"] == 256 and p["lds"] <= 160 * 1024 - 256
+    assert 1 <= p["splits"] <= K // 128
+    ntiles = -(-(-(-N // 64)) // 4)
+    assert p["grid"] == ntiles * p["splits"]
+    # the split-K workspace (64 MiB) holds every partial
+    assert p["splits"] == 1 or p["splits"] * M * (-(-N // 64) * 64) * 4 <= 64 << 20
+
+
+def test_forced_plans():
+    p = w4.w4a16_plan(1, 8192, 8192, kernel=w4.W4_KERNEL_MFMA, splits=3)
+    assert p["kernel"] == w4.W4_KERNEL_MFMA and p["splits"] == 3
+    p = w4.w4a16_plan(4, 256, 512, splits=100)
+    assert p["splits"] == 4
