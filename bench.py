@@ -1,0 +1,444 @@
+#!/usr/bin/env python3
+"""Verify-pass benchmark of the W4A16 linear on one MI355X.
+
+Workload (the full-model verify sweep): a Llama-3-70B-shaped target with 80
+decoder layers of seven int4 linears (q 8192->8192, k/v 8192->1024,
+o 8192->8192, gate/up 8192->28672, down 28672->8192) and an int4 lm_head
+8192->128256, uint4 codes with fp16 scales and uint4 zeros per group of 128,
+W ~ N(0, 0.02) quantised round-to-nearest; layer L's linear idx uses seed
+10000 + 7L + idx and the lm_head seed 20000.  ~36.1 GB of packed weights stay
+resident in HBM.  One *step* is three verify passes, at M = 1 (plain decode),
+M = 5 (a sequence draft) and M = 64 (a flattened tree draft): 561 linear
+launches each, captured once per M in a HIP graph and replayed.
+
+Printed JSON line: `value` is the step's effective HBM throughput (algorithmic
+bytes of the three passes / step time, TB/s); per-M microseconds per pass,
+t(M)/t(1), roofline fractions, the measured HBM read ceiling, the oracle's
+host throughput on a bounded sample and the oracle spot checks ride along.
+
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import queue
+import sys
+import threading
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16, published
+PASS_M = (1, 5, 64)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(M: int, N: int, K: int) -> int:
+    """Algorithmic HBM bytes of one linear: packed codes (N K / 2), fp16 scales
+    and uint4 zeros per group of 128 (N K / 64 + N K / 256), x once (2 M K)
+    and y once (4 M N)."""
+    return N * K // 2 + N * K // 64 + N * K // 256 + 2 * M * K + 4 * M * N
+
+
+def alg_flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle on the host")
+    p.add_argument("--no-parity", action="store_true", help="skip the oracle spot checks")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# model construction: host generation (threads) -> pinned -> HBM -> repack
+# ---------------------------------------------------------------------------
+
+def model_specs():
+    import synth
+
+    specs = []
+    for L in range(synth.N_LAYERS):
+        for idx, (name, N, K) in enumerate(synth.LAYER_LINEARS):
+            specs.append(dict(layer=L, name=name, N=N, K=K, seed=10000 + 7 * L + idx))
+    name, N, K = synth.LM_HEAD
+    specs.append(dict(layer=None, name=name, N=N, K=K, seed=20000))
+    return specs
+
+
+class PinnedSlot:
+    """A pinned host buffer big enough for the largest linear's canonical arrays."""
+
+    def __init__(self, torch, max_nk: int, max_groups_n: int):
+        self.q = torch.empty(max_nk // 8, dtype=torch.int32, pin_memory=True)
+        self.s = torch.empty(max_groups_n, dtype=torch.int16, pin_memory=True)
+        self.z = torch.empty(max_groups_n // 8, dtype=torch.int32, pin_memory=True)
+
+    def views(self, N, K):
+        G = K // 128
+        return {"qweight": self.q[: N * K // 8].numpy().reshape(K // 8, N),
+                "scales": self.s[: G * N].numpy().view(np.uint16).reshape(G, N),
+                "zeros": self.z[: G * N // 8].numpy().reshape(G, N // 8)}
+
+    def tensors(self, N, K):
+        G = K // 128
+        return self.q[: N * K // 8], self.s[: G * N], self.z[: G * N // 8]
+
+
+def build_model(torch, w4, keep_layers, keep_linears=()):
+    """Generate, upload and repack every linear.  Returns (packed, host_copies)
+    where host_copies holds the canonical arrays of the layers the oracle
+    checks and of `keep_linears`."""
+    import synth
+
+    dev = torch.device("cuda:0")
+    specs = model_specs()
+    max_nk = max(s["N"] * s["K"] for s in specs)
+    max_gn = max(s["N"] * s["K"] // 128 for s in specs)
+    slots = [PinnedSlot(torch, max_nk, max_gn) for _ in range(3)]
+    free = queue.Queue()
+    for s in slots:
+        free.put(s)
+    ready = queue.Queue(maxsize=len(slots))
+    threads = synth._threads()
+
+    def producer():
+        for spec in specs:
+            slot = free.get()
+            synth.gen_linear(spec["seed"], spec["N"], spec["K"], out=slot.views(spec["N"], spec["K"]), nthreads=threads)
+            ready.put((spec, slot))
+
+    th = threading.Thread(target=producer, daemon=True)
+    th.start()
+    stage_q = torch.empty(max_nk // 8, dtype=torch.int32, device=dev)
+    stage_s = torch.empty(max_gn, dtype=torch.int16, device=dev)
+    stage_z = torch.empty(max_gn // 8, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    packed = {}
+    host = {}
+    t0 = time.time()
+    for i in range(len(specs)):
+        spec, slot = ready.get()
+        N, K = spec["N"], spec["K"]
+        key = (spec["layer"], spec["name"])
+        if spec["layer"] in keep_layers or key in keep_linears:
+            host[key] = {k: v.copy() for k, v in slot.views(N, K).items()}
+        hq, hs, hz = slot.tensors(N, K)
+        dq, ds, dz = stage_q[: hq.numel()], stage_s[: hs.numel()], stage_z[: hz.numel()]
+        dq.copy_(hq, non_blocking=True)
+        ds.copy_(hs, non_blocking=True)
+        dz.copy_(hz, non_blocking=True)
+        pk = w4.repack(dq, ds, dz, N, K)
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        ev.synchronize()  # the slot's host data has been consumed
+        free.put(slot)
+        packed[key] = pk
+        if (i + 1) % 70 == 0 or i + 1 == len(specs):
+            log(f"[bench] model: {i + 1}/{len(specs)} linears resident ({time.time() - t0:.1f} s)")
+    th.join()
+    del stage_q, stage_s, stage_z
+    torch.cuda.synchronize()
+    return packed, host
+
+
+# ---------------------------------------------------------------------------
+# measurement pieces
+# ---------------------------------------------------------------------------
+
+def hbm_read_ceiling(torch, w4, nbytes=8 << 30, reps=5):
+    """Achievable HBM read bandwidth: one 128-bit-load pass over 8 GiB."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
+    sink = torch.empty(w4.w4_bench_read_blocks(), dtype=torch.int32, device="cuda:0")
+    w4.w4_bench_read(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        w4.w4_bench_read(buf, nbytes, sink)
+        e.record()
+        e.synchronize()
+        best = max(best, nbytes / (s.elapsed_time(e) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
+def per_launch_durations(torch, w4, descs, M, reps=2):
+    """Eager pass with events around every launch (ms per launch, mean over reps)."""
+    dur = np.zeros(len(descs))
+    for _ in range(reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in descs]
+        for d, (s, e) in zip(descs, evs):
+            s.record()
+            w4.w4a16_verify_pass([d], M)
+            e.record()
+        torch.cuda.synchronize()
+        dur += np.array([s.elapsed_time(e) for s, e in evs])
+    return dur / reps
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "speculative_decoding_verification_w4a16_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_name: str):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_digest") != source_digest():
+        return None
+    ent = data.get("kernels", {}).get(kernel_name)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(host, budget_s=25.0):
+    """The oracle, as it stands, on a bounded sample of the workload: layer 0's
+    q, k, v and o linears at M = 5, one linear at a time until the budget."""
+    import synth
+    from oracle import linear64
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    done, secs, nbytes = [], 0.0, 0
+    for name, N, K in synth.LAYER_LINEARS:
+        key = (0, name)
+        if key not in host or secs > budget_s * 0.5:
+            continue
+        lin = host[key]
+        x = synth.gen_x(5, K)
+        t = time.perf_counter()
+        linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+        secs += time.perf_counter() - t
+        nbytes += alg_bytes(5, N, K)
+        done.append(name)
+        if secs > budget_s:
+            break
+    return {"value": round(nbytes / secs / 1e12, 6), "unit": "TB/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 oracle (numpy, BLAS threads={cores}) on layer 0 linears {done} at M=5: "
+                      f"{nbytes / 1e9:.3f} GB of algorithmic traffic in {secs:.2f} s"}
+
+
+def parity_checks(torch, w4, packed, host, xs, check_layers, n0):
+    """Oracle spot checks (3 layers x 7 linears on sampled column slices, and
+    the lm_head on a 512-column slice) at every pass M, using the same launch
+    plan as the sweep."""
+    import synth
+    from oracle import check_contract, linear64_columns
+
+    worst = 0.0
+    rng = np.random.default_rng(1)
+    for M in PASS_M:
+        for L in check_layers:
+            for name, N, K in synth.LAYER_LINEARS:
+                lin = host[(L, name)]
+                y = w4.linear(xs[K][:M], packed[(L, name)])
+                torch.cuda.synchronize()
+                yh = y.cpu().numpy()
+                mid = int(rng.integers(1, N // 64 - 1)) * 64
+                for a, b in ((0, 64), (mid, mid + 64), (N - 64, N)):
+                    Y, A = linear64_columns(synth.gen_x(M, K), lin["qweight"], lin["scales"], lin["zeros"], 128, a, b)
+                    ok, r = check_contract(yh[:, a:b], Y, A)
+                    worst = max(worst, r)
+                    if not ok:
+                        raise AssertionError(f"parity failure layer {L} {name} M={M} cols {a}:{b} ratio {r}")
+        lin = host[(None, "lm_head")]
+        name, N, K = synth.LM_HEAD
+        y = w4.linear(xs[K][:M], packed[(None, "lm_head")])
+        torch.cuda.synchronize()
+        Y, A = linear64_columns(synth.gen_x(M, K), lin["qweight"], lin["scales"], lin["zeros"], 128, n0, n0 + 512)
+        ok, r = check_contract(y.cpu().numpy()[:, n0:n0 + 512], Y, A)
+        worst = max(worst, r)
+        if not ok:
+            raise AssertionError(f"parity failure lm_head M={M} ratio {r}")
+    return worst
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the verify linear is measured on one MI355X); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import speculative_decoding_verification_w4a16_amd as w4
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    t_start = time.time()
+    w4.w4_init()
+    rng = np.random.default_rng(0)
+    check_layers = sorted(int(v) for v in rng.choice(synth.N_LAYERS, 3, replace=False))
+    n0 = int(rng.integers(0, (synth.LM_HEAD[1] - 512) // 8)) * 8
+    keep = set(check_layers) | {0}
+    packed, host = build_model(torch, w4, keep, keep_linears={(None, "lm_head")})
+    t_model = time.time() - t_start
+    log(f"[bench] model resident after {t_model:.1f} s; checked layers {check_layers}, lm_head cols {n0}..{n0 + 512}")
+
+    dev = "cuda:0"
+    xs = {K: torch.from_numpy(synth.gen_x(64, K).view(np.int16)).to(dev) for K in (8192, 28672)}
+    ys = {N: torch.empty((64, N), dtype=torch.float32, device=dev) for N in (1024, 8192, 28672, 128256)}
+    specs = model_specs()
+
+    def descs_for(M):
+        out = []
+        for s in specs:
+            pk = packed[(s["layer"], s["name"])]
+            out.append(dict(x=xs[s["K"]][:M], qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t,
+                            y=ys[s["N"]][:M], N=s["N"], K=s["K"]))
+        return out
+
+    descs = {M: descs_for(M) for M in PASS_M}
+    pass_bytes = {M: sum(alg_bytes(M, s["N"], s["K"]) for s in specs) for M in PASS_M}
+    pass_flops = {M: sum(alg_flops(M, s["N"], s["K"]) for s in specs) for M in PASS_M}
+
+    # eager pass once per M (also the graph's warm-up), then capture
+    for M in PASS_M:
+        w4.w4a16_verify_pass(descs[M], M)
+    torch.cuda.synchronize()
+    graphs = {}
+    cap = torch.cuda.Stream()
+    for M in PASS_M:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            w4.w4a16_verify_pass(descs[M], M)
+        graphs[M] = g
+    torch.cuda.synchronize()
+
+    def step():
+        for M in PASS_M:
+            graphs[M].replay()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    step_bytes = sum(pass_bytes.values())
+    value_tbs = step_bytes / (ms_per_step * 1e-3) / 1e12
+
+    # per-M pass times (graph replays)
+    us_per_pass = {}
+    for M in PASS_M:
+        reps = max(3, args.steps)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            graphs[M].replay()
+        e.record()
+        torch.cuda.synchronize()
+        us_per_pass[M] = s.elapsed_time(e) * 1e3 / reps
+    # eager (no graph) pass times, for the launch-overhead comparison
+    us_eager = {}
+    for M in PASS_M:
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        w4.w4a16_verify_pass(descs[M], M)
+        e.record()
+        torch.cuda.synchronize()
+        us_eager[M] = s.elapsed_time(e) * 1e3
+
+    # per-kernel roofline: every launch of a pass runs one kernel instantiation
+    # (M=1 -> GEMV, M=5 -> MFMA with one m-block, M=64 -> MFMA with four)
+    kernel_of = {1: "w4a16_gemv_kernel", 5: "w4a16_mfma_kernel<1>", 64: "w4a16_mfma_kernel<4>"}
+    kernels = {}
+    for M in PASS_M:
+        dur_ms = per_launch_durations(torch, w4, descs[M], M)
+        mean_us = float(dur_ms.mean() * 1e3)
+        bytes_per_launch = pass_bytes[M] / len(specs)
+        flops_per_launch = pass_flops[M] / len(specs)
+        achieved = bytes_per_launch / (mean_us * 1e-6) / 1e9
+        kernels[kernel_of[M]] = {
+            "M": M, "launches_per_pass": len(specs), "mean_launch_us": round(mean_us, 3),
+            "alg_bytes_per_launch": int(bytes_per_launch), "achieved_GBps": round(achieved, 1),
+            "frac_hbm": round(achieved / HBM_PEAK_GBS, 4),
+            "mfma_util": round(flops_per_launch / (mean_us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+            "time_share_us": round(float(dur_ms.sum() * 1e3), 1)}
+    dom = max(kernels, key=lambda k: kernels[k]["time_share_us"])
+    dk = kernels[dom]
+    traffic = traffic_from_profiles(dom)
+    roofline = {"bound": "hbm", "achieved": dk["achieved_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dk["achieved_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
+                "per_launch": "alg_bytes_per_launch = 0.51953125 N K + 2 M K + 4 M N averaged over the 561 "
+                              "linears of the pass; achieved = that / mean event-timed launch duration"}
+
+    ceiling = hbm_read_ceiling(torch, w4)
+    parity = None
+    if not args.no_parity:
+        parity = {"layers": check_layers, "lm_head_cols": [n0, n0 + 512],
+                  "worst_err_over_bound": parity_checks(torch, w4, packed, host, xs, check_layers, n0)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(host)
+
+    t_roof = {M: max(pass_bytes[M] / (HBM_PEAK_GBS * 1e9), pass_flops[M] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+              for M in PASS_M}
+    out = {
+        "metric": "int4-weight verify GEMM us/pass + HBM TB/s, Llama-3-70B shapes, M=1/5/64",
+        "value": round(value_tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian weights quantised to uint4 g=128, Gaussian bf16 activations)",
+        "config": {"workload": "llama3-70b-w4a16-verify-sweep", "layers": 80, "linears_per_pass": len(specs),
+                   "passes_per_step": list(PASS_M), "group": 128, "weight_bytes": int(sum(
+                       s["N"] * s["K"] * 0.51953125 for s in specs)), "graph": True},
+        "us_per_pass": {str(M): round(us_per_pass[M], 1) for M in PASS_M},
+        "us_per_pass_eager": {str(M): round(us_eager[M], 1) for M in PASS_M},
+        "tbps_per_pass": {str(M): round(pass_bytes[M] / (us_per_pass[M] * 1e-6) / 1e12, 4) for M in PASS_M},
+        "roofline_frac_per_pass": {str(M): round(t_roof[M] / us_per_pass[M], 4) for M in PASS_M},
+        "t_over_t1": {str(M): round(us_per_pass[M] / us_per_pass[1], 4) for M in PASS_M},
+        "hbm_read_ceiling_tbps": round(ceiling / 1000, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "setup_s": round(t_model, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,8 +17,14 @@ constexpr int kTileN = kWaves * kChunkN;  // output columns per workgroup
 
 enum KernelId { kAuto = 0, kGemv = 1, kMfma = 2 };
 
+// Kernel variants behind the ids: the VALU GEMV (M = 1), the MFMA kernel
+// with A operands loaded straight from global memory (M <= 32), and the MFMA
+// kernel with activations staged through an LDS ring (M = 33..64).
+enum Variant { kVarGemv = 0, kVarDirect = 1, kVarLdsRing = 2 };
+
 struct Plan {
     int kernel;   // kGemv or kMfma
+    int variant;  // Variant
     int mb;       // m-blocks of 16 rows (MFMA)
     int splits;   // K splits (workgroups per column tile)
     int gps;      // groups per split

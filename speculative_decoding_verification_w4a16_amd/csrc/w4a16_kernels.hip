@@ -210,134 +210,197 @@ struct LinearArgs {
     uint32_t magic;  // 0x43004300: bf16 128.0 in both halves
 };
 
-// Stage x[0:M, g0*128 : g1*128] into LDS rows of `row_stride` bytes, then a
-// 64-byte zero line (the A operand of padded rows).
-__device__ __forceinline__ void stage_x(const LinearArgs& a, char* smem, int g0, int ng) {
-    const int per_row = ng * (kGroup / 8);  // 16-byte pieces per row
-    const int total = a.M * per_row;
-    for (int p = threadIdx.x; p < total; p += kThreads) {
-        const int m = p / per_row;
-        const int q = p - m * per_row;
-        const u32x4 v = *(const u32x4*)(a.x + (size_t)m * a.K + (size_t)g0 * kGroup + 8 * q);
-        *(u32x4*)(smem + m * a.row_stride + 16 * q) = v;
-    }
-    if (threadIdx.x < 4) *(u32x4*)(smem + a.M * a.row_stride + 16 * threadIdx.x) = u32x4{0, 0, 0, 0};
+// Workgroup barrier for an LDS producer/consumer hand-off.  It waits for this
+// wave's LDS operations only: __syncthreads() also waits for every
+// outstanding global load, which would drain the weight ring at each stage.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-// Split-K epilogue: the last workgroup of a column tile sums the partials in
-// split order (deterministic) and writes y; it then re-arms the counter.
+// Split-K partial sums travel through device memory with agent-scope (sc1)
+// stores and loads, which are made visible at, and read from, the device
+// coherence point directly.  No L2 write-back or invalidate is needed; those
+// (what __threadfence() emits) serialise per XCD and cost far more than the
+// kernel itself when every workgroup issues them.
+__device__ __forceinline__ void store_partial(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_partial(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Split-K epilogue: once every wave's partial stores are acknowledged at
+// agent scope, one thread counts the workgroup in; the last workgroup of a
+// column tile sums the partials in split order (deterministic), writes y and
+// re-arms the counter for the next launch.
 __device__ void splitk_fixup(const LinearArgs& a, int tile) {
     __shared__ int last;
-    __threadfence();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = (old == a.splits - 1);
     }
     __syncthreads();
     if (!last) return;
-    __threadfence();
     const size_t npad = (size_t)a.NC * kChunkN;
+    const size_t sstride = (size_t)a.M * npad;  // between splits
     const int n0 = tile * kTileN;
+    // Partials are fetched kFixBatch at a time (all in flight together) and
+    // added in split order; past the last split the index is clamped and the
+    // value replaced by zero, so the loads stay unconditional.
+    constexpr int kFixBatch = 16;
     for (int idx = threadIdx.x; idx < a.M * kTileN; idx += kThreads) {
         const int m = idx / kTileN;
-        const int n = n0 + (idx - m * kTileN);
-        if (n >= a.N) continue;
+        const int n = min(n0 + (idx - m * kTileN), a.N - 1);
+        const float* src = a.ws + (size_t)m * npad + n;
         float acc = 0.0f;
-        for (int s = 0; s < a.splits; ++s) acc += a.ws[((size_t)s * a.M + m) * npad + n];
-        a.y[(size_t)m * a.N + n] = acc;
+        for (int s0 = 0; s0 < a.splits; s0 += kFixBatch) {
+            float v[kFixBatch];
+#pragma unroll
+            for (int i = 0; i < kFixBatch; ++i) v[i] = load_partial(src + (size_t)min(s0 + i, a.splits - 1) * sstride);
+#pragma unroll
+            for (int i = 0; i < kFixBatch; ++i) acc += (s0 + i < a.splits) ? v[i] : 0.0f;
+        }
+        if (n0 + (idx - m * kTileN) < a.N) a.y[(size_t)m * a.N + n] = acc;
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Ring of weight loads: D groups (4 x 16 B per lane each) in flight.
-constexpr int kRing = 3;
+// Weight ring.  A wave keeps kRing groups of weights (4 x 16 bytes per lane
+// each, plus the group's scales and zeros) in flight ahead of the group it
+// computes.  Every slot is reloaded unconditionally right after its group is
+// consumed -- past the wave's last group the address is clamped to that group
+// (an L2 hit) -- so the compiler never has to merge an old and a new value of
+// a slot, which would force it to wait for the load it just issued.
+template <int R>
+struct WeightRing {
+    u32x4 w[R][4];
+    uint2 s[R];
+    uint32_t z[R];
+};
+
+struct WaveStream {
+    const u32x4* wp;    // first weight word of the wave's first group (lane offset applied)
+    const uint2* sp;    // scales of the first group (column offset applied)
+    const uint16_t* zp; // zeros of the first group
+};
+
+template <int R>
+__device__ __forceinline__ void ring_load(WeightRing<R>& ring, int slot, const WaveStream& ws, int gl) {
+    // keep the reload after the slot's last use: if the scheduler hoisted it,
+    // old and new values would be live together and the register allocator
+    // would insert copies that wait for the load
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) ring.w[slot][kk] = ws.wp[(gl * 4 + kk) * 64];
+    ring.s[slot] = ws.sp[gl * 16];
+    ring.z[slot] = ws.zp[gl * 16];
+}
+
+__device__ __forceinline__ WaveStream wave_stream(const LinearArgs& a, int c, int g0, int lane) {
+    WaveStream ws;
+    ws.wp = a.qt + ((size_t)c * a.KB + (size_t)g0 * 4) * 64 + lane;
+    ws.sp = a.st + ((size_t)c * a.G + g0) * 16 + (lane & 15);
+    ws.zp = a.zt + ((size_t)c * a.G + g0) * 16 + (lane & 15);
+    return ws;
+}
+
+__device__ __forceinline__ void decode_scales(uint2 sv, float (&sj)[4]) {
+    sj[0] = f16_bits_to_f32(sv.x & 0xFFFFu);
+    sj[1] = f16_bits_to_f32(sv.x >> 16);
+    sj[2] = f16_bits_to_f32(sv.y & 0xFFFFu);
+    sj[3] = f16_bits_to_f32(sv.y >> 16);
+}
 
 // ---------------------------------------------------------------------------
 // M = 1: VALU GEMV (bf16 dot2, fp32 accumulation, cross-lane shuffles)
 // ---------------------------------------------------------------------------
 //
 // Lane (o = l/16, t = l%16) accumulates, for its 4 columns 64c + 16j + t, the
-// k of octet o in every k-block; the four octet lanes of a column are summed
-// with two xor-shuffles at the end.
+// k of octet o in every k-block.  Its activation octets come straight from
+// global memory (x is only 2K bytes and stays in L1/L2) in the same load ring
+// as the weights, so a wave never waits on LDS or a barrier, and the
+// per-group sum of those octets (the zero-point term) is the lane's own.  The
+// four octet lanes of a column are summed with two xor-shuffles at the end.
 
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 (1.0, 1.0)
+
+// Groups of loads each wave keeps in flight (a slot is 4 weight words, the
+// activation pieces, one scale word and one zero word per lane; the total
+// stays under the 63 outstanding loads a wave can track).
+constexpr int kRingGemv = 4;
+constexpr int kRingDirect1 = 4;
+constexpr int kRingDirect2 = 3;
+
+template <int R>
 __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
-    extern __shared__ __align__(16) char smem[];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x / a.ntiles;
     const int tile = blockIdx.x - split * a.ntiles;
     const int g0 = split * a.gps;
     const int ng = min(a.G, g0 + a.gps) - g0;
     const int c = tile * kWaves + wave;
     const int o = lane >> 4, t = lane & 15;
+    const uint32_t mask = a.mask, magic = a.magic;
+    // waves past the last chunk stream the last chunk again (never stored):
+    // branch-free loads keep the compiler's wait counts exact
+    const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
+    const u32x4* xp = (const u32x4*)(a.x + (size_t)g0 * kGroup + 8 * o);  // 16-byte units
 
-    stage_x(a, smem, g0, ng);
-    __syncthreads();
-    // per (group, octet) sums of x: 32 values each
-    for (int p = threadIdx.x; p < ng * 4; p += kThreads) {
-        const int gl = p >> 2, oo = p & 3;
-        float acc = 0.0f;
+    u32x4 rw[R][4], rx[R][4];
+    uint2 rs[R];
+    uint32_t rz[R];
+    auto load = [&](int d, int gl) {
+        __builtin_amdgcn_sched_barrier(0);  // keep the reload after the slot's last use
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = sum8_bf16(*(const u32x4*)(smem + (gl * kGroup + kk * kKBlock + 8 * oo) * 2), acc);
-        *(float*)(smem + a.xs_off + p * 4) = acc;
-    }
-    __syncthreads();
+        for (int kk = 0; kk < 4; ++kk) rw[d][kk] = ws.wp[(gl * 4 + kk) * 64];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) rx[d][kk] = xp[gl * 16 + kk * 4];
+        rs[d] = ws.sp[gl * 16];
+        rz[d] = ws.zp[gl * 16];
+    };
 
     float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (c < a.NC) {
-        const uint32_t mask = a.mask, magic = a.magic;
-        const u32x4* wp = a.qt + ((size_t)c * a.KB + (size_t)g0 * 4) * 64 + lane;
-        const uint2* sp = a.st + ((size_t)c * a.G + g0) * 16 + t;
-        const uint16_t* zp = a.zt + ((size_t)c * a.G + g0) * 16 + t;
-
-        u32x4 wr[kRing][4];
-        uint2 sr[kRing];
-        uint32_t zr[kRing];
 #pragma unroll
-        for (int d = 0; d < kRing; ++d) {
-            if (d < ng) {
+    for (int d = 0; d < R; ++d) load(d, min(d, ng - 1));
+    for (int gb = 0; gb < ng; gb += R) {
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) wr[d][kk] = wp[(d * 4 + kk) * 64];
-                sr[d] = sp[d * 16];
-                zr[d] = zp[d * 16];
-            }
-        }
-        for (int gb = 0; gb < ng; gb += kRing) {
+        for (int d = 0; d < R; ++d) {
+            const int gl = gb + d;
+            if (gl < ng) {
+                float acc[4];
+                float xs = 0.0f;
 #pragma unroll
-            for (int d = 0; d < kRing; ++d) {
-                const int gl = gb + d;
-                if (gl < ng) {
-                    float acc[4];
+                for (int kk = 0; kk < 4; ++kk) {
+                    const u32x4 xa = rx[d][kk];
+                    const uint32_t x0 = xa[0], x1 = xa[1], x2 = xa[2], x3 = xa[3];
+                    xs = dot2(x0, kOnesBf16x2, xs);
+                    xs = dot2(x1, kOnesBf16x2, xs);
+                    xs = dot2(x2, kOnesBf16x2, xs);
+                    xs = dot2(x3, kOnesBf16x2, xs);
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const u32x4 xa = *(const u32x4*)(smem + (gl * kGroup + kk * kKBlock + 8 * o) * 2);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const u32x4 b = unpack_biased(wr[d][kk][j], mask, magic);
-                            float s0 = kk == 0 ? 0.0f : acc[j];
-                            s0 = dot2(b[0], xa[0], s0);
-                            s0 = dot2(b[1], xa[1], s0);
-                            s0 = dot2(b[2], xa[2], s0);
-                            s0 = dot2(b[3], xa[3], s0);
-                            acc[j] = s0;
-                        }
-                    }
-                    const float xs = *(const float*)(smem + a.xs_off + (gl * 4 + o) * 4);
-                    const uint2 sv = sr[d];
-                    const uint32_t zw = zr[d];
-                    const float sj[4] = {f16_bits_to_f32(sv.x & 0xFFFFu), f16_bits_to_f32(sv.x >> 16),
-                                         f16_bits_to_f32(sv.y & 0xFFFFu), f16_bits_to_f32(sv.y >> 16)};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) yv[j] = fmaf(sj[j], fmaf(-biased_zero(zw, j), xs, acc[j]), yv[j]);
-                    if (gl + kRing < ng) {
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk) wr[d][kk] = wp[((gl + kRing) * 4 + kk) * 64];
-                        sr[d] = sp[(gl + kRing) * 16];
-                        zr[d] = zp[(gl + kRing) * 16];
+                    for (int j = 0; j < 4; ++j) {
+                        const u32x4 b = unpack_biased(rw[d][kk][j], mask, magic);
+                        float s0 = kk == 0 ? 0.0f : acc[j];
+                        s0 = dot2(b[0], x0, s0);
+                        s0 = dot2(b[1], x1, s0);
+                        s0 = dot2(b[2], x2, s0);
+                        s0 = dot2(b[3], x3, s0);
+                        acc[j] = s0;
                     }
                 }
+                float sj[4];
+                decode_scales(rs[d], sj);
+                const uint32_t zw = rz[d];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) yv[j] = fmaf(sj[j], fmaf(-biased_zero(zw, j), xs, acc[j]), yv[j]);
             }
+            load(d, min(gl + R, ng - 1));
         }
     }
     // sum the four octet lanes of each column
@@ -354,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
                 if (a.splits == 1)
                     a.y[n] = yv[j];
                 else
-                    a.ws[(size_t)split * a.NC * kChunkN + n] = yv[j];
+                    store_partial(a.ws + (size_t)split * a.NC * kChunkN + n, yv[j]);
             }
         }
     }
@@ -362,7 +425,130 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// M = 2..64: bf16 MFMA, split-K, activations streamed through an LDS ring
+// M = 1..32: bf16 MFMA with activations loaded straight into A operands
+// ---------------------------------------------------------------------------
+//
+// For small M the activation rows are tiny and L1/L2-resident, so each lane
+// loads its own A operand (row 16mb + l%16, k-octet l/16 of each k-block)
+// from global memory in the same ring as the weights: no LDS, no barriers.
+// Rows past M are zeroed in registers.  One extra MFMA per k-block against an
+// all-ones B operand yields the per-(row, group) sums of x that the
+// zero-point term needs, already in the result layout (rows 4(l/16) + r).
+
+template <int MB, int R>
+__global__ __launch_bounds__(kThreads) void w4a16_mfma_direct_kernel(LinearArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int split = blockIdx.x / a.ntiles;
+    const int tile = blockIdx.x - split * a.ntiles;
+    const int g0 = split * a.gps;
+    const int ng = min(a.G, g0 + a.gps) - g0;
+    const int c = tile * kWaves + wave;
+    const int o = lane >> 4, t = lane & 15;
+    const uint32_t mask = a.mask, magic = a.magic;
+    const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
+    const u32x4* xp[MB];
+    bool xvalid[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int row = 16 * mb + t;
+        xvalid[mb] = row < a.M;
+        xp[mb] = (const u32x4*)(a.x + (size_t)min(row, a.M - 1) * a.K + (size_t)g0 * kGroup + 8 * o);
+    }
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2});
+
+    u32x4 rw[R][4], rx[R][4][MB];
+    uint2 rs[R];
+    uint32_t rz[R];
+    auto load = [&](int d, int gl) {
+        __builtin_amdgcn_sched_barrier(0);  // keep the reload after the slot's last use
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) rw[d][kk] = ws.wp[(gl * 4 + kk) * 64];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) rx[d][kk][mb] = xp[mb][gl * 16 + kk * 4];
+        rs[d] = ws.sp[gl * 16];
+        rz[d] = ws.zp[gl * 16];
+    };
+
+    f32x4 yv[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yv[mb][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+    for (int d = 0; d < R; ++d) load(d, min(d, ng - 1));
+    for (int gb = 0; gb < ng; gb += R) {
+#pragma unroll
+        for (int d = 0; d < R; ++d) {
+            const int gl = gb + d;
+            if (gl < ng) {
+                f32x4 acc[MB][4], accx[MB];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    bf16x8 av[MB];
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const u32x4 raw = xvalid[mb] ? rx[d][kk][mb] : u32x4{0, 0, 0, 0};
+                        av[mb] = __builtin_bit_cast(bf16x8, raw);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const u32x4 braw = unpack_biased(rw[d][kk][j], mask, magic);
+                        const bf16x8 bv = __builtin_bit_cast(bf16x8, braw);
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb)
+                            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                av[mb], bv, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][j], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        accx[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            av[mb], ones, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : accx[mb], 0, 0, 0);
+                }
+                float sj[4];
+                decode_scales(rs[d], sj);
+                const uint32_t zw = rz[d];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float cz = biased_zero(zw, j);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            yv[mb][j][r] = fmaf(sj[j], fmaf(-cz, accx[mb][r], acc[mb][j][r]), yv[mb][j][r]);
+                    }
+            }
+            load(d, min(gl + R, ng - 1));
+        }
+    }
+
+    if (c < a.NC) {
+        const size_t npad = (size_t)a.NC * kChunkN;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int n = c * kChunkN + 16 * j + t;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 16 * mb + 4 * o + r;
+                    if (m < a.M && n < a.N) {
+                        if (a.splits == 1)
+                            a.y[(size_t)m * a.N + n] = yv[mb][j][r];
+                        else
+                            store_partial(a.ws + ((size_t)split * a.M + m) * npad + n, yv[mb][j][r]);
+                    }
+                }
+            }
+    }
+    if (a.splits > 1) splitk_fixup(a, tile);
+}
+
+// ---------------------------------------------------------------------------
+// M = 33..64: bf16 MFMA, split-K, activations streamed through an LDS ring
 // ---------------------------------------------------------------------------
 //
 // A operand (activations, 16 rows x 32 k per m-block) comes from a
@@ -404,8 +590,11 @@ __device__ __forceinline__ void mfma_load_x(const LinearArgs& a, int g0, int ng,
         const int rem = p - m * (kStage * 16);
         const int gl = st * kStage + (rem >> 4);
         const int q = rem & 15;
-        xr[i] = u32x4{0, 0, 0, 0};
-        if (m < a.M && gl < ng) xr[i] = *(const u32x4*)(a.x + (size_t)m * a.K + (size_t)(g0 + gl) * kGroup + 8 * q);
+        // every lane loads (an in-range piece when its own is past the end;
+        // mfma_store_x drops those): no divergent loads in the pipelined loop
+        const bool valid = m < a.M && gl < ng;
+        const int mm = valid ? m : 0, gg = valid ? gl : 0;
+        xr[i] = *(const u32x4*)(a.x + (size_t)mm * a.K + (size_t)(g0 + gg) * kGroup + 8 * q);
     }
 }
 
@@ -422,7 +611,7 @@ __device__ __forceinline__ void mfma_store_x(const LinearArgs& a, const MfmaLds&
         const int q = rem & 15;
         const bool valid = m < a.M && gs < g_in_stage_max;
         if (valid) *(u32x4*)(buf + m * L.row_stride + gs * kGroup * 2 + 16 * q) = xr[i];
-        float s = sum8_bf16(xr[i], 0.0f);
+        float s = valid ? sum8_bf16(xr[i], 0.0f) : 0.0f;
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         s += __shfl_xor(s, 4);
@@ -435,8 +624,9 @@ template <int MB>
 __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(LinearArgs a) {
     extern __shared__ __align__(16) char smem[];
     constexpr int XSW = 16 * MB;  // x sums per group (rows, padded to the m-blocks)
+    constexpr int R = 2 * kStage; // groups of weights in flight: two LDS stages
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x / a.ntiles;
     const int tile = blockIdx.x - split * a.ntiles;
     const int g0 = split * a.gps;
@@ -468,9 +658,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(LinearArgs a) {
         for (int j = 0; j < 4; ++j) yv[mb][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const uint32_t mask = a.mask, magic = a.magic;
-    const u32x4* wp = a.qt + ((size_t)(active ? c : 0) * a.KB + (size_t)g0 * 4) * 64 + lane;
-    const uint2* sp = a.st + ((size_t)(active ? c : 0) * a.G + g0) * 16 + t;
-    const uint16_t* zp = a.zt + ((size_t)(active ? c : 0) * a.G + g0) * 16 + t;
+    // waves past the last chunk stream the last chunk again (never stored):
+    // branch-free loads keep the compiler's wait counts exact
+    const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
     int aoff[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -479,60 +669,54 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(LinearArgs a) {
     }
     const int xs_lane = L.xs_off + 4 * (4 * o);
 
-    // weight ring: kStage groups in flight ahead of the one being computed
-    constexpr int R = 2 * kStage;
-    u32x4 wr[R][4];
-    uint2 sr[R];
-    uint32_t zr[R];
-    if (active) {
+    WeightRing<R> ring;
 #pragma unroll
-        for (int d = 0; d < R; ++d) {
-            if (d < ng) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) wr[d][kk] = wp[(d * 4 + kk) * 64];
-                sr[d] = sp[d * 16];
-                zr[d] = zp[d * 16];
-            }
-        }
-    }
+    for (int d = 0; d < R; ++d) ring_load(ring, d, ws, min(d, ng - 1));
 
-    u32x4 xr[MB * kStage];  // next stage's activations, in flight during a stage
-    for (int gb = 0; gb < ng; gb += R) {
+    // Two LDS stages per iteration, one ring slot per group.  Compute and the
+    // stage bookkeeping sit in wave-uniform branches; the ring reloads do not.
+    for (int sp = 0; sp < nst; sp += 2) {
 #pragma unroll
-        for (int d = 0; d < R; ++d) {
-            const int gl = gb + d;
-            if (gl < ng) {
-                const int st = gl / kStage;
-                const int gs = gl - st * kStage;
-                if (gs == 0 && st + 1 < nst) mfma_load_x<MB>(a, g0, ng, st + 1, xr);
-                const char* buf = smem + (st & 1) * L.buf;
-                if (active) {
+        for (int h = 0; h < 2; ++h) {
+            const int st = sp + h;
+            u32x4 xr[MB * kStage];  // the next stage's activations
+            mfma_load_x<MB>(a, g0, ng, min(st + 1, nst - 1), xr);
+            // pin the loads here: sunk to their use at the end of the stage
+            // they would make the wave wait for them right away
+            asm volatile("" ::: "memory");
+            const int bufo = (st & 1) * L.buf;
+#pragma unroll
+            for (int gs = 0; gs < kStage; ++gs) {
+                const int d = h * kStage + gs;
+                const int gl = st * kStage + gs;
+                if (active && gl < ng) {
                     f32x4 acc[MB][4];
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
                         bf16x8 av[MB];
 #pragma unroll
                         for (int mb = 0; mb < MB; ++mb) {
-                            const int off = 16 * mb + t < a.M ? (st & 1) * L.buf + aoff[mb] + (gs * kGroup + kk * kKBlock) * 2
+                            const int off = 16 * mb + t < a.M ? bufo + aoff[mb] + (gs * kGroup + kk * kKBlock) * 2
                                                               : aoff[mb];
-                            av[mb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + off));
+                            const u32x4 araw = *(const u32x4*)(smem + off);
+                            av[mb] = __builtin_bit_cast(bf16x8, araw);
                         }
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const bf16x8 bv = __builtin_bit_cast(bf16x8, unpack_biased(wr[d][kk][j], mask, magic));
+                            const u32x4 braw = unpack_biased(ring.w[d][kk][j], mask, magic);
+                            const bf16x8 bv = __builtin_bit_cast(bf16x8, braw);
 #pragma unroll
                             for (int mb = 0; mb < MB; ++mb)
                                 acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                     av[mb], bv, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][j], 0, 0, 0);
                         }
                     }
-                    const uint2 sv = sr[d];
-                    const uint32_t zw = zr[d];
-                    const float sj[4] = {f16_bits_to_f32(sv.x & 0xFFFFu), f16_bits_to_f32(sv.x >> 16),
-                                         f16_bits_to_f32(sv.y & 0xFFFFu), f16_bits_to_f32(sv.y >> 16)};
+                    float sj[4];
+                    decode_scales(ring.s[d], sj);
+                    const uint32_t zw = ring.z[d];
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
-                        const f32x4 xs = *(const f32x4*)(buf + xs_lane + (gs * XSW + 16 * mb) * 4);
+                        const f32x4 xs = *(const f32x4*)(smem + bufo + xs_lane + (gs * XSW + 16 * mb) * 4);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const float cz = biased_zero(zw, j);
@@ -541,21 +725,14 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(LinearArgs a) {
                                 yv[mb][j][r] = fmaf(sj[j], fmaf(-cz, xs[r], acc[mb][j][r]), yv[mb][j][r]);
                         }
                     }
-                    if (gl + R < ng) {
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk) wr[d][kk] = wp[((gl + R) * 4 + kk) * 64];
-                        sr[d] = sp[(gl + R) * 16];
-                        zr[d] = zp[(gl + R) * 16];
-                    }
                 }
-                if (gs == kStage - 1 || gl == ng - 1) {
-                    if (st + 1 < nst) {
-                        // everyone finished stage st-1, whose buffer this is
-                        mfma_store_x<MB>(a, L, smem + ((st + 1) & 1) * L.buf, min(kStage, ng - (st + 1) * kStage),
-                                         xr);
-                    }
-                    __syncthreads();
-                }
+                ring_load(ring, d, ws, min(gl + R, ng - 1));
+            }
+            if (st < nst) {
+                // every wave has finished stage st-1, whose buffer this is
+                if (st + 1 < nst)
+                    mfma_store_x<MB>(a, L, smem + ((st + 1) & 1) * L.buf, min(kStage, ng - (st + 1) * kStage), xr);
+                lds_barrier();
             }
         }
     }
@@ -574,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(LinearArgs a) {
                         if (a.splits == 1)
                             a.y[(size_t)m * a.N + n] = yv[mb][j][r];
                         else
-                            a.ws[((size_t)split * a.M + m) * npad + n] = yv[mb][j][r];
+                            store_partial(a.ws + ((size_t)split * a.M + m) * npad + n, yv[mb][j][r]);
                     }
                 }
             }
@@ -627,15 +804,6 @@ __global__ __launch_bounds__(256) void bench_copy_kernel(u32x4* __restrict__ dst
 
 static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
-// LDS bytes of the GEMV kernel with `gps` groups per split (the whole
-// K-range of x is staged once).
-static int gemv_lds(int gps, int* row_stride, int* xs_off) {
-    const int rs = gps * kGroup * 2 + 16;
-    if (row_stride) *row_stride = rs;
-    if (xs_off) *xs_off = rs + 64;
-    return rs + 64 + gps * 4 * 4;
-}
-
 int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Plan* p) {
     if (kernel == kAuto) kernel = (M == 1) ? kGemv : kMfma;
     if (kernel == kGemv && M != 1) return -1;
@@ -643,44 +811,44 @@ int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Pl
     const int G = K / kGroup;
     const int ntiles = ceil_div(NC, kWaves);
     const int mb = ceil_div(M, 16);
-    // GEMV stages its whole K-range of x; the MFMA kernel streams it
-    int gmax = G;
-    if (kernel == kGemv)
-        while (gmax > 1 && gemv_lds(gmax, nullptr, nullptr) > kLdsLimit) --gmax;
+    const int variant = kernel == kGemv ? kVarGemv : (mb <= 2 ? kVarDirect : kVarLdsRing);
     int S;
     if (splits > 0) {
         S = splits;
     } else {
-        // aim for ~2 workgroups per CU (256 CUs), fewer splits when the
-        // partial sums would be a large fraction of the weight bytes
-        const int target = 512;
-        S = ceil_div(target, ntiles);
+        // Measured on MI355X: about one workgroup per CU (256) streams best;
+        // more workgroups add per-workgroup start-up and split-K fix-up cost
+        // without adding bandwidth.  Keep >= 4 groups per wave so a wave's
+        // load ring is full, and the split-K partial traffic under half the
+        // weight bytes.
+        const int target_wgs = 256;
+        S = ceil_div(target_wgs, ntiles);
+        S = std::min(S, std::max(1, G / 4));
         const long weight_bytes = (long)NC * kChunkN * K / 2;
-        const long partial_per_split = (long)M * NC * kChunkN * 4;
-        const int s_traffic = (int)std::max<long>(1, weight_bytes / (4 * partial_per_split));
+        const long partial_per_split = (long)M * NC * kChunkN * 4 * 2;  // written + read
+        const int s_traffic = (int)std::max<long>(1, weight_bytes / (2 * partial_per_split));
         S = std::min(S, s_traffic);
     }
     S = std::max(1, std::min(S, G));
     int gps = ceil_div(G, S);
-    if (gps > gmax) gps = gmax;
     S = ceil_div(G, gps);
     // the split-K workspace must hold S partial [M][NC*64] tiles
     while (S > 1 && (size_t)S * M * NC * kChunkN * 4 > ws_bytes) {
-        if (gps >= gmax) return -2;
         ++gps;
         S = ceil_div(G, gps);
     }
     if (S > 1 && ntiles > kCounters) return -2;
     p->kernel = kernel;
+    p->variant = variant;
     p->mb = mb;
     p->splits = S;
     p->gps = gps;
     p->ntiles = ntiles;
     p->grid = ntiles * S;
     p->block = kThreads;
-    if (kernel == kGemv) {
-        p->lds = gemv_lds(gps, &p->row_stride, nullptr);
-    } else {
+    p->lds = 0;
+    p->row_stride = 0;
+    if (variant == kVarLdsRing) {
         const MfmaLds L = mfma_lds(M, mb);
         p->lds = L.total;
         p->row_stride = L.row_stride;
@@ -689,14 +857,8 @@ int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Pl
 }
 
 hipError_t set_kernel_attributes() {
-    hipError_t e;
-    e = hipFuncSetAttribute((const void*)w4a16_gemv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)w4a16_mfma_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)w4a16_mfma_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)w4a16_mfma_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+    hipError_t e = hipFuncSetAttribute((const void*)w4a16_mfma_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kLdsLimit);
     if (e != hipSuccess) return e;
     return hipFuncSetAttribute((const void*)w4a16_mfma_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                kLdsLimit);
@@ -763,18 +925,19 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
     a.gps = p.gps;
     a.splits = p.splits;
     a.ntiles = p.ntiles;
-    a.row_stride = 0;
+    a.row_stride = p.row_stride;
     a.xs_off = 0;
     a.mask = kNibbleMask;
     a.magic = kBiasMagic;
-    if (p.kernel == kGemv) gemv_lds(p.gps, &a.row_stride, &a.xs_off);
     const dim3 grid(p.grid), block(p.block);
-    if (p.kernel == kGemv) return launch(w4a16_gemv_kernel, grid, block, p.lds, stream, a);
-    switch (p.mb) {
-        case 1: return launch(w4a16_mfma_kernel<1>, grid, block, p.lds, stream, a);
-        case 2: return launch(w4a16_mfma_kernel<2>, grid, block, p.lds, stream, a);
-        case 3: return launch(w4a16_mfma_kernel<3>, grid, block, p.lds, stream, a);
-        default: return launch(w4a16_mfma_kernel<4>, grid, block, p.lds, stream, a);
+    switch (p.variant) {
+        case kVarGemv: return launch(w4a16_gemv_kernel<kRingGemv>, grid, block, 0, stream, a);
+        case kVarDirect:
+            if (p.mb == 1) return launch(w4a16_mfma_direct_kernel<1, kRingDirect1>, grid, block, 0, stream, a);
+            return launch(w4a16_mfma_direct_kernel<2, kRingDirect2>, grid, block, 0, stream, a);
+        default:
+            if (p.mb == 3) return launch(w4a16_mfma_kernel<3>, grid, block, p.lds, stream, a);
+            return launch(w4a16_mfma_kernel<4>, grid, block, p.lds, stream, a);
     }
 }
 
