@@ -19,8 +19,9 @@ enum KernelId { kAuto = 0, kGemv = 1, kMfma = 2 };
 
 // Kernel variants behind the ids: the VALU GEMV (M = 1), the MFMA kernel
 // with A operands loaded straight from global memory (M <= 32), and the MFMA
-// kernel with activations staged through an LDS ring (M = 33..64).
-enum Variant { kVarGemv = 0, kVarDirect = 1, kVarLdsRing = 2 };
+// kernel with two waves per chunk and activations staged through an LDS ring
+// (M = 33..64).
+enum Variant { kVarGemv = 0, kVarDirect = 1, kVarWide = 2 };
 
 struct Plan {
     int kernel;   // kGemv or kMfma
@@ -28,7 +29,7 @@ struct Plan {
     int mb;       // m-blocks of 16 rows (MFMA)
     int splits;   // K splits (workgroups per column tile)
     int gps;      // groups per split
-    int ntiles;   // column tiles of kTileN
+    int ntiles;   // column tiles (kTileN columns, 128 for the wide variant)
     int grid;     // workgroups
     int block;    // threads per workgroup
     int lds;      // dynamic LDS bytes per workgroup

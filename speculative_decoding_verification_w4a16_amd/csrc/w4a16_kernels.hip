@@ -236,6 +236,7 @@ __device__ __forceinline__ float load_partial(const float* p) {
 // agent scope, one thread counts the workgroup in; the last workgroup of a
 // column tile sums the partials in split order (deterministic), writes y and
 // re-arms the counter for the next launch.
+template <int TW>
 __device__ void splitk_fixup(const LinearArgs& a, int tile) {
     __shared__ int last;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -246,26 +247,40 @@ __device__ void splitk_fixup(const LinearArgs& a, int tile) {
     }
     __syncthreads();
     if (!last) return;
+    // Thread i owns column n0 + i % TW of the tile and every (kThreads/TW)-th
+    // row from i / TW.  Partials are fetched in batches of kFixRows rows x
+    // kFixSplits splits, all in flight together, and added in split order;
+    // indices past the end are clamped and their values replaced by zero, so
+    // the loads stay unconditional.
+    static_assert(kThreads % TW == 0, "tile width divides the workgroup");
+    constexpr int kRowStep = kThreads / TW;
+    constexpr int kFixRows = 4, kFixSplits = 8;
     const size_t npad = (size_t)a.NC * kChunkN;
     const size_t sstride = (size_t)a.M * npad;  // between splits
-    const int n0 = tile * kTileN;
-    // Partials are fetched kFixBatch at a time (all in flight together) and
-    // added in split order; past the last split the index is clamped and the
-    // value replaced by zero, so the loads stay unconditional.
-    constexpr int kFixBatch = 16;
-    for (int idx = threadIdx.x; idx < a.M * kTileN; idx += kThreads) {
-        const int m = idx / kTileN;
-        const int n = min(n0 + (idx - m * kTileN), a.N - 1);
-        const float* src = a.ws + (size_t)m * npad + n;
-        float acc = 0.0f;
-        for (int s0 = 0; s0 < a.splits; s0 += kFixBatch) {
-            float v[kFixBatch];
+    const int nt = tile * TW + (int)(threadIdx.x % TW);
+    const int n = min(nt, a.N - 1);
+    const int mfirst = threadIdx.x / TW;
+    for (int mb0 = 0; mb0 < a.M; mb0 += kFixRows * kRowStep) {
+        const int m0 = mb0 + mfirst;  // rows m0, m0 + kRowStep, ...
+        float acc[kFixRows] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s0 = 0; s0 < a.splits; s0 += kFixSplits) {
+            float v[kFixRows][kFixSplits];
 #pragma unroll
-            for (int i = 0; i < kFixBatch; ++i) v[i] = load_partial(src + (size_t)min(s0 + i, a.splits - 1) * sstride);
+            for (int e = 0; e < kFixRows; ++e)
 #pragma unroll
-            for (int i = 0; i < kFixBatch; ++i) acc += (s0 + i < a.splits) ? v[i] : 0.0f;
+                for (int i = 0; i < kFixSplits; ++i)
+                    v[e][i] = load_partial(a.ws + (size_t)min(s0 + i, a.splits - 1) * sstride +
+                                           (size_t)min(m0 + e * kRowStep, a.M - 1) * npad + n);
+#pragma unroll
+            for (int e = 0; e < kFixRows; ++e)
+#pragma unroll
+                for (int i = 0; i < kFixSplits; ++i) acc[e] += (s0 + i < a.splits) ? v[e][i] : 0.0f;
         }
-        if (n0 + (idx - m * kTileN) < a.N) a.y[(size_t)m * a.N + n] = acc;
+#pragma unroll
+        for (int e = 0; e < kFixRows; ++e) {
+            const int m = m0 + e * kRowStep;
+            if (m < a.M && nt < a.N) a.y[(size_t)m * a.N + n] = acc[e];
+        }
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -421,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
             }
         }
     }
-    if (a.splits > 1) splitk_fixup(a, tile);
+    if (a.splits > 1) splitk_fixup<kTileN>(a, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -544,219 +559,215 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_direct_kernel(LinearArgs 
                 }
             }
     }
-    if (a.splits > 1) splitk_fixup(a, tile);
+    if (a.splits > 1) splitk_fixup<kTileN>(a, tile);
 }
 
 // ---------------------------------------------------------------------------
-// M = 33..64: bf16 MFMA, split-K, activations streamed through an LDS ring
+// M = 33..64: bf16 MFMA, two waves per 64-column chunk, LDS-staged activations
 // ---------------------------------------------------------------------------
 //
-// A operand (activations, 16 rows x 32 k per m-block) comes from a
-// double-buffered LDS ring of kStage groups per stage; B operand (weights,
-// 32 k x 16 columns) is unpacked in registers from the 128-bit weight load.
-// Lane l of a 16x16 fp32 MFMA result holds rows 4(l/16) + r, r = 0..3, of
-// column l%16.  While a stage is computed the next stage's activations are
-// loaded into registers; at the end of the stage they are written to the
-// other LDS buffer together with their per-(row, group) sums, reduced over
-// the 16 lanes that hold one row-group (fixed order, deterministic).
+// A workgroup covers two chunks (128 columns); each wave owns two of a
+// chunk's four n-tiles and reads its 8-byte half of every lane's 16-byte tile
+// word (the two waves of a chunk share cache lines, so HBM sees each byte
+// once).  Splitting columns rather than rows halves the per-wave MFMA
+// accumulators, which keeps a wave under 256 registers: two waves per SIMD
+// then overlap one wave's MFMAs with the other's unpack and epilogue VALU.
+// The activation rows of the next group are loaded into registers while the
+// current one is computed, written to the other half of a double-buffered LDS
+// ring at the end of the group together with their per-(row, group) sums
+// (reduced over the 16 lanes of a row piece with DPP), and handed over with
+// an LDS-only barrier.
 
-constexpr int kStage = 2;  // groups per LDS stage
+constexpr int kWideRing = 4;
+constexpr int kWideTileN = 2 * kChunkN;
 
-struct MfmaLds {
-    int row_stride;  // bytes per staged row (kStage groups + 16 bytes of skew)
-    int xs_off;      // offset of the x sums inside a buffer
+struct WideLds {
+    int row_stride;  // one group of a row (256 bytes) plus 16 bytes of skew
+    int xs_off;      // per-row group sums inside a buffer
     int buf;         // bytes per buffer
-    int zero_off;    // offset of the 64-byte zero line
+    int zero_off;    // 64-byte zero line for padded A rows
     int total;
 };
 
-__host__ __device__ inline MfmaLds mfma_lds(int M, int mb) {
-    MfmaLds l;
-    l.row_stride = kStage * kGroup * 2 + 16;
+__host__ __device__ inline WideLds wide_lds(int M, int mb) {
+    WideLds l;
+    l.row_stride = kGroup * 2 + 16;
     l.xs_off = M * l.row_stride;
-    l.buf = (l.xs_off + kStage * 16 * mb * 4 + 15) & ~15;
+    l.buf = (l.xs_off + 16 * mb * 4 + 15) & ~15;
     l.zero_off = 2 * l.buf;
     l.total = l.zero_off + 64;
     return l;
 }
 
-// Load the activation pieces of stage `st` (16 bytes of one row-group each).
+// Sum over the 16 lanes of a DPP row (every lane gets the total; the add
+// tree is the same in every lane, so the result is identical across lanes).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+    return v;
+}
+
+// Activation pieces of group `gl` (16 bytes of one row each; thread p takes
+// row p/16, piece p%16).  Rows past M and groups past the split load an
+// in-range piece that wide_store_x drops.
 template <int MB>
-__device__ __forceinline__ void mfma_load_x(const LinearArgs& a, int g0, int ng, int st, u32x4 (&xr)[MB * kStage]) {
+__device__ __forceinline__ void wide_load_x(const LinearArgs& a, int g0, int ng, int gl, u32x4 (&xr)[MB]) {
+    const int gg = min(gl, ng - 1);
 #pragma unroll
-    for (int i = 0; i < MB * kStage; ++i) {
+    for (int i = 0; i < MB; ++i) {
         const int p = threadIdx.x + kThreads * i;
-        const int m = p / (kStage * 16);
-        const int rem = p - m * (kStage * 16);
-        const int gl = st * kStage + (rem >> 4);
-        const int q = rem & 15;
-        // every lane loads (an in-range piece when its own is past the end;
-        // mfma_store_x drops those): no divergent loads in the pipelined loop
-        const bool valid = m < a.M && gl < ng;
-        const int mm = valid ? m : 0, gg = valid ? gl : 0;
+        const int m = p >> 4, q = p & 15;
+        const int mm = m < a.M ? m : 0;
         xr[i] = *(const u32x4*)(a.x + (size_t)mm * a.K + (size_t)(g0 + gg) * kGroup + 8 * q);
     }
 }
 
 template <int MB>
-__device__ __forceinline__ void mfma_store_x(const LinearArgs& a, const MfmaLds& L, char* buf, int g_in_stage_max,
-                                             const u32x4 (&xr)[MB * kStage]) {
-    constexpr int XSW = 16 * MB;
+__device__ __forceinline__ void wide_store_x(const LinearArgs& a, const WideLds& L, char* buf,
+                                             const u32x4 (&xr)[MB]) {
 #pragma unroll
-    for (int i = 0; i < MB * kStage; ++i) {
+    for (int i = 0; i < MB; ++i) {
         const int p = threadIdx.x + kThreads * i;
-        const int m = p / (kStage * 16);
-        const int rem = p - m * (kStage * 16);
-        const int gs = rem >> 4;
-        const int q = rem & 15;
-        const bool valid = m < a.M && gs < g_in_stage_max;
-        if (valid) *(u32x4*)(buf + m * L.row_stride + gs * kGroup * 2 + 16 * q) = xr[i];
-        float s = valid ? sum8_bf16(xr[i], 0.0f) : 0.0f;
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if (valid && q == 0) *(float*)(buf + L.xs_off + (gs * XSW + m) * 4) = s;
+        const int m = p >> 4, q = p & 15;
+        const bool valid = m < a.M;
+        if (valid) *(u32x4*)(buf + m * L.row_stride + 16 * q) = xr[i];
+        const float s = row16_sum(valid ? sum8_bf16(xr[i], 0.0f) : 0.0f);
+        if (valid && q == 0) *(float*)(buf + L.xs_off + m * 4) = s;
     }
 }
 
-template <int MB>
-__global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(LinearArgs a) {
+template <int MB, int R>
+__global__ __launch_bounds__(kThreads) void w4a16_mfma_wide_kernel(LinearArgs a) {
     extern __shared__ __align__(16) char smem[];
-    constexpr int XSW = 16 * MB;  // x sums per group (rows, padded to the m-blocks)
-    constexpr int R = 2 * kStage; // groups of weights in flight: two LDS stages
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int split = blockIdx.x / a.ntiles;
     const int tile = blockIdx.x - split * a.ntiles;
     const int g0 = split * a.gps;
     const int ng = min(a.G, g0 + a.gps) - g0;
-    const int nst = (ng + kStage - 1) / kStage;
-    const int c = tile * kWaves + wave;
-    const bool active = c < a.NC;
+    const int c = tile * 2 + (wave >> 1);
+    const int h = wave & 1;  // n-tiles 2h, 2h+1 of the chunk
     const int o = lane >> 4, t = lane & 15;
-    const MfmaLds L = mfma_lds(a.M, MB);
+    const uint32_t mask = a.mask, magic = a.magic;
+    const WideLds L = wide_lds(a.M, MB);
 
     // sums of padded rows stay zero; the zero line feeds padded A rows
-    for (int p = threadIdx.x; p < 2 * kStage * XSW; p += kThreads) {
-        const int b = p / (kStage * XSW), r = p - b * (kStage * XSW);
-        *(float*)(smem + b * L.buf + L.xs_off + r * 4) = 0.0f;
+    for (int p = threadIdx.x; p < 2 * 16 * MB; p += kThreads) {
+        const int b = p / (16 * MB), r = p - b * (16 * MB);
+        if (r >= a.M) *(float*)(smem + b * L.buf + L.xs_off + r * 4) = 0.0f;
     }
     if (threadIdx.x < 4) *(u32x4*)(smem + L.zero_off + 16 * threadIdx.x) = u32x4{0, 0, 0, 0};
-    __syncthreads();
+
+    // weights: this wave's 8-byte half of each lane word; waves past the last
+    // chunk stream the last chunk again (never stored)
+    const int cc = min(c, a.NC - 1);
+    const uint2* wp = (const uint2*)a.qt + (((size_t)cc * a.KB + (size_t)g0 * 4) * 64 + lane) * 2 + h;
+    const uint32_t* sp = (const uint32_t*)a.st + ((size_t)cc * a.G + g0) * 32 + t * 2 + h;
+    const uint16_t* zp = a.zt + ((size_t)cc * a.G + g0) * 16 + t;
+    uint2 rw[R][4];
+    uint32_t rs[R], rz[R];
+    auto load = [&](int d, int gl) {
+        __builtin_amdgcn_sched_barrier(0);  // keep the reload after the slot's last use
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) rw[d][kk] = wp[(gl * 4 + kk) * 128];
+        rs[d] = sp[gl * 32];
+        rz[d] = zp[gl * 16];
+    };
     {
-        u32x4 xr[MB * kStage];
-        mfma_load_x<MB>(a, g0, ng, 0, xr);
-        mfma_store_x<MB>(a, L, smem, min(kStage, ng), xr);
+        u32x4 xr[MB];
+        wide_load_x<MB>(a, g0, ng, 0, xr);
+#pragma unroll
+        for (int d = 0; d < R; ++d) load(d, min(d, ng - 1));
+        wide_store_x<MB>(a, L, smem, xr);
+        lds_barrier();  // group 0's rows, sums, the zeroed sums and the zero line
     }
-    __syncthreads();
 
-    f32x4 yv[MB][4];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) yv[mb][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const uint32_t mask = a.mask, magic = a.magic;
-    // waves past the last chunk stream the last chunk again (never stored):
-    // branch-free loads keep the compiler's wait counts exact
-    const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
     int aoff[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int row = 16 * mb + t;
-        aoff[mb] = (row < a.M ? row * L.row_stride : L.zero_off) + 16 * o;
+        aoff[mb] = row < a.M ? row * L.row_stride + 16 * o : -1;
     }
-    const int xs_lane = L.xs_off + 4 * (4 * o);
+    const int zero_lane = L.zero_off + 16 * o;
 
-    WeightRing<R> ring;
+    f32x4 yv[MB][2];
 #pragma unroll
-    for (int d = 0; d < R; ++d) ring_load(ring, d, ws, min(d, ng - 1));
+    for (int mb = 0; mb < MB; ++mb) yv[mb][0] = yv[mb][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Two LDS stages per iteration, one ring slot per group.  Compute and the
-    // stage bookkeeping sit in wave-uniform branches; the ring reloads do not.
-    for (int sp = 0; sp < nst; sp += 2) {
+    for (int gb = 0; gb < ng; gb += R) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int st = sp + h;
-            u32x4 xr[MB * kStage];  // the next stage's activations
-            mfma_load_x<MB>(a, g0, ng, min(st + 1, nst - 1), xr);
-            // pin the loads here: sunk to their use at the end of the stage
-            // they would make the wave wait for them right away
-            asm volatile("" ::: "memory");
-            const int bufo = (st & 1) * L.buf;
+        for (int d = 0; d < R; ++d) {
+            const int gl = gb + d;
+            u32x4 xr[MB];  // the next group's activations
+            wide_load_x<MB>(a, g0, ng, gl + 1, xr);
+            asm volatile("" ::: "memory");  // keep those loads here, ahead of the compute
+            const int bufo = (gl & 1) * L.buf;
+            if (gl < ng) {
+                f32x4 acc[MB][2];
 #pragma unroll
-            for (int gs = 0; gs < kStage; ++gs) {
-                const int d = h * kStage + gs;
-                const int gl = st * kStage + gs;
-                if (active && gl < ng) {
-                    f32x4 acc[MB][4];
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        bf16x8 av[MB];
-#pragma unroll
-                        for (int mb = 0; mb < MB; ++mb) {
-                            const int off = 16 * mb + t < a.M ? bufo + aoff[mb] + (gs * kGroup + kk * kKBlock) * 2
-                                                              : aoff[mb];
-                            const u32x4 araw = *(const u32x4*)(smem + off);
-                            av[mb] = __builtin_bit_cast(bf16x8, araw);
-                        }
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const u32x4 braw = unpack_biased(ring.w[d][kk][j], mask, magic);
-                            const bf16x8 bv = __builtin_bit_cast(bf16x8, braw);
-#pragma unroll
-                            for (int mb = 0; mb < MB; ++mb)
-                                acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    av[mb], bv, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][j], 0, 0, 0);
-                        }
-                    }
-                    float sj[4];
-                    decode_scales(ring.s[d], sj);
-                    const uint32_t zw = ring.z[d];
+                for (int kk = 0; kk < 4; ++kk) {
+                    bf16x8 av[MB];
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
-                        const f32x4 xs = *(const f32x4*)(smem + bufo + xs_lane + (gs * XSW + 16 * mb) * 4);
+                        const int off = aoff[mb] >= 0 ? bufo + aoff[mb] + kk * kKBlock * 2 : zero_lane;
+                        const u32x4 araw = *(const u32x4*)(smem + off);
+                        av[mb] = __builtin_bit_cast(bf16x8, araw);
+                    }
+                    const uint2 wv = rw[d][kk];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float cz = biased_zero(zw, j);
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const u32x4 braw = unpack_biased(jj == 0 ? wv.x : wv.y, mask, magic);
+                        const bf16x8 bv = __builtin_bit_cast(bf16x8, braw);
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                yv[mb][j][r] = fmaf(sj[j], fmaf(-cz, xs[r], acc[mb][j][r]), yv[mb][j][r]);
-                        }
+                        for (int mb = 0; mb < MB; ++mb)
+                            acc[mb][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                av[mb], bv, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][jj], 0, 0, 0);
                     }
                 }
-                ring_load(ring, d, ws, min(gl + R, ng - 1));
+                const uint32_t sv = rs[d], zw = rz[d];
+                const float sj[2] = {f16_bits_to_f32(sv & 0xFFFFu), f16_bits_to_f32(sv >> 16)};
+                const float cz[2] = {biased_zero(zw, 2 * h), biased_zero(zw, 2 * h + 1)};
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const f32x4 xs = *(const f32x4*)(smem + bufo + L.xs_off + (16 * mb + 4 * o) * 4);
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            yv[mb][jj][r] = fmaf(sj[jj], fmaf(-cz[jj], xs[r], acc[mb][jj][r]), yv[mb][jj][r]);
+                }
             }
-            if (st < nst) {
-                // every wave has finished stage st-1, whose buffer this is
-                if (st + 1 < nst)
-                    mfma_store_x<MB>(a, L, smem + ((st + 1) & 1) * L.buf, min(kStage, ng - (st + 1) * kStage), xr);
+            load(d, min(gl + R, ng - 1));
+            if (gl < ng) {
+                // every wave has finished group gl-1, whose buffer this is
+                if (gl + 1 < ng) wide_store_x<MB>(a, L, smem + ((gl + 1) & 1) * L.buf, xr);
                 lds_barrier();
             }
         }
     }
 
-    if (active) {
+    if (c < a.NC) {
         const size_t npad = (size_t)a.NC * kChunkN;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = c * kChunkN + 16 * j + t;
+            for (int jj = 0; jj < 2; ++jj) {
+                const int n = c * kChunkN + 16 * (2 * h + jj) + t;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = 16 * mb + 4 * o + r;
                     if (m < a.M && n < a.N) {
                         if (a.splits == 1)
-                            a.y[(size_t)m * a.N + n] = yv[mb][j][r];
+                            a.y[(size_t)m * a.N + n] = yv[mb][jj][r];
                         else
-                            store_partial(a.ws + ((size_t)split * a.M + m) * npad + n, yv[mb][j][r]);
+                            store_partial(a.ws + ((size_t)split * a.M + m) * npad + n, yv[mb][jj][r]);
                     }
                 }
             }
     }
-    if (a.splits > 1) splitk_fixup(a, tile);
+    if (a.splits > 1) splitk_fixup<kWideTileN>(a, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -809,9 +820,9 @@ int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Pl
     if (kernel == kGemv && M != 1) return -1;
     const int NC = ceil_div(N, kChunkN);
     const int G = K / kGroup;
-    const int ntiles = ceil_div(NC, kWaves);
     const int mb = ceil_div(M, 16);
-    const int variant = kernel == kGemv ? kVarGemv : (mb <= 2 ? kVarDirect : kVarLdsRing);
+    const int variant = kernel == kGemv ? kVarGemv : (mb <= 2 ? kVarDirect : kVarWide);
+    const int ntiles = ceil_div(NC, variant == kVarWide ? 2 : kWaves);
     int S;
     if (splits > 0) {
         S = splits;
@@ -848,8 +859,8 @@ int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Pl
     p->block = kThreads;
     p->lds = 0;
     p->row_stride = 0;
-    if (variant == kVarLdsRing) {
-        const MfmaLds L = mfma_lds(M, mb);
+    if (variant == kVarWide) {
+        const WideLds L = wide_lds(M, mb);
         p->lds = L.total;
         p->row_stride = L.row_stride;
     }
@@ -857,11 +868,8 @@ int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Pl
 }
 
 hipError_t set_kernel_attributes() {
-    hipError_t e = hipFuncSetAttribute((const void*)w4a16_mfma_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kLdsLimit);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void*)w4a16_mfma_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               kLdsLimit);
+    // the LDS ring of the wide kernel stays under 64 KB; nothing to raise
+    return hipSuccess;
 }
 
 static constexpr uint32_t kNibbleMask = 0x000F000Fu;
@@ -936,8 +944,8 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
             if (p.mb == 1) return launch(w4a16_mfma_direct_kernel<1, kRingDirect1>, grid, block, 0, stream, a);
             return launch(w4a16_mfma_direct_kernel<2, kRingDirect2>, grid, block, 0, stream, a);
         default:
-            if (p.mb == 3) return launch(w4a16_mfma_kernel<3>, grid, block, p.lds, stream, a);
-            return launch(w4a16_mfma_kernel<4>, grid, block, p.lds, stream, a);
+            if (p.mb == 3) return launch(w4a16_mfma_wide_kernel<3, kWideRing>, grid, block, p.lds, stream, a);
+            return launch(w4a16_mfma_wide_kernel<4, kWideRing>, grid, block, p.lds, stream, a);
     }
 }
 
