@@ -62,6 +62,16 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle on the host")
     p.add_argument("--no-parity", action="store_true", help="skip the oracle spot checks")
+    p.add_argument("--shapes", action="store_true",
+                   help="per-linear report instead of the sweep: each decoder shape and the lm_head at every M of "
+                        "--m, graph-replayed over rotating weight copies (>= --rotate-gib) so HBM, not the 256 MB "
+                        "MALL, serves them; one JSON line per (shape, M)")
+    p.add_argument("--m", default="1,2,4,5,8,16,32,48,64", help="M grid for --shapes")
+    p.add_argument("--names", default="q,k,v,o,gate,up,down,lm_head", help="linears for --shapes")
+    p.add_argument("--splits", type=int, default=0, help="force the K split count in --shapes (0 = planner)")
+    p.add_argument("--rotate-gib", type=float, default=2.0)
+    p.add_argument("--copy-calib", type=int, default=0,
+                   help="with --shapes: also run w4_bench_copy over this many MiB (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -286,12 +296,77 @@ def parity_checks(torch, w4, packed, host, xs, check_layers, n0):
 
 # ---------------------------------------------------------------------------
 
+def shapes_report(args):
+    """Per-linear microseconds and effective TB/s (the tiny, plain-decode,
+    sequence-draft and tree-draft configurations' shapes)."""
+    import torch
+
+    import speculative_decoding_verification_w4a16_amd as w4
+    import synth
+
+    dev = "cuda:0"
+    w4.w4_init()
+    table = {name: (N, K, 1000 + i) for i, (name, N, K) in enumerate(synth.LAYER_LINEARS)}
+    table["lm_head"] = (synth.LM_HEAD[1], synth.LM_HEAD[2], 20000)
+    Ms = [int(v) for v in args.m.split(",")]
+    if args.copy_calib:
+        nb = args.copy_calib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        src.fill_(3)
+        for _ in range(5):
+            w4.w4_bench_copy(dst, src, nb)
+        torch.cuda.synchronize()
+        del src, dst
+    for name in args.names.split(","):
+        N, K, seed = table[name]
+        lin = synth.gen_linear(seed, N, K)
+        base = w4.repack(torch.from_numpy(lin["qweight"]).to(dev), torch.from_numpy(lin["scales"].view(np.int16)).to(dev),
+                         torch.from_numpy(lin["zeros"]).to(dev), N, K)
+        R = max(2, int(args.rotate_gib * (1 << 30) // base.nbytes))
+        copies = [base] + [w4.PackedLinear(base.qweight_t.clone(), base.scales_t.clone(), base.zeros_t.clone(), N, K)
+                           for _ in range(R - 1)]
+        x = torch.from_numpy(synth.gen_x(max(Ms), K).view(np.int16)).to(dev)
+        y = torch.empty((max(Ms), N), dtype=torch.float32, device=dev)
+        for M in Ms:
+            plan = w4.w4a16_plan(M, N, K, splits=args.splits)
+            for pk in copies[:2]:
+                w4.linear(x[:M], pk, y=y[:M], splits=args.splits)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for pk in copies:
+                    w4.linear(x[:M], pk, y=y[:M], splits=args.splits)
+            g.replay()
+            torch.cuda.synchronize()
+            best = float("inf")
+            for _ in range(max(3, args.steps)):
+                s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s0.record()
+                g.replay()
+                s1.record()
+                s1.synchronize()
+                best = min(best, s0.elapsed_time(s1) * 1e3 / R)
+            B, F = alg_bytes(M, N, K), alg_flops(M, N, K)
+            t_roof = max(B / (HBM_PEAK_GBS * 1e9), F / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+            print(json.dumps({"linear": name, "N": N, "K": K, "M": M, "us": round(best, 3),
+                              "tbps": round(B / (best * 1e-6) / 1e12, 4), "roofline_frac": round(t_roof / best, 4),
+                              "mfma_util": round(F / (best * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+                              "plan": plan, "rotation_copies": R}), flush=True)
+            del g
+        del copies, base
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the verify linear is measured on one MI355X); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+    if args.shapes:
+        shapes_report(args)
+        return
     import torch
 
     import speculative_decoding_verification_w4a16_amd as w4
@@ -378,8 +453,8 @@ def main():
 
     # per-kernel roofline: every launch of a pass runs one kernel instantiation
     # (M=1 -> the GEMV, M=5 -> the direct MFMA kernel with one m-block,
-    # M=64 -> the two-waves-per-chunk MFMA kernel with four m-blocks)
-    kernel_of = {1: "w4a16_gemv_kernel<4>", 5: "w4a16_mfma_direct_kernel<1, 4>", 64: "w4a16_mfma_wide_kernel<4, 4>"}
+    # M=64 -> the LDS-ring MFMA kernel with four m-blocks)
+    kernel_of = {1: "w4a16_gemv_kernel<4>", 5: "w4a16_mfma_direct_kernel<1, 4>", 64: "w4a16_mfma_lds_kernel<4>"}
     # The graph of a pass holds nothing but that kernel's 561 launches (the
     # gaps between them measure ~0 in the kernel trace), so the pass time per
     # launch is the mean launch duration; events around single eager launches

@@ -16,9 +16,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are disabled for all device code (the compiler would
-# otherwise form v_pk_{add,mul,fma}_f32 from scalar float code).
+# otherwise form v_pk_{add,mul,fma}_f32 from scalar float code).  MFMA
+# accumulators are kept in architectural VGPRs: with a one-wave-per-SIMD
+# register budget the compiler otherwise places them in AGPRs, which costs a
+# v_accvgpr_read per epilogue operand and slows independent MFMA chains.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+          "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-unused-command-line-argument"]
 
 
 def build(verbose: bool = False) -> str:

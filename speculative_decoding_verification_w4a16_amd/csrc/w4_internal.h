@@ -18,10 +18,9 @@ constexpr int kTileN = kWaves * kChunkN;  // output columns per workgroup
 enum KernelId { kAuto = 0, kGemv = 1, kMfma = 2 };
 
 // Kernel variants behind the ids: the VALU GEMV (M = 1), the MFMA kernel
-// with A operands loaded straight from global memory (M <= 32), and the MFMA
-// kernel with two waves per chunk and activations staged through an LDS ring
-// (M = 33..64).
-enum Variant { kVarGemv = 0, kVarDirect = 1, kVarWide = 2 };
+// with A operands loaded straight from global memory (M <= 16), and the MFMA
+// kernel with activations copied into an LDS ring (M = 17..64).
+enum Variant { kVarGemv = 0, kVarDirect = 1, kVarLds = 2 };
 
 struct Plan {
     int kernel;   // kGemv or kMfma
@@ -29,11 +28,10 @@ struct Plan {
     int mb;       // m-blocks of 16 rows (MFMA)
     int splits;   // K splits (workgroups per column tile)
     int gps;      // groups per split
-    int ntiles;   // column tiles (kTileN columns, 128 for the wide variant)
+    int ntiles;   // column tiles of kTileN columns
     int grid;     // workgroups
     int block;    // threads per workgroup
     int lds;      // dynamic LDS bytes per workgroup
-    int row_stride;  // LDS bytes per staged x row
 };
 
 struct Workspace {

@@ -36,6 +36,16 @@ namespace w4 {
 // small device helpers
 // ---------------------------------------------------------------------------
 
+// A wave-uniform value copied into a VGPR (once, at kernel start).  With the
+// unpack mask in an SGPR and the magic value in a VGPR the compiler forms one
+// v_and_or_b32 per bf16 pair; with both in SGPRs it needs an AND and an OR
+// (a VALU op may read only one SGPR), and with literals it cannot fuse at all.
+__device__ __forceinline__ uint32_t to_vgpr(uint32_t s) {
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
+    return v;
+}
+
 // 8 packed codes -> 4 bf16 pairs (128 + q): dword d holds k offsets 2d, 2d+1.
 // `mask` (0x000F000F) and `magic` (0x43004300) arrive as kernel arguments so
 // that the compiler keeps them in registers and forms one v_and_or_b32 per
@@ -67,15 +77,6 @@ __device__ __forceinline__ float biased_zero(uint32_t zw, int j) {
 // elements are always copied into a scalar first.
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
-}
-
-// sum of the 8 bf16 values in a 16-byte vector, fp32, via dot2 with ones.
-__device__ __forceinline__ float sum8_bf16(u32x4 v, float acc) {
-    const uint32_t v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-    acc = dot2(v0, 0x3F803F80u, acc);
-    acc = dot2(v1, 0x3F803F80u, acc);
-    acc = dot2(v2, 0x3F803F80u, acc);
-    return dot2(v3, 0x3F803F80u, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -200,12 +201,11 @@ struct LinearArgs {
     const uint16_t* zt;
     float* y;
     float* ws;
+    size_t ws_bytes;  // split-K workspace size (< 2 GiB)
     int* counters;
     int M, N, K;
     int NC, KB, G;
     int gps, splits, ntiles;
-    int row_stride;  // LDS bytes per staged x row
-    int xs_off;      // LDS byte offset of the per-group x sums
     uint32_t mask;   // 0x000F000F (see unpack_biased)
     uint32_t magic;  // 0x43004300: bf16 128.0 in both halves
 };
@@ -228,8 +228,15 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float load_partial(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// 16 bytes of partials read at the device coherence point: a buffer load
+// with the sc1 cache policy, the vector form of the agent-scope loads above
+// (another XCD's L2 may hold stale lines of the workspace from an earlier
+// launch).  The buffer descriptor spans the workspace, so an offset past its
+// end reads zeros instead of faulting.
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data format
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ f32x4 load_partial4(__amdgpu_buffer_rsrc_t ws, size_t byte_offset) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, (int)byte_offset, 0, kCachePolicySc1));
 }
 
 // Split-K epilogue: once every wave's partial stores are acknowledged at
@@ -247,39 +254,46 @@ __device__ void splitk_fixup(const LinearArgs& a, int tile) {
     }
     __syncthreads();
     if (!last) return;
-    // Thread i owns column n0 + i % TW of the tile and every (kThreads/TW)-th
-    // row from i / TW.  Partials are fetched in batches of kFixRows rows x
-    // kFixSplits splits, all in flight together, and added in split order;
-    // indices past the end are clamped and their values replaced by zero, so
-    // the loads stay unconditional.
-    static_assert(kThreads % TW == 0, "tile width divides the workgroup");
-    constexpr int kRowStep = kThreads / TW;
+    // Thread i owns the four columns n0 + 4(i % (TW/4)) .. +3 of the tile and
+    // every (kThreads*4/TW)-th row from i / (TW/4).  Partials are fetched as
+    // 16-byte vectors in batches of kFixRows rows x kFixSplits splits, all in
+    // flight together, and added in split order; indices past the end are
+    // clamped and their values replaced by zero, so the loads stay
+    // unconditional.  N is a multiple of 8, so a column quad is either wholly
+    // inside y or wholly past its end.
+    static_assert(kThreads % (TW / 4) == 0, "tile width divides the workgroup");
+    constexpr int kQuads = TW / 4;
+    constexpr int kRowStep = kThreads / kQuads;
     constexpr int kFixRows = 4, kFixSplits = 8;
     const size_t npad = (size_t)a.NC * kChunkN;
     const size_t sstride = (size_t)a.M * npad;  // between splits
-    const int nt = tile * TW + (int)(threadIdx.x % TW);
-    const int n = min(nt, a.N - 1);
-    const int mfirst = threadIdx.x / TW;
+    const int nq = tile * TW + 4 * (int)(threadIdx.x % kQuads);
+    const int n = min(nq, a.N - 4);
+    const int mfirst = threadIdx.x / kQuads;
+    const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, (int)a.ws_bytes, kBufferWord3);
     for (int mb0 = 0; mb0 < a.M; mb0 += kFixRows * kRowStep) {
         const int m0 = mb0 + mfirst;  // rows m0, m0 + kRowStep, ...
-        float acc[kFixRows] = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 acc[kFixRows];
+#pragma unroll
+        for (int e = 0; e < kFixRows; ++e) acc[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         for (int s0 = 0; s0 < a.splits; s0 += kFixSplits) {
-            float v[kFixRows][kFixSplits];
+            f32x4 v[kFixRows][kFixSplits];
 #pragma unroll
             for (int e = 0; e < kFixRows; ++e)
 #pragma unroll
                 for (int i = 0; i < kFixSplits; ++i)
-                    v[e][i] = load_partial(a.ws + (size_t)min(s0 + i, a.splits - 1) * sstride +
-                                           (size_t)min(m0 + e * kRowStep, a.M - 1) * npad + n);
+                    v[e][i] = load_partial4(wsr, 4 * ((size_t)min(s0 + i, a.splits - 1) * sstride +
+                                                      (size_t)min(m0 + e * kRowStep, a.M - 1) * npad + n));
 #pragma unroll
             for (int e = 0; e < kFixRows; ++e)
 #pragma unroll
-                for (int i = 0; i < kFixSplits; ++i) acc[e] += (s0 + i < a.splits) ? v[e][i] : 0.0f;
+                for (int i = 0; i < kFixSplits; ++i)
+                    if (s0 + i < a.splits) acc[e] += v[e][i];
         }
 #pragma unroll
         for (int e = 0; e < kFixRows; ++e) {
             const int m = m0 + e * kRowStep;
-            if (m < a.M && nt < a.N) a.y[(size_t)m * a.N + n] = acc[e];
+            if (m < a.M && nq < a.N) *(f32x4*)(a.y + (size_t)m * a.N + n) = acc[e];
         }
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -349,7 +363,6 @@ constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 (1.0, 1.0)
 // stays under the 63 outstanding loads a wave can track).
 constexpr int kRingGemv = 4;
 constexpr int kRingDirect1 = 4;
-constexpr int kRingDirect2 = 3;
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
@@ -361,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
     const int ng = min(a.G, g0 + a.gps) - g0;
     const int c = tile * kWaves + wave;
     const int o = lane >> 4, t = lane & 15;
-    const uint32_t mask = a.mask, magic = a.magic;
+    const uint32_t mask = a.mask, magic = to_vgpr(a.magic);
     // waves past the last chunk stream the last chunk again (never stored):
     // branch-free loads keep the compiler's wait counts exact
     const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
@@ -440,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// M = 1..32: bf16 MFMA with activations loaded straight into A operands
+// M = 2..16: bf16 MFMA with activations loaded straight into A operands
 // ---------------------------------------------------------------------------
 //
 // For small M the activation rows are tiny and L1/L2-resident, so each lane
@@ -460,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_direct_kernel(LinearArgs 
     const int ng = min(a.G, g0 + a.gps) - g0;
     const int c = tile * kWaves + wave;
     const int o = lane >> 4, t = lane & 15;
-    const uint32_t mask = a.mask, magic = a.magic;
+    const uint32_t mask = a.mask, magic = to_vgpr(a.magic);
     const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
     const u32x4* xp[MB];
     bool xvalid[MB];
@@ -563,83 +576,77 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_direct_kernel(LinearArgs 
 }
 
 // ---------------------------------------------------------------------------
-// M = 33..64: bf16 MFMA, two waves per 64-column chunk, LDS-staged activations
+// M = 17..64: bf16 MFMA, one wave per 64-column chunk over all rows,
+// activations copied into a three-deep LDS ring by the LDS DMA path
 // ---------------------------------------------------------------------------
 //
-// A workgroup covers two chunks (128 columns); each wave owns two of a
-// chunk's four n-tiles and reads its 8-byte half of every lane's 16-byte tile
-// word (the two waves of a chunk share cache lines, so HBM sees each byte
-// once).  Splitting columns rather than rows halves the per-wave MFMA
-// accumulators, which keeps a wave under 256 registers: two waves per SIMD
-// then overlap one wave's MFMAs with the other's unpack and epilogue VALU.
-// The activation rows of the next group are loaded into registers while the
-// current one is computed, written to the other half of a double-buffered LDS
-// ring at the end of the group together with their per-(row, group) sums
-// (reduced over the 16 lanes of a row piece with DPP), and handed over with
-// an LDS-only barrier.
+// Each wave owns one chunk and every row block of 16, so each unpacked weight
+// feeds MB MFMAs and each A operand read from LDS feeds four: the LDS traffic
+// is four bytes of activations per byte of weights at M = 64.  Two waves per
+// SIMD (two workgroups per CU) overlap one wave's MFMAs with the other's
+// unpack and epilogue VALU work; a wave raises its priority while it issues
+// MFMAs, so the matrix pipe is fed first whenever both waves are ready.
+//
+// Activations never pass through VGPRs: global_load_lds_dwordx4 writes a
+// lane's 16 bytes straight to byte 16*lane of a 1 KB LDS line, and the
+// global address of each lane is free, so the line is filled in a
+// bank-swizzled order: row r of a group keeps k-octet q at 16-byte slot
+// q ^ (r & 15).  A wave's A-operand read (rows 16mb + l%16, octet 4kk + l/16)
+// then touches sixteen distinct 16-byte slots of a 256-byte bank window in
+// every sixteen lanes.
+//
+// The per-(row, group) activation sums of the zero-point term come from one
+// extra MFMA per k-block against an all-ones B operand: wave w computes them
+// for row block w one group ahead and publishes them through LDS.
+//
+// Pipeline per group g (one workgroup barrier):
+//   MFMAs of group g from buffer g%3 and weight ring slot g%3, the last
+//   k-block row block by row block;
+//   epilogue of each row block two row blocks after its last MFMA (an MFMA
+//   result takes far longer to become readable by the VALU than by a
+//   dependent MFMA), the sums of group g+1 in between;
+//   wait for this wave's DMA of group g+2, then barrier;
+//   DMA of group g+3 into buffer g%3, then the weight loads of group g+3
+//   into ring slot g%3.
+// Every buffer is rewritten only after the barrier that follows its last
+// read.  The DMA is issued from inline asm: the compiler's wait-count pass
+// treats LDS DMA and register loads in flight together as possibly out of
+// order and would wait for every load (vmcnt(0)) before each use of the
+// weight ring.  Loads retire in issue order, so the explicit wait for the
+// DMA of group g+2 needs only the ring loads issued after it to stay in
+// flight, and the compiler's own waits for ring data (which do not count the
+// hidden DMA) can only wait longer than needed, never too little.
 
-constexpr int kWideRing = 4;
-constexpr int kWideTileN = 2 * kChunkN;
+constexpr int kLdsRing = 3;  // activation buffers, sum slots and weight ring depth
 
-struct WideLds {
-    int row_stride;  // one group of a row (256 bytes) plus 16 bytes of skew
-    int xs_off;      // per-row group sums inside a buffer
-    int buf;         // bytes per buffer
-    int zero_off;    // 64-byte zero line for padded A rows
-    int total;
-};
+__host__ __device__ constexpr int lds_ring_xbuf(int mb) { return 16 * mb * kGroup * 2; }
+__host__ __device__ constexpr int lds_ring_bytes(int mb) { return kLdsRing * (lds_ring_xbuf(mb) + 16 * mb * 4); }
 
-__host__ __device__ inline WideLds wide_lds(int M, int mb) {
-    WideLds l;
-    l.row_stride = kGroup * 2 + 16;
-    l.xs_off = M * l.row_stride;
-    l.buf = (l.xs_off + 16 * mb * 4 + 15) & ~15;
-    l.zero_off = 2 * l.buf;
-    l.total = l.zero_off + 64;
-    return l;
+// Wait until at most N vector memory loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Sum over the 16 lanes of a DPP row (every lane gets the total; the add
-// tree is the same in every lane, so the result is identical across lanes).
-__device__ __forceinline__ float row16_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
-    return v;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 l (the LDS line address travels in M0, wave-uniform).  Issued
+// from inline asm so the compiler's wait-count pass does not see it; callers
+// wait for it with wait_vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory", "m0");
 }
 
-// Activation pieces of group `gl` (16 bytes of one row each; thread p takes
-// row p/16, piece p%16).  Rows past M and groups past the split load an
-// in-range piece that wide_store_x drops.
 template <int MB>
-__device__ __forceinline__ void wide_load_x(const LinearArgs& a, int g0, int ng, int gl, u32x4 (&xr)[MB]) {
-    const int gg = min(gl, ng - 1);
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        const int p = threadIdx.x + kThreads * i;
-        const int m = p >> 4, q = p & 15;
-        const int mm = m < a.M ? m : 0;
-        xr[i] = *(const u32x4*)(a.x + (size_t)mm * a.K + (size_t)(g0 + gg) * kGroup + 8 * q);
-    }
-}
-
-template <int MB>
-__device__ __forceinline__ void wide_store_x(const LinearArgs& a, const WideLds& L, char* buf,
-                                             const u32x4 (&xr)[MB]) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        const int p = threadIdx.x + kThreads * i;
-        const int m = p >> 4, q = p & 15;
-        const bool valid = m < a.M;
-        if (valid) *(u32x4*)(buf + m * L.row_stride + 16 * q) = xr[i];
-        const float s = row16_sum(valid ? sum8_bf16(xr[i], 0.0f) : 0.0f);
-        if (valid && q == 0) *(float*)(buf + L.xs_off + m * 4) = s;
-    }
-}
-
-template <int MB, int R>
-__global__ __launch_bounds__(kThreads) void w4a16_mfma_wide_kernel(LinearArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void w4a16_mfma_lds_kernel(LinearArgs a) {
+    constexpr int R = kLdsRing;
+    constexpr int XB = lds_ring_xbuf(MB);  // bytes per activation buffer
+    constexpr int XS = R * XB;             // first sum slot
+    constexpr int XSS = 16 * MB * 4;       // bytes per sum slot
+    constexpr int kRingOps = 6;            // loads per weight ring slot: 4 weight words, scales, zeros
     extern __shared__ __align__(16) char smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -647,127 +654,152 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_wide_kernel(LinearArgs a)
     const int tile = blockIdx.x - split * a.ntiles;
     const int g0 = split * a.gps;
     const int ng = min(a.G, g0 + a.gps) - g0;
-    const int c = tile * 2 + (wave >> 1);
-    const int h = wave & 1;  // n-tiles 2h, 2h+1 of the chunk
+    const int c = tile * kWaves + wave;
     const int o = lane >> 4, t = lane & 15;
-    const uint32_t mask = a.mask, magic = a.magic;
-    const WideLds L = wide_lds(a.M, MB);
+    const uint32_t mask = a.mask, magic = to_vgpr(a.magic);
+    const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2});
 
-    // sums of padded rows stay zero; the zero line feeds padded A rows
-    for (int p = threadIdx.x; p < 2 * 16 * MB; p += kThreads) {
-        const int b = p / (16 * MB), r = p - b * (16 * MB);
-        if (r >= a.M) *(float*)(smem + b * L.buf + L.xs_off + r * 4) = 0.0f;
-    }
-    if (threadIdx.x < 4) *(u32x4*)(smem + L.zero_off + 16 * threadIdx.x) = u32x4{0, 0, 0, 0};
-
-    // weights: this wave's 8-byte half of each lane word; waves past the last
-    // chunk stream the last chunk again (never stored)
-    const int cc = min(c, a.NC - 1);
-    const uint2* wp = (const uint2*)a.qt + (((size_t)cc * a.KB + (size_t)g0 * 4) * 64 + lane) * 2 + h;
-    const uint32_t* sp = (const uint32_t*)a.st + ((size_t)cc * a.G + g0) * 32 + t * 2 + h;
-    const uint16_t* zp = a.zt + ((size_t)cc * a.G + g0) * 16 + t;
-    uint2 rw[R][4];
-    uint32_t rs[R], rz[R];
-    auto load = [&](int d, int gl) {
-        __builtin_amdgcn_sched_barrier(0);  // keep the reload after the slot's last use
+    // DMA sources.  Wave w fills lines w + 4ii (ii < MB) of a buffer; line i
+    // holds rows 4i..4i+3 and lane l lands in row 4i + l/16, slot l%16, which
+    // holds k-octet (l%16) ^ (row & 15).  Rows past M repeat row M-1 (their
+    // results are never stored), groups past the split repeat its last group.
+    int xoff[MB];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) rw[d][kk] = wp[(gl * 4 + kk) * 128];
-        rs[d] = sp[gl * 32];
-        rz[d] = zp[gl * 16];
+    for (int ii = 0; ii < MB; ++ii) {
+        const int r = 4 * (wave + 4 * ii) + o;
+        xoff[ii] = min(r, a.M - 1) * a.K + 8 * (t ^ (r & 15));
+    }
+    const uint16_t* xg = a.x + (size_t)g0 * kGroup;
+    auto issue_x = [&](int buf, int gl) {
+        const uint16_t* src = xg + (size_t)min(gl, ng - 1) * kGroup;
+#pragma unroll
+        for (int ii = 0; ii < MB; ++ii) lds_dma16(src + xoff[ii], smem + buf * XB + 1024 * (wave + 4 * ii));
     };
-    {
-        u32x4 xr[MB];
-        wide_load_x<MB>(a, g0, ng, 0, xr);
-#pragma unroll
-        for (int d = 0; d < R; ++d) load(d, min(d, ng - 1));
-        wide_store_x<MB>(a, L, smem, xr);
-        lds_barrier();  // group 0's rows, sums, the zeroed sums and the zero line
-    }
 
-    int aoff[MB];
+    // A operand of (row block mb, k-block kk) in buffer b: row 16mb + t, octet
+    // 4kk + o, at slot (4kk + o) ^ t.  One base per kk; the buffer and the
+    // row block are immediate offsets.
+    int ab[4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int row = 16 * mb + t;
-        aoff[mb] = row < a.M ? row * L.row_stride + 16 * o : -1;
-    }
-    const int zero_lane = L.zero_off + 16 * o;
+    for (int kk = 0; kk < 4; ++kk) ab[kk] = (16 * t + ((4 * kk + o) ^ t)) * 16;
+    auto a_frag = [&](int b, int mb, int kk) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + ab[kk] + b * XB + mb * 4096));
+    };
+    // zero-point sums of row block `wave` of the group in buffer b, into sum slot b
+    auto compute_xs = [&](int b) {
+        if (wave < MB) {
+            f32x4 accx = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 av =
+                    __builtin_bit_cast(bf16x8, *(const u32x4*)(smem + ab[kk] + wave * 4096 + b * XB));
+                accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, ones, accx, 0, 0, 0);
+            }
+            // D rows 4o + r of the block; every column holds the same sums
+            if (t == 0) *(f32x4*)(smem + XS + b * XSS + (16 * wave + 4 * o) * 4) = accx;
+        }
+    };
 
-    f32x4 yv[MB][2];
+    WeightRing<R> ring;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) yv[mb][0] = yv[mb][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int d = 0; d < R; ++d) {
+        issue_x(d, d);
+        ring_load(ring, d, ws, min(d, ng - 1));
+    }
+    // groups 0 and 1 landed: after them only the ring slot of group 1, then
+    // the DMA and ring slot of group 2 may still be in flight
+    wait_vmcnt<2 * kRingOps + MB>();
+    lds_barrier();
+    compute_xs(0);
+    lds_barrier();
+
+    f32x4 yv[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yv[mb][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (int gb = 0; gb < ng; gb += R) {
 #pragma unroll
         for (int d = 0; d < R; ++d) {
-            const int gl = gb + d;
-            u32x4 xr[MB];  // the next group's activations
-            wide_load_x<MB>(a, g0, ng, gl + 1, xr);
-            asm volatile("" ::: "memory");  // keep those loads here, ahead of the compute
-            const int bufo = (gl & 1) * L.buf;
+            const int gl = gb + d;  // buffer, sum slot and ring slot are all d = gl % 3
             if (gl < ng) {
-                f32x4 acc[MB][2];
+                __builtin_amdgcn_s_setprio(1);
+                f32x4 acc[MB][4];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
+                for (int kk = 0; kk < 3; ++kk) {
                     bf16x8 av[MB];
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        const int off = aoff[mb] >= 0 ? bufo + aoff[mb] + kk * kKBlock * 2 : zero_lane;
-                        const u32x4 araw = *(const u32x4*)(smem + off);
-                        av[mb] = __builtin_bit_cast(bf16x8, araw);
-                    }
-                    const uint2 wv = rw[d][kk];
+                    for (int mb = 0; mb < MB; ++mb) av[mb] = a_frag(d, mb, kk);
 #pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        const u32x4 braw = unpack_biased(jj == 0 ? wv.x : wv.y, mask, magic);
+                    for (int j = 0; j < 4; ++j) {
+                        const u32x4 braw = unpack_biased(ring.w[d][kk][j], mask, magic);
                         const bf16x8 bv = __builtin_bit_cast(bf16x8, braw);
 #pragma unroll
                         for (int mb = 0; mb < MB; ++mb)
-                            acc[mb][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                av[mb], bv, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][jj], 0, 0, 0);
+                            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                av[mb], bv, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][j], 0, 0, 0);
                     }
                 }
-                const uint32_t sv = rs[d], zw = rz[d];
-                const float sj[2] = {f16_bits_to_f32(sv & 0xFFFFu), f16_bits_to_f32(sv >> 16)};
-                const float cz[2] = {biased_zero(zw, 2 * h), biased_zero(zw, 2 * h + 1)};
+                __builtin_amdgcn_s_setprio(0);
+                float sj[4], cz[4];
+                decode_scales(ring.s[d], sj);
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const f32x4 xs = *(const f32x4*)(smem + bufo + L.xs_off + (16 * mb + 4 * o) * 4);
+                for (int j = 0; j < 4; ++j) cz[j] = biased_zero(ring.z[d], j);
+                // last k-block row block by row block, so the epilogue of one
+                // row block can issue while the MFMAs of the next one run
+                bf16x8 bv3[4];
 #pragma unroll
-                    for (int jj = 0; jj < 2; ++jj)
+                for (int j = 0; j < 4; ++j) bv3[j] = __builtin_bit_cast(bf16x8, unpack_biased(ring.w[d][3][j], mask, magic));
+                auto epi = [&](int mb) {
+                    const f32x4 xs = *(const f32x4*)(smem + XS + d * XSS + (16 * mb + 4 * o) * 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            yv[mb][jj][r] = fmaf(sj[jj], fmaf(-cz[jj], xs[r], acc[mb][jj][r]), yv[mb][jj][r]);
+                            yv[mb][j][r] = fmaf(sj[j], fmaf(-cz[j], xs[r], acc[mb][j][r]), yv[mb][j][r]);
+                };
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const bf16x8 av = a_frag(d, mb, 3);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv3[j], acc[mb][j], 0, 0, 0);
+                    if (mb >= 2) epi(mb - 2);
                 }
-            }
-            load(d, min(gl + R, ng - 1));
-            if (gl < ng) {
-                // every wave has finished group gl-1, whose buffer this is
-                if (gl + 1 < ng) wide_store_x<MB>(a, L, smem + ((gl + 1) & 1) * L.buf, xr);
+                if (gl + 1 < ng) compute_xs((d + 1) % R);
+#pragma unroll
+                for (int mb = MB - 2; mb < MB; ++mb) epi(mb);
+                wait_vmcnt<kRingOps>();  // this wave's DMA of group gl+2 (its ring slot may still fly)
                 lds_barrier();
+                issue_x(d, gl + R);
             }
+            ring_load(ring, d, ws, min(gl + R, ng - 1));
         }
     }
+    wait_vmcnt<0>();  // no DMA into LDS outlives the loop
 
     if (c < a.NC) {
         const size_t npad = (size_t)a.NC * kChunkN;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int n = c * kChunkN + 16 * (2 * h + jj) + t;
+            for (int j = 0; j < 4; ++j) {
+                const int n = c * kChunkN + 16 * j + t;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = 16 * mb + 4 * o + r;
                     if (m < a.M && n < a.N) {
                         if (a.splits == 1)
-                            a.y[(size_t)m * a.N + n] = yv[mb][jj][r];
+                            a.y[(size_t)m * a.N + n] = yv[mb][j][r];
                         else
-                            store_partial(a.ws + ((size_t)split * a.M + m) * npad + n, yv[mb][jj][r]);
+                            store_partial(a.ws + ((size_t)split * a.M + m) * npad + n, yv[mb][j][r]);
                     }
                 }
             }
     }
-    if (a.splits > 1) splitk_fixup<kWideTileN>(a, tile);
+    if (a.splits > 1) splitk_fixup<kTileN>(a, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -821,24 +853,37 @@ int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Pl
     const int NC = ceil_div(N, kChunkN);
     const int G = K / kGroup;
     const int mb = ceil_div(M, 16);
-    const int variant = kernel == kGemv ? kVarGemv : (mb <= 2 ? kVarDirect : kVarWide);
-    const int ntiles = ceil_div(NC, variant == kVarWide ? 2 : kWaves);
+    const int variant = kernel == kGemv ? kVarGemv : (mb == 1 ? kVarDirect : kVarLds);
+    const int ntiles = ceil_div(NC, kWaves);
     int S;
     if (splits > 0) {
         S = splits;
     } else {
-        // Measured on MI355X: about one workgroup per CU (256) streams best;
-        // more workgroups add per-workgroup start-up and split-K fix-up cost
-        // without adding bandwidth.  Keep >= 4 groups per wave so a wave's
-        // load ring is full, and the split-K partial traffic under half the
-        // weight bytes.
-        const int target_wgs = 256;
-        S = ceil_div(target_wgs, ntiles);
-        S = std::min(S, std::max(1, G / 4));
+        // Measured on MI355X: a launch streams best with about one
+        // workgroup per CU; a partly filled last round leaves CUs idle, and
+        // every workgroup pays a start-up and split-K fix-up cost worth about
+        // four groups of work.  So pick the split count S minimising
+        //     rounds(S) * (groups per workgroup + 4),   rounds = ceil(wgs / 256),
+        // the smallest such S, with >= 4 groups per workgroup and the split-K
+        // partial traffic capped.
+        const int slots = 256;
         const long weight_bytes = (long)NC * kChunkN * K / 2;
         const long partial_per_split = (long)M * NC * kChunkN * 4 * 2;  // written + read
-        const int s_traffic = (int)std::max<long>(1, weight_bytes / (2 * partial_per_split));
-        S = std::min(S, s_traffic);
+        // partials stay under half the weight bytes, or under all of them for
+        // the M > 32 kernel, which is bound by its MFMA and VALU work per CU
+        // rather than by HBM
+        const int s_traffic =
+            (int)std::max<long>(1, weight_bytes / ((variant == kVarLds ? 1 : 2) * partial_per_split));
+        const int smax = std::max(1, std::min(G / 4, s_traffic));
+        S = 1;
+        double best = 1e30;
+        for (int s = 1; s <= smax; ++s) {
+            const double cost = (double)ceil_div((long)ntiles * s, slots) * ((double)G / s + 4.0);
+            if (cost < best - 1e-9) {
+                best = cost;
+                S = s;
+            }
+        }
     }
     S = std::max(1, std::min(S, G));
     int gps = ceil_div(G, S);
@@ -858,11 +903,8 @@ int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Pl
     p->grid = ntiles * S;
     p->block = kThreads;
     p->lds = 0;
-    p->row_stride = 0;
-    if (variant == kVarWide) {
-        const WideLds L = wide_lds(M, mb);
-        p->lds = L.total;
-        p->row_stride = L.row_stride;
+    if (variant == kVarLds) {
+        p->lds = lds_ring_bytes(mb);
     }
     return 0;
 }
@@ -923,6 +965,7 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
     a.zt = zeros_t;
     a.y = y;
     a.ws = ws.partial;
+    a.ws_bytes = ws.partial_bytes;
     a.counters = ws.counters;
     a.M = M;
     a.N = N;
@@ -933,19 +976,17 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
     a.gps = p.gps;
     a.splits = p.splits;
     a.ntiles = p.ntiles;
-    a.row_stride = p.row_stride;
-    a.xs_off = 0;
     a.mask = kNibbleMask;
     a.magic = kBiasMagic;
     const dim3 grid(p.grid), block(p.block);
     switch (p.variant) {
         case kVarGemv: return launch(w4a16_gemv_kernel<kRingGemv>, grid, block, 0, stream, a);
         case kVarDirect:
-            if (p.mb == 1) return launch(w4a16_mfma_direct_kernel<1, kRingDirect1>, grid, block, 0, stream, a);
-            return launch(w4a16_mfma_direct_kernel<2, kRingDirect2>, grid, block, 0, stream, a);
+            return launch(w4a16_mfma_direct_kernel<1, kRingDirect1>, grid, block, 0, stream, a);
         default:
-            if (p.mb == 3) return launch(w4a16_mfma_wide_kernel<3, kWideRing>, grid, block, p.lds, stream, a);
-            return launch(w4a16_mfma_wide_kernel<4, kWideRing>, grid, block, p.lds, stream, a);
+            if (p.mb == 2) return launch(w4a16_mfma_lds_kernel<2>, grid, block, p.lds, stream, a);
+            if (p.mb == 3) return launch(w4a16_mfma_lds_kernel<3>, grid, block, p.lds, stream, a);
+            return launch(w4a16_mfma_lds_kernel<4>, grid, block, p.lds, stream, a);
     }
 }
 
