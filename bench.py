@@ -451,14 +451,16 @@ def main():
         torch.cuda.synchronize()
         us_eager[M] = s.elapsed_time(e) * 1e3
 
-    # per-kernel roofline: every launch of a pass runs one kernel instantiation
+    # per-kernel roofline: every linear of a pass runs one kernel instantiation
     # (M=1 -> the GEMV, M=5 -> the direct MFMA kernel with one m-block,
-    # M=64 -> the LDS-ring MFMA kernel with four m-blocks)
+    # M=64 -> the LDS-ring MFMA kernel with four m-blocks), followed, when its
+    # K is split, by splitk_reduce_kernel; the unit of the figures below is
+    # the linear, i.e. that kernel plus its reduction.
     kernel_of = {1: "w4a16_gemv_kernel<4>", 5: "w4a16_mfma_direct_kernel<1, 4>", 64: "w4a16_mfma_lds_kernel<4>"}
-    # The graph of a pass holds nothing but that kernel's 561 launches (the
-    # gaps between them measure ~0 in the kernel trace), so the pass time per
-    # launch is the mean launch duration; events around single eager launches
-    # are reported beside it (they add a few microseconds each).
+    # The graph of a pass holds nothing but those launches (the gaps between
+    # them measure ~0 in the kernel trace), so the pass time per linear is the
+    # mean duration of a linear; events around single eager linears are
+    # reported beside it (they add a few microseconds each).
     kernels = {}
     for M in PASS_M:
         dur_ms = per_launch_durations(torch, w4, descs[M], M)
@@ -479,7 +481,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": dk["achieved_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dk["achieved_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
                 "per_launch": "alg_bytes_per_launch = 0.51953125 N K + 2 M K + 4 M N averaged over the 561 "
-                              "linears of the pass; achieved = that / (graph pass time / 561)"}
+                              "linears of the pass; achieved = that / (graph pass time / 561); a linear is the "
+                              "kernel plus splitk_reduce_kernel when its K is split"}
 
     ceiling = hbm_read_ceiling(torch, w4)
     parity = None

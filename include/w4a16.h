@@ -26,10 +26,12 @@
  *    stream has drained.
  *  - Arguments are validated before any HIP call; a failed check returns a
  *    status and launches nothing.  The library never prints or aborts.
- *  - Hidden state: one split-K workspace and counter array per device,
- *    allocated on the first call that needs it (or by w4_init) and kept
- *    until the process ends.  Calls that overlap in time on one device
- *    (different streams) share it and must not run concurrently.
+ *  - Hidden state: one 64 MiB split-K workspace per device, allocated on
+ *    the first call that needs it (or by w4_init) and kept until the
+ *    process ends.  A linear with a K split runs as two launches on the
+ *    caller's stream (the streaming kernel, then the reduction of its
+ *    partials).  Calls that overlap in time on one device (different
+ *    streams) share the workspace and must not run concurrently.
  */
 #ifndef W4A16_H
 #define W4A16_H

@@ -35,18 +35,15 @@ struct Plan {
 };
 
 struct Workspace {
-    float* partial;      // split-K partial sums
+    float* partial;  // split-K partial sums, [S][M][NC*64] fp32
     size_t partial_bytes;
-    int* counters;       // per column tile, self-resetting
-    int n_counters;
 };
 
 // LDS budget per workgroup for the staged activation tile.
 constexpr int kLdsLimit = 160 * 1024 - 256;  // room for the small static LDS
 
-// Workspace sizes (per device).
+// Split-K workspace size (per device).
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;
-constexpr int kCounters = 1 << 16;
 
 int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Plan* p);
 

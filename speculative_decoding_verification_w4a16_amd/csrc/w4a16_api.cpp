@@ -48,26 +48,10 @@ int device_state(w4::Workspace* out) {
         e = w4::set_kernel_attributes();
         if (e != hipSuccess) return hip_fail("hipFuncSetAttribute", e);
         void* p = nullptr;
-        void* c = nullptr;
         e = hipMalloc(&p, w4::kWorkspaceBytes);
         if (e != hipSuccess) return hip_fail("hipMalloc(workspace)", e);
-        e = hipMalloc(&c, sizeof(int) * w4::kCounters);
-        if (e != hipSuccess) {
-            (void)hipFree(p);
-            return hip_fail("hipMalloc(counters)", e);
-        }
-        // counters start at zero; kernels re-arm them after every use
-        e = hipMemset(c, 0, sizeof(int) * w4::kCounters);
-        if (e == hipSuccess) e = hipDeviceSynchronize();
-        if (e != hipSuccess) {
-            (void)hipFree(p);
-            (void)hipFree(c);
-            return hip_fail("hipMemset(counters)", e);
-        }
         st.ws.partial = (float*)p;
         st.ws.partial_bytes = w4::kWorkspaceBytes;
-        st.ws.counters = (int*)c;
-        st.ws.n_counters = w4::kCounters;
         st.ready = true;
     }
     if (out) *out = st.ws;
