@@ -66,10 +66,16 @@ def parse():
                    help="per-linear report instead of the sweep: each decoder shape and the lm_head at every M of "
                         "--m, graph-replayed over rotating weight copies (>= --rotate-gib) so HBM, not the 256 MB "
                         "MALL, serves them; one JSON line per (shape, M)")
+    p.add_argument("--floor", action="store_true",
+                   help="instead of the sweep: plain streaming reads of each linear's packed bytes (one launch "
+                        "each), an empty launch, and their sum over a pass")
     p.add_argument("--m", default="1,2,4,5,8,16,32,48,64", help="M grid for --shapes")
     p.add_argument("--names", default="q,k,v,o,gate,up,down,lm_head", help="linears for --shapes")
     p.add_argument("--splits", type=int, default=0, help="force the K split count in --shapes (0 = planner)")
     p.add_argument("--rotate-gib", type=float, default=2.0)
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="instead of running: turn two rocprofv3 --pmc runs of the sweep (FETCH_SIZE, WRITE_SIZE; "
+                        "taken with --copy-calib) into profiles/traffic.json")
     p.add_argument("--copy-calib", type=int, default=0,
                    help="with --shapes: also run w4_bench_copy over this many MiB (HBM counter calibration)")
     return p.parse_args()
@@ -213,9 +219,9 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_name: str):
-    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they
-    were taken on the current kernel sources; else None."""
+def traffic_from_profiles(M: int):
+    """HBM bytes per linear of the pass at M from the committed PMC summary,
+    if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -226,13 +232,15 @@ def traffic_from_profiles(kernel_name: str):
         return None
     if data.get("source_digest") != source_digest():
         return None
-    ent = data.get("kernels", {}).get(kernel_name)
-    return None if ent is None else ent.get("hbm_bytes_per_launch")
+    ent = data.get("passes", {}).get(str(M))
+    return None if ent is None else ent.get("hbm_bytes_per_linear")
 
 
-def cpu_baseline(host, budget_s=25.0):
-    """The oracle, as it stands, on a bounded sample of the workload: layer 0's
-    q, k, v and o linears at M = 5, one linear at a time until the budget."""
+def cpu_baseline(host, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the workload: the
+    sweep's linears held in host memory (layer 0, then the parity layers), each
+    at the pass M = 1, 5 and 64, one (layer, M, linear) unit at a time until
+    about budget_s seconds of CPU work."""
     import synth
     from oracle import linear64
 
@@ -240,22 +248,26 @@ def cpu_baseline(host, budget_s=25.0):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         cores = os.cpu_count() or 1
-    done, secs, nbytes = [], 0.0, 0
-    for name, N, K in synth.LAYER_LINEARS:
-        key = (0, name)
-        if key not in host or secs > budget_s * 0.5:
-            continue
-        lin = host[key]
-        x = synth.gen_x(5, K)
-        t = time.perf_counter()
-        linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
-        secs += time.perf_counter() - t
-        nbytes += alg_bytes(5, N, K)
-        done.append(name)
-        if secs > budget_s:
-            break
+    units, secs, nbytes = 0, 0.0, 0
+    layers = sorted({L for (L, _) in host if L is not None})
+    xs = {}
+    for L in layers:
+        for M in PASS_M:
+            for name, N, K in synth.LAYER_LINEARS:
+                key = (L, name)
+                if key not in host or secs > budget_s:
+                    continue
+                lin = host[key]
+                if K not in xs:
+                    xs[K] = synth.gen_x(64, K)
+                t = time.perf_counter()
+                linear64(xs[K][:M], lin["qweight"], lin["scales"], lin["zeros"])
+                secs += time.perf_counter() - t
+                nbytes += alg_bytes(M, N, K)
+                units += 1
     return {"value": round(nbytes / secs / 1e12, 6), "unit": "TB/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 oracle (numpy, BLAS threads={cores}) on layer 0 linears {done} at M=5: "
+            "sample": f"float64 oracle (numpy, BLAS threads={cores}) on {units} (layer, M, linear) units of the "
+                      f"sweep (layers {layers}, M in {list(PASS_M)}, in that order until ~{budget_s:.0f} s): "
                       f"{nbytes / 1e9:.3f} GB of algorithmic traffic in {secs:.2f} s"}
 
 
@@ -296,6 +308,70 @@ def parity_checks(torch, w4, packed, host, xs, check_layers, n0):
 
 # ---------------------------------------------------------------------------
 
+def copy_calibration(torch, w4, mib):
+    """A plain copy of known size (mib MiB read and written, five times): what
+    the HBM byte counters read for it scales their readings of the kernels."""
+    nb = mib << 20
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    src.fill_(3)
+    for _ in range(5):
+        w4.w4_bench_copy(dst, src, nb)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def traffic_from_pmc(fetch_dir, write_dir, copy_mib, out_path):
+    """HBM bytes per linear of each sweep pass from two rocprofv3 --pmc runs of
+    the sweep (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
+    what the counter reads for w4_bench_copy of copy_mib MiB.  A linear is its
+    streaming kernel plus the split-K reductions dispatched right after it;
+    the streaming kernel names the pass (GEMV: M=1, direct MFMA: M=5, LDS
+    MFMA: M=64).  Writes profiles/traffic.json (tagged with the kernel-source
+    digest) and returns it."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        vals, names = {}, {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                i = int(r["Dispatch_Id"])
+                vals[i] = vals.get(i, 0.0) + float(r["Counter_Value"])
+                names[i] = r["Kernel_Name"]
+        return vals, names
+
+    out = {"source_digest": source_digest(), "copy_calibration_mib": copy_mib, "passes": {}}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals, names = per_dispatch(d, counter)
+        copies = [vals[i] for i in vals if "bench_copy" in names[i]]
+        factor = (copy_mib * 1024.0) / (sum(copies) / len(copies))  # true KiB per counted KiB
+        out[counter + "_factor"] = round(factor, 4)
+        pass_of = {"gemv": "1", "direct": "5", "lds": "64"}
+        sums, counts, cur = {}, {}, None
+        for i in sorted(vals):
+            n = names[i]
+            if "splitk_reduce" in n:
+                if cur is not None:
+                    sums[cur] += vals[i] * factor * 1024
+                continue
+            cur = next((m for k, m in pass_of.items() if f"w4a16_{'mfma_' if k != 'gemv' else ''}{k}" in n), None)
+            if cur is not None:
+                sums[cur] = sums.get(cur, 0.0) + vals[i] * factor * 1024
+                counts[cur] = counts.get(cur, 0) + 1
+        for m in sums:
+            ent = out["passes"].setdefault(m, {"linears_counted": counts[m]})
+            ent[counter.lower() + "_bytes_per_linear"] = int(sums[m] / counts[m])
+    for m, ent in out["passes"].items():
+        ent["hbm_bytes_per_linear"] = ent.get("fetch_size_bytes_per_linear", 0) + \
+            ent.get("write_size_bytes_per_linear", 0)
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def shapes_report(args):
     """Per-linear microseconds and effective TB/s (the tiny, plain-decode,
     sequence-draft and tree-draft configurations' shapes)."""
@@ -310,14 +386,7 @@ def shapes_report(args):
     table["lm_head"] = (synth.LM_HEAD[1], synth.LM_HEAD[2], 20000)
     Ms = [int(v) for v in args.m.split(",")]
     if args.copy_calib:
-        nb = args.copy_calib << 20
-        src = torch.empty(nb, dtype=torch.uint8, device=dev)
-        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
-        src.fill_(3)
-        for _ in range(5):
-            w4.w4_bench_copy(dst, src, nb)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch, w4, args.copy_calib)
     for name in args.names.split(","):
         N, K, seed = table[name]
         lin = synth.gen_linear(seed, N, K)
@@ -358,6 +427,68 @@ def shapes_report(args):
         torch.cuda.empty_cache()
 
 
+def floor_report(args):
+    """Separate-launch floor: a plain 128-bit streaming read (w4_bench_read,
+    graph-replayed over rotating buffers past the MALL) of each linear's packed
+    bytes, an empty launch, and the sum of those reads over the 561 linears of
+    a pass -- the least time any design that keeps one launch per linear can
+    take, against the 8 TB/s roofline of the same bytes."""
+    import torch
+
+    import speculative_decoding_verification_w4a16_amd as w4
+    import synth
+
+    dev = "cuda:0"
+    sink = torch.empty(w4.w4_bench_read_blocks(), dtype=torch.int32, device=dev)
+
+    def timed(nbytes, copies):
+        for b in copies[:2]:
+            w4.w4_bench_read(b, nbytes, sink)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for b in copies:
+                w4.w4_bench_read(b, nbytes, sink)
+        g.replay()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(max(3, args.steps)):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            g.replay()
+            s1.record()
+            s1.synchronize()
+            best = min(best, s0.elapsed_time(s1) * 1e3 / len(copies))
+        del g
+        return best
+
+    tiny = [torch.zeros(16, dtype=torch.uint8, device=dev) for _ in range(200)]
+    us_empty = timed(16, tiny)
+    del tiny
+    print(json.dumps({"launch": "w4_bench_read of 16 bytes", "us": round(us_empty, 3)}), flush=True)
+    shapes = list(synth.LAYER_LINEARS) + [synth.LM_HEAD]
+    floors = {}
+    for name, N, K in shapes:
+        nbytes = (int(N * K * 0.51953125) + 15) // 16 * 16
+        R = max(2, int(args.rotate_gib * (1 << 30) // nbytes))
+        copies = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(R)]
+        for b in copies:
+            b.fill_(1)
+        us = timed(nbytes, copies)
+        floors[name] = us
+        print(json.dumps({"linear": name, "N": N, "K": K, "bytes": nbytes, "us": round(us, 3),
+                          "tbps": round(nbytes / (us * 1e-6) / 1e12, 4), "rotation_copies": R}), flush=True)
+        del copies
+        torch.cuda.empty_cache()
+    pass_us = synth.N_LAYERS * sum(floors[n] for n, _, _ in synth.LAYER_LINEARS) + floors["lm_head"]
+    pass_bytes = synth.N_LAYERS * sum(N * K * 0.51953125 for _, N, K in synth.LAYER_LINEARS) + \
+        synth.LM_HEAD[1] * synth.LM_HEAD[2] * 0.51953125
+    print(json.dumps({"pass_floor_us": round(pass_us, 1), "pass_bytes": int(pass_bytes),
+                      "floor_tbps": round(pass_bytes / (pass_us * 1e-6) / 1e12, 4),
+                      "floor_roofline_frac": round(pass_bytes / (HBM_PEAK_GBS * 1e9) * 1e6 / pass_us, 4)}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -366,6 +497,14 @@ def main():
         sys.exit(2)
     if args.shapes:
         shapes_report(args)
+        return
+    if args.floor:
+        floor_report(args)
+        return
+    if args.traffic_from:
+        out = traffic_from_pmc(args.traffic_from[0], args.traffic_from[1], args.copy_calib or 1024,
+                               os.path.join(ROOT, "profiles", "traffic.json"))
+        print(json.dumps(out))
         return
     import torch
 
@@ -384,6 +523,8 @@ def main():
     log(f"[bench] model resident after {t_model:.1f} s; checked layers {check_layers}, lm_head cols {n0}..{n0 + 512}")
 
     dev = "cuda:0"
+    if args.copy_calib:
+        copy_calibration(torch, w4, args.copy_calib)
     xs = {K: torch.from_numpy(synth.gen_x(64, K).view(np.int16)).to(dev) for K in (8192, 28672)}
     ys = {N: torch.empty((64, N), dtype=torch.float32, device=dev) for N in (1024, 8192, 28672, 128256)}
     specs = model_specs()
@@ -477,7 +618,7 @@ def main():
             "time_share_us": round(us_per_pass[M], 1)}
     dom = max(kernels, key=lambda k: kernels[k]["time_share_us"])
     dk = kernels[dom]
-    traffic = traffic_from_profiles(dom)
+    traffic = traffic_from_profiles(dk["M"])
     roofline = {"bound": "hbm", "achieved": dk["achieved_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dk["achieved_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
                 "per_launch": "alg_bytes_per_launch = 0.51953125 N K + 2 M K + 4 M N averaged over the 561 "

@@ -772,27 +772,38 @@ __global__ void zero_kernel(float* __restrict__ y, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) y[i] = 0.0f;
 }
 
-__global__ __launch_bounds__(256) void bench_read_kernel(const u32x4* __restrict__ buf, size_t n16,
+// Streaming read of a buffer (the HBM read ceiling and the per-linear read
+// floor): workgroup b reads the contiguous 1 KB blocks [b*per, (b+1)*per),
+// wave w every fourth of them, U 16-byte loads per lane in flight; the last
+// workgroup also reads the tail past the last whole block.  Each workgroup
+// writes the xor of everything it read to sink[b], so no load can be dropped.
+template <int U>
+__global__ __launch_bounds__(256) void bench_read_kernel(const u32x4* __restrict__ buf, size_t n16, size_t per,
                                                          uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const size_t nblk = n16 / 64;
+    const size_t b0 = (size_t)blockIdx.x * per;
+    const size_t b1 = min(nblk, b0 + per);
     uint32_t acc = 0;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4 v0 = __builtin_nontemporal_load(buf + i);
-        const u32x4 v1 = __builtin_nontemporal_load(buf + i + stride);
-        const u32x4 v2 = __builtin_nontemporal_load(buf + i + 2 * stride);
-        const u32x4 v3 = __builtin_nontemporal_load(buf + i + 3 * stride);
-        acc ^= v0[0] ^ v0[1] ^ v0[2] ^ v0[3] ^ v1[0] ^ v1[1] ^ v1[2] ^ v1[3];
-        acc ^= v2[0] ^ v2[1] ^ v2[2] ^ v2[3] ^ v3[0] ^ v3[1] ^ v3[2] ^ v3[3];
+    size_t b = b0 + wave;
+    for (; b + 4 * (U - 1) < b1; b += 4 * U) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(buf + (b + 4 * u) * 64 + lane);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     }
-    for (; i < n16; i += stride) {
-        const u32x4 v = buf[i];
+    for (; b < b1; b += 4) {
+        const u32x4 v = buf[b * 64 + lane];
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
-    // xor-reduce the workgroup
+    if (blockIdx.x == gridDim.x - 1 && wave == 0 && nblk * 64 + lane < n16) {
+        const u32x4 v = buf[nblk * 64 + lane];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
     for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
     __shared__ uint32_t part[4];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    if (lane == 0) part[wave] = acc;
     __syncthreads();
     if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
@@ -961,7 +972,16 @@ hipError_t launch_zero(float* y, size_t n, hipStream_t stream) {
 }
 
 hipError_t launch_bench_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream) {
-    return launch(bench_read_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4*)buf, bytes / 16, sink);
+    // Measured on MI355X (graph-replayed, rotating past the MALL): up to
+    // 64 MB, `blocks` (2048) workgroups with 4 loads per lane in flight
+    // stream best; above, a quarter of them with 8.
+    const size_t n16 = bytes / 16;
+    const size_t nblk = n16 / 64;
+    const bool big = bytes > (size_t(64) << 20);
+    const int grid = (int)std::max<size_t>(1, std::min<size_t>(big ? blocks / 4 : blocks, std::max<size_t>(nblk, 1)));
+    const size_t per = (nblk + grid - 1) / grid;
+    if (big) return launch(bench_read_kernel<8>, dim3(grid), dim3(256), 0, stream, (const u32x4*)buf, n16, per, sink);
+    return launch(bench_read_kernel<4>, dim3(grid), dim3(256), 0, stream, (const u32x4*)buf, n16, per, sink);
 }
 
 hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
