@@ -832,28 +832,33 @@ int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Pl
     if (splits > 0) {
         S = splits;
     } else {
-        // Measured on MI355X: a launch streams best with about one
-        // workgroup per CU; a partly filled last round leaves CUs idle, and
-        // every workgroup pays a start-up and split-K fix-up cost worth about
-        // four groups of work.  So pick the split count S minimising
-        //     rounds(S) * (groups per workgroup + 4),   rounds = ceil(wgs / 256),
-        // the smallest such S, with >= 4 groups per workgroup and the split-K
-        // partial traffic capped.
-        const int slots = 256;
-        const long weight_bytes = (long)NC * kChunkN * K / 2;
-        const long partial_per_split = (long)M * NC * kChunkN * 4 * 2;  // written + read
-        // partials stay under half the weight bytes, or under all of them for
-        // the M > 32 kernel, which is bound by its MFMA and VALU work per CU
-        // rather than by HBM
-        const int s_traffic =
-            (int)std::max<long>(1, weight_bytes / ((variant == kVarLds ? 1 : 2) * partial_per_split));
-        const int smax = std::max(1, std::min(G / 4, s_traffic));
+        // Time model, calibrated on MI355X sweeps of forced split counts:
+        //   t(S) = rounds(S) * (G/S + 4) * t_group
+        //        + [S > 1] * (2 us + S * M * NCpad * 8 bytes / 5 TB/s)
+        // rounds: about one workgroup per CU streams best.  For the
+        // memory-bound M <= 16 kernels rounds = ceil(workgroups / 256) (a
+        // partly filled last round leaves CUs idle) and a workgroup keeps >= 4
+        // groups; the compute-bound M > 16 kernel fits two workgroups per CU
+        // side by side, which smooths a partial round: rounds = max(1,
+        // workgroups / 256), down to 2 groups per workgroup.  Every workgroup
+        // pays start-up worth ~4 groups; a split adds the reduction launch
+        // and its partial traffic (written, then read back).  t_group is one
+        // group of one workgroup: ~0.64 us for the M <= 16 kernels (16 KB of
+        // weights at a CU's share of HBM), ~0.375 us per row block of 16 for
+        // the M > 16 kernel.  The smallest S of least t wins.
+        const bool lds = variant == kVarLds;
+        const double t_group = lds ? 0.375 * mb : 0.64;
+        const double red_bytes = (double)M * NC * kChunkN * 8;
+        const int smax = std::max(1, lds ? G / 2 : G / 4);
         S = 1;
         double best = 1e30;
         for (int s = 1; s <= smax; ++s) {
-            const double cost = (double)ceil_div((long)ntiles * s, slots) * ((double)G / s + 4.0);
-            if (cost < best - 1e-9) {
-                best = cost;
+            const double wgs = (double)ntiles * s;
+            const double rounds = lds ? std::max(1.0, wgs / 256.0) : (double)ceil_div((long)ntiles * s, 256);
+            double t = rounds * ((double)G / s + 4.0) * t_group;
+            if (s > 1) t += 2.0 + s * red_bytes / 5e6;
+            if (t < best - 1e-9) {
+                best = t;
                 S = s;
             }
         }
