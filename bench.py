@@ -308,6 +308,18 @@ def parity_checks(torch, w4, packed, host, xs, check_layers, n0):
 
 # ---------------------------------------------------------------------------
 
+def cost_table(us_per_pass):
+    """Speed-up of speculative decoding over plain decoding from the measured
+    pass times (the verification-cost model of the package's cost_model)."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location(
+        "cost_model", os.path.join(ROOT, "speculative_decoding_verification_w4a16_amd", "cost_model.py"))
+    cm = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(cm)
+    return cm.table(us_per_pass)
+
+
 def copy_calibration(torch, w4, mib):
     """A plain copy of known size (mib MiB read and written, five times): what
     the HBM byte counters read for it scales their readings of the kernels."""
@@ -658,6 +670,7 @@ def main():
         "hbm_read_ceiling_tbps": round(ceiling / 1000, 4),
         "roofline": roofline,
         "kernels": kernels,
+        "cost_model": cost_table(us_per_pass),
         "cpu_baseline": cpu,
         "parity": parity,
         "setup_s": round(t_model, 1),
