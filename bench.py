@@ -308,6 +308,107 @@ def parity_checks(torch, w4, packed, host, xs, check_layers, n0):
 
 # ---------------------------------------------------------------------------
 
+def fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args):
+    """The same pass with the projections that share an input fused: per
+    layer qkv (N = 10240) | o | gate+up (N = 57344) | down, plus the lm_head
+    (321 launches instead of 561), with fp32 output and with the bf16
+    epilogue.  Weights are the sweep's, concatenated on the device (the tile
+    layout is chunk-major).  Graph-replayed like the sweep; parity of the
+    fused linears on the checked layers' sampled columns (fp32 output against
+    the contract, bf16 output against the rounded fp32 output)."""
+    import synth
+    from oracle import check_contract, linear64_columns
+
+    dev = "cuda:0"
+    groups = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",))]
+    fpk, fspec = {}, []
+    for L in range(synth.N_LAYERS):
+        for fname, names in groups:
+            pk = packed[(L, names[0])] if len(names) == 1 else w4.concat_packed([packed[(L, n)] for n in names])
+            fpk[(L, fname)] = pk
+            fspec.append((L, fname, pk.N, pk.K))
+    fpk[(None, "lm_head")] = packed[(None, "lm_head")]
+    fspec.append((None, "lm_head", synth.LM_HEAD[1], synth.LM_HEAD[2]))
+    yf = {N: torch.empty((64, N), dtype=torch.float32, device=dev) for N in {s[2] for s in fspec}}
+    yb = {N: torch.empty((64, N), dtype=torch.int16, device=dev) for N in {s[2] for s in fspec}}
+    out = {"launches_per_pass": len(fspec), "us_per_pass": {}, "us_per_pass_bf16_out": {}, "tbps_per_pass": {},
+           "roofline_frac_per_pass": {}}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            fn()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(3, args.steps)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(reps):
+            g.replay()
+        s1.record()
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) * 1e3 / reps
+
+    for M in PASS_M:
+        descs = [dict(x=xs[K][:M], qweight_t=fpk[(L, f)].qweight_t, scales_t=fpk[(L, f)].scales_t,
+                      zeros_t=fpk[(L, f)].zeros_t, y=yf[N][:M], N=N, K=K) for (L, f, N, K) in fspec]
+        us = timed(lambda: w4.w4a16_verify_pass(descs, M))
+
+        def bf16_pass():
+            for (L, f, N, K) in fspec:
+                w4.linear(xs[K][:M], fpk[(L, f)], y=yb[N][:M], out_bf16=True)
+
+        us_b = timed(bf16_pass)
+        B = sum(alg_bytes(M, N, K) for (_, _, N, K) in fspec)
+        F = sum(alg_flops(M, N, K) for (_, _, N, K) in fspec)
+        t_roof = max(B / (HBM_PEAK_GBS * 1e9), F / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+        out["us_per_pass"][str(M)] = round(us, 1)
+        out["us_per_pass_bf16_out"][str(M)] = round(us_b, 1)
+        out["tbps_per_pass"][str(M)] = round(B / (us * 1e-6) / 1e12, 4)
+        out["roofline_frac_per_pass"][str(M)] = round(t_roof / us, 4)
+    if args.no_parity:
+        out["worst_err_over_bound"] = None
+    else:
+        rng = np.random.default_rng(5)
+        worst = 0.0
+        for M in PASS_M:
+            for L in check_layers:
+                for fname, names in groups:
+                    if len(names) == 1:
+                        continue
+                    pk = fpk[(L, fname)]
+                    K = pk.K
+                    y = w4.linear(xs[K][:M], pk).cpu().numpy()
+                    ybits = w4.linear(xs[K][:M], pk, out_bf16=True).cpu().numpy().view(np.uint16)
+                    if not np.array_equal(ybits, oracle_round_bf16(y)):
+                        raise SystemExit(f"fused bf16 output != rounded fp32 output: layer {L} {fname} M={M}")
+                    c0 = 0
+                    for n in names:
+                        lin = host[(L, n)]
+                        N = lin["scales"].shape[1]
+                        a = int(rng.integers(0, N // 64)) * 64
+                        Y, A = linear64_columns(synth.gen_x(M, K), lin["qweight"], lin["scales"], lin["zeros"], 128,
+                                                a, a + 64)
+                        ok, w = check_contract(y[:, c0 + a:c0 + a + 64], Y, A)
+                        if not ok:
+                            raise SystemExit(f"fused parity failure: layer {L} {fname}/{n} M={M} ratio {w}")
+                        worst = max(worst, w)
+                        c0 += N
+        out["worst_err_over_bound"] = worst
+    del fpk, yf, yb
+    torch.cuda.empty_cache()
+    return out
+
+
+def oracle_round_bf16(y):
+    from oracle import round_to_bf16
+
+    return round_to_bf16(y)
+
+
 def cost_table(us_per_pass):
     """Speed-up of speculative decoding over plain decoding from the measured
     pass times (the verification-cost model of the package's cost_model)."""
@@ -637,6 +738,8 @@ def main():
                               "linears of the pass; achieved = that / (graph pass time / 561); a linear is the "
                               "kernel plus splitk_reduce_kernel when its K is split"}
 
+    fused = fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args)
+
     ceiling = hbm_read_ceiling(torch, w4)
     parity = None
     if not args.no_parity:
@@ -670,7 +773,9 @@ def main():
         "hbm_read_ceiling_tbps": round(ceiling / 1000, 4),
         "roofline": roofline,
         "kernels": kernels,
+        "fused": fused,
         "cost_model": cost_table(us_per_pass),
+        "cost_model_fused": cost_table(fused["us_per_pass"]),
         "cpu_baseline": cpu,
         "parity": parity,
         "setup_s": round(t_model, 1),

@@ -97,8 +97,8 @@ int w4_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* zer
  *   y[M][N] (device, fp32, row-major, overwritten) =
  *       x[M][K] (device, bf16 bits, row-major) . dequant(qweight_t, scales_t, zeros_t)
  * with the tile-layout arrays from w4_repack.  0 <= M <= 64; M == 0 or
- * N == 0 does nothing; K == 0 writes y = 0.  Alignment: x and qweight_t 16
- * bytes, scales_t 8, zeros_t 2, y 4.  y must not overlap any input.
+ * N == 0 does nothing; K == 0 writes y = 0.  Alignment: x, qweight_t and y
+ * 16 bytes, scales_t 8, zeros_t 2.  y must not overlap any input.
  * Accumulation is fp32; each element is within 4e-3 * sum_k |x w| of the
  * exact value (in practice orders of magnitude closer).  The result does
  * not depend on the stream or on other calls.  M == 1 runs the VALU dot
@@ -116,6 +116,24 @@ enum { W4_KERNEL_AUTO = 0, W4_KERNEL_GEMV = 1, W4_KERNEL_MFMA = 2 };
 int w4a16_linear_cfg(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
                      const uint16_t* zeros_t, int M, int N, int K, int group, float* y, int kernel, int splits,
                      void* stream);
+
+/* Output element types for w4a16_linear_out. */
+enum { W4_OUT_F32 = 0, W4_OUT_BF16 = 1 };
+
+/* w4a16_linear_cfg with a choice of output type.  W4_OUT_F32: y is fp32, as
+ * in w4a16_linear.  W4_OUT_BF16: y (device, 16-byte aligned, M*N uint16
+ * bf16 bit patterns, row-major) receives the fp32 result rounded to nearest,
+ * ties to even -- bit for bit what rounding w4a16_linear_cfg's fp32 output
+ * with the same kernel and split count would give; half the output bytes,
+ * and the activation type the next layer consumes.  The pages leave the
+ * output type open; this is the bf16 epilogue of the fused-projection
+ * follow-up (qkv as one N = 10240 linear, gate|up as N = 57344: the tile
+ * layout of a column concatenation is the concatenation of the parts' tile
+ * layouts when every part's N is a multiple of 64).  Other out_dtype values:
+ * W4_ERR_INVALID. */
+int w4a16_linear_out(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                     const uint16_t* zeros_t, int M, int N, int K, int group, void* y, int out_dtype, int kernel,
+                     int splits, void* stream);
 
 /* The launch plan w4a16_linear_cfg would use (host outputs, any may be
  * NULL): kernel id, K splits, workgroups, threads per workgroup, LDS bytes

@@ -136,3 +136,27 @@ def check_contract(y, Y64, A64, rtol: float = CONTRACT_RTOL):
         ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
     worst = float(ratio.max()) if ratio.size else 0.0
     return bool(worst <= 1.0), worst
+
+
+def round_to_bf16(v) -> np.ndarray:
+    """bf16 epilogue (an output-type option; the pages leave the output type
+    open): the bf16 value nearest to each finite float32 input, ties to the
+    even significand, as uint16 bit patterns.  Written from the definition:
+    the two bf16 neighbours of v are its truncation toward zero and the next
+    bf16 away from zero; the nearer wins, measured exactly in float64."""
+    a = np.asarray(v, dtype=np.float32)
+    if not np.all(np.isfinite(a)):
+        raise ValueError("finite inputs only")
+    u = a.view(np.uint32).astype(np.uint64)
+    lo = u & np.uint64(0xFFFF0000)                 # toward zero
+    hi = lo + np.uint64(0x00010000)                # away from zero (may carry into the exponent: still correct)
+    vlo = lo.astype(np.uint32).view(np.float32).astype(np.float64)
+    vhi = hi.astype(np.uint32).view(np.float32).astype(np.float64)
+    # past the largest bf16 the next step is the overflow threshold 2^128
+    vhi = np.where(np.isinf(vhi), np.sign(vhi) * 2.0 ** 128, vhi)
+    x = a.astype(np.float64)
+    dlo, dhi = np.abs(x - vlo), np.abs(vhi - x)
+    lo_even = ((lo >> np.uint64(16)) & np.uint64(1)) == 0
+    take_hi = (dhi < dlo) | ((dhi == dlo) & ~lo_even)
+    return np.where(take_hi, hi, lo).astype(np.uint64) >> np.uint64(16)
+

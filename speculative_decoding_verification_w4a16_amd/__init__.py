@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 W4_OK, W4_ERR_INVALID, W4_ERR_UNSUPPORTED, W4_ERR_HIP = 0, 1, 2, 3
 W4_KERNEL_AUTO, W4_KERNEL_GEMV, W4_KERNEL_MFMA = 0, 1, 2
+W4_OUT_F32, W4_OUT_BF16 = 0, 1
 GROUP = 128
 MAX_M = 64
 
@@ -60,6 +61,7 @@ _c = {
     "w4_repack": _sig("w4_repack", [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "w4a16_linear": _sig("w4a16_linear", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "w4a16_linear_cfg": _sig("w4a16_linear_cfg", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _vp]),
+    "w4a16_linear_out": _sig("w4a16_linear_out", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp]),
     "w4a16_plan": _sig("w4a16_plan", [_i, _i, _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 5),
     "w4a16_verify_pass": _sig("w4a16_verify_pass", [ctypes.POINTER(W4LinearDesc), _i, _i, _i, _vp]),
     "w4_unpack": _sig("w4_unpack", [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
@@ -148,6 +150,13 @@ def w4a16_linear_cfg(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, kernel=
                                   kernel, splits, st), "w4a16_linear_cfg")
 
 
+def w4a16_linear_out(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype=W4_OUT_F32,
+                     kernel=W4_KERNEL_AUTO, splits=0, stream=None):
+    st = _stream(stream, x, y)
+    _check(_c["w4a16_linear_out"](_ptr(x), _ptr(qweight_t), _ptr(scales_t), _ptr(zeros_t), M, N, K, group, _ptr(y),
+                                  out_dtype, kernel, splits, st), "w4a16_linear_out")
+
+
 def w4a16_plan(M, N, K, group=GROUP, kernel=W4_KERNEL_AUTO, splits=0) -> dict:
     outs = [_i() for _ in range(5)]
     _check(_c["w4a16_plan"](M, N, K, group, kernel, splits, *[ctypes.byref(o) for o in outs]), "w4a16_plan")
@@ -213,12 +222,28 @@ def repack(qweight, scales, zeros, N, K, group=GROUP, stream=None) -> PackedLine
     return PackedLinear(qt, st, zt, N, K, group)
 
 
-def linear(x, w: PackedLinear, y=None, kernel=W4_KERNEL_AUTO, splits=0, stream=None):
-    """y[M, N] fp32 = x[M, K] (bf16 tensor or int16 bf16 bits) . dequant(w)."""
+def linear(x, w: PackedLinear, y=None, kernel=W4_KERNEL_AUTO, splits=0, stream=None, out_bf16=False):
+    """y[M, N] = x[M, K] (bf16 tensor or int16 bf16 bits) . dequant(w): fp32,
+    or bf16 bit patterns (int16 tensor) with out_bf16."""
     import torch
 
     M = x.shape[0]
     if y is None:
-        y = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
-    w4a16_linear_cfg(x, w.qweight_t, w.scales_t, w.zeros_t, M, w.N, w.K, w.group, y, kernel, splits, stream)
+        y = torch.empty((M, w.N), dtype=torch.int16 if out_bf16 else torch.float32, device=x.device)
+    w4a16_linear_out(x, w.qweight_t, w.scales_t, w.zeros_t, M, w.N, w.K, w.group, y,
+                     W4_OUT_BF16 if out_bf16 else W4_OUT_F32, kernel, splits, stream)
     return y
+
+
+def concat_packed(parts) -> PackedLinear:
+    """One linear computing the column concatenation of `parts` (same K and
+    group, every N a multiple of 64): the tile layout is chunk-major, so the
+    fused arrays are the parts' arrays end to end (a device copy)."""
+    import torch
+
+    K, group = parts[0].K, parts[0].group
+    for p in parts:
+        if p.K != K or p.group != group or p.N % 64 != 0:
+            raise ValueError("concat_packed needs equal K and group and every N a multiple of 64")
+    return PackedLinear(torch.cat([p.qweight_t for p in parts]), torch.cat([p.scales_t for p in parts]),
+                        torch.cat([p.zeros_t for p in parts]), sum(p.N for p in parts), K, group)

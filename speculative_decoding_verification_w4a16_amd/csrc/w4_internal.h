@@ -55,8 +55,9 @@ hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const i
 hipError_t launch_unpack(const uint32_t* qweight_t, const uint16_t* zeros_t, int N, int K, uint8_t* q_out,
                          uint8_t* z_out, hipStream_t stream);
 
+// y: fp32 [M][N], or bf16 bits [M][N] when out_bf16.
 hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
-                         const uint16_t* zeros_t, int M, int N, int K, float* y, const Workspace& ws,
+                         const uint16_t* zeros_t, int M, int N, int K, void* y, int out_bf16, const Workspace& ws,
                          hipStream_t stream);
 
 hipError_t launch_zero(float* y, size_t n, hipStream_t stream);

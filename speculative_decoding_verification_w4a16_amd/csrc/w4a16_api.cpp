@@ -86,17 +86,18 @@ void tile_sizes(int N, int K, size_t* qb, size_t* sb, size_t* zb) {
 
 // Validation of one linear call; fills the plan on success.
 int check_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, const uint16_t* zt, int M, int N, int K,
-                 int group, const float* y, int kernel, int splits, w4::Plan* plan) {
+                 int group, const void* y, int out_dtype, int kernel, int splits, w4::Plan* plan) {
     if (M < 0) return W4_ERR_INVALID;
     int rc = check_shape(N, K, group);
     if (rc != W4_OK) return rc;
     if (M > W4_MAX_M) return W4_ERR_UNSUPPORTED;
     if (kernel < W4_KERNEL_AUTO || kernel > W4_KERNEL_MFMA || splits < 0) return W4_ERR_INVALID;
+    if (out_dtype != W4_OUT_F32 && out_dtype != W4_OUT_BF16) return W4_ERR_INVALID;
     if (kernel == W4_KERNEL_GEMV && M > 1) return W4_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return W4_OK;  // nothing to compute
     if (!y) return W4_ERR_INVALID;
-    if (!aligned(y, 4)) return W4_ERR_INVALID;
-    const size_t ybytes = (size_t)M * N * 4;
+    if (!aligned(y, 16)) return W4_ERR_INVALID;
+    const size_t ybytes = (size_t)M * N * (out_dtype == W4_OUT_BF16 ? 2 : 4);
     if (K == 0) return W4_OK;  // y = 0
     if (!x || !qt || !st || !zt) return W4_ERR_INVALID;
     if (!aligned(x, 16) || !aligned(qt, 16) || !aligned(st, 8) || !aligned(zt, 2)) return W4_ERR_INVALID;
@@ -112,9 +113,13 @@ int check_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, cons
 }
 
 int run_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, const uint16_t* zt, int M, int N, int K,
-               float* y, const w4::Plan& plan, hipStream_t stream) {
+               void* y, int out_dtype, const w4::Plan& plan, hipStream_t stream) {
     if (M == 0 || N == 0) return W4_OK;
-    if (K == 0) return hip_status("zero_kernel launch", w4::launch_zero(y, (size_t)M * N, stream));
+    if (K == 0) {
+        // y = 0: M*N fp32 zeros, or half as many bytes of bf16 zeros
+        const size_t n = (size_t)M * N / (out_dtype == W4_OUT_BF16 ? 2 : 1);
+        return hip_status("zero_kernel launch", w4::launch_zero((float*)y, n, stream));
+    }
     w4::Workspace ws{};
     if (plan.splits > 1) {
         int rc = device_state(&ws);
@@ -123,7 +128,8 @@ int run_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, const 
         int rc = device_state(nullptr);  // kernel attributes
         if (rc != W4_OK) return rc;
     }
-    return hip_status("verify-linear launch", w4::launch_linear(plan, x, qt, st, zt, M, N, K, y, ws, stream));
+    return hip_status("verify-linear launch", w4::launch_linear(plan, x, qt, st, zt, M, N, K, y,
+                                                                out_dtype == W4_OUT_BF16, ws, stream));
 }
 
 }  // namespace
@@ -177,13 +183,20 @@ int w4_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* zer
                                                           (hipStream_t)stream));
 }
 
+int w4a16_linear_out(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                     const uint16_t* zeros_t, int M, int N, int K, int group, void* y, int out_dtype, int kernel,
+                     int splits, void* stream) {
+    w4::Plan plan{};
+    int rc = check_linear(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype, kernel, splits, &plan);
+    if (rc != W4_OK) return rc;
+    return run_linear(x, qweight_t, scales_t, zeros_t, M, N, K, y, out_dtype, plan, (hipStream_t)stream);
+}
+
 int w4a16_linear_cfg(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
                      const uint16_t* zeros_t, int M, int N, int K, int group, float* y, int kernel, int splits,
                      void* stream) {
-    w4::Plan plan{};
-    int rc = check_linear(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, kernel, splits, &plan);
-    if (rc != W4_OK) return rc;
-    return run_linear(x, qweight_t, scales_t, zeros_t, M, N, K, y, plan, (hipStream_t)stream);
+    return w4a16_linear_out(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, W4_OUT_F32, kernel, splits,
+                            stream);
 }
 
 int w4a16_linear(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t, const uint16_t* zeros_t,
@@ -214,8 +227,8 @@ int w4a16_verify_pass(const w4_linear_desc* linears, int n, int M, int group, vo
     // validate everything first so a bad entry launches nothing
     for (int i = 0; i < n; ++i) {
         const w4_linear_desc& d = linears[i];
-        int rc = check_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, group, d.y, W4_KERNEL_AUTO, 0,
-                              nullptr);
+        int rc = check_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, group, d.y, W4_OUT_F32,
+                              W4_KERNEL_AUTO, 0, nullptr);
         if (rc != W4_OK) return rc;
     }
     for (int i = 0; i < n; ++i) {
@@ -224,7 +237,8 @@ int w4a16_verify_pass(const w4_linear_desc* linears, int n, int M, int group, vo
         if (M > 0 && d.N > 0 && d.K > 0 &&
             w4::plan_linear(M, d.N, d.K, W4_KERNEL_AUTO, 0, w4::kWorkspaceBytes, &plan) != 0)
             return W4_ERR_UNSUPPORTED;
-        int rc = run_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, d.y, plan, (hipStream_t)stream);
+        int rc = run_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, d.y, W4_OUT_F32, plan,
+                            (hipStream_t)stream);
         if (rc != W4_OK) return rc;
     }
     return W4_OK;

@@ -199,7 +199,8 @@ struct LinearArgs {
     const u32x4* qt;
     const uint2* st;
     const uint16_t* zt;
-    float* y;
+    float* y;        // fp32 output, or
+    uint16_t* yb;    // bf16 output (round to nearest even) when not null
     float* ws;
     int M, N, K;
     int NC, KB, G;
@@ -207,6 +208,21 @@ struct LinearArgs {
     uint32_t mask;   // 0x000F000F (see unpack_biased)
     uint32_t magic;  // 0x43004300: bf16 128.0 in both halves
 };
+
+// fp32 -> bf16, round to nearest, ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Final value of y[i] (unsplit K): fp32, or bf16 for the bf16 epilogue.
+__device__ __forceinline__ void store_y(const LinearArgs& a, size_t i, float v) {
+    if (a.yb)
+        a.yb[i] = f32_to_bf16_rne(v);
+    else
+        a.y[i] = v;
+}
 
 // Workgroup barrier for an LDS producer/consumer hand-off.  It waits for this
 // wave's LDS operations only: __syncthreads() also waits for every
@@ -370,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
             const int n = c * kChunkN + 16 * j + t;
             if (n < a.N) {
                 if (a.splits == 1)
-                    a.y[n] = yv[j];
+                    store_y(a, n, yv[j]);
                 else
                     store_partial(a.ws + (size_t)split * a.NC * kChunkN + n, yv[j]);
             }
@@ -491,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_direct_kernel(LinearArgs 
                     const int m = 16 * mb + 4 * o + r;
                     if (m < a.M && n < a.N) {
                         if (a.splits == 1)
-                            a.y[(size_t)m * a.N + n] = yv[mb][j][r];
+                            store_y(a, (size_t)m * a.N + n, yv[mb][j][r]);
                         else
                             store_partial(a.ws + ((size_t)split * a.M + m) * npad + n, yv[mb][j][r]);
                     }
@@ -717,7 +733,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     const int m = 16 * mb + 4 * o + r;
                     if (m < a.M && n < a.N) {
                         if (a.splits == 1)
-                            a.y[(size_t)m * a.N + n] = yv[mb][j][r];
+                            store_y(a, (size_t)m * a.N + n, yv[mb][j][r]);
                         else
                             store_partial(a.ws + ((size_t)split * a.M + m) * npad + n, yv[mb][j][r]);
                     }
@@ -741,7 +757,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // row keeps its S partial vectors in flight together and adds them in split
 // order (deterministic).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, float* __restrict__ y,
-                                                          int M, int N, int npad, int splits) {
+                                                          uint16_t* __restrict__ yb, int M, int N, int npad,
+                                                          int splits) {
     const int nq = N / 4;
     const size_t total = (size_t)M * nq;
     const size_t plane = (size_t)M * npad;
@@ -760,7 +777,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
             for (int i = 0; i < kB; ++i)
                 if (s0 + i < splits) acc += v[i];
         }
-        *(f32x4*)(y + (size_t)m * N + n) = acc;
+        const size_t o = (size_t)m * N + n;
+        if (yb) {
+            const float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+            const uint32_t lo = f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+            const uint32_t hi = f32_to_bf16_rne(a2) | ((uint32_t)f32_to_bf16_rne(a3) << 16);
+            *(uint2*)(yb + o) = uint2{lo, hi};
+        } else {
+            *(f32x4*)(y + o) = acc;
+        }
     }
 }
 
@@ -933,14 +958,15 @@ hipError_t launch_unpack(const uint32_t* qweight_t, const uint16_t* zeros_t, int
 }
 
 hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
-                         const uint16_t* zeros_t, int M, int N, int K, float* y, const Workspace& ws,
+                         const uint16_t* zeros_t, int M, int N, int K, void* y, int out_bf16, const Workspace& ws,
                          hipStream_t stream) {
     LinearArgs a;
     a.x = x;
     a.qt = (const u32x4*)qweight_t;
     a.st = (const uint2*)scales_t;
     a.zt = zeros_t;
-    a.y = y;
+    a.y = out_bf16 ? nullptr : (float*)y;
+    a.yb = out_bf16 ? (uint16_t*)y : nullptr;
     a.ws = ws.partial;
     a.M = M;
     a.N = N;
@@ -969,7 +995,7 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
     if (e != hipSuccess || p.splits == 1) return e;
     const size_t total = (size_t)M * (N / 4);
     return launch(splitk_reduce_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, (const float*)ws.partial,
-                  y, M, N, a.NC * kChunkN, p.splits);
+                  a.y, a.yb, M, N, a.NC * kChunkN, p.splits);
 }
 
 hipError_t launch_zero(float* y, size_t n, hipStream_t stream) {

@@ -73,6 +73,24 @@ def test_linear_argument_errors(kw, code):
     assert e.value.status == code
 
 
+def test_linear_out_argument_errors():
+    def out(**kw):
+        a = dict(x=0x1000, q=0x2000, s=0x3000, z=0x4000, M=4, N=256, K=512, g=128, y=0x100000, dt=0)
+        a.update(kw)
+        return w4.w4a16_linear_out(a["x"], a["q"], a["s"], a["z"], a["M"], a["N"], a["K"], a["g"], a["y"], a["dt"],
+                                   stream=0)
+    for kw, code in [(dict(dt=2), 1), (dict(dt=-1), 1), (dict(y=0x100008), 1), (dict(y=0x100008, dt=1), 1),
+                     (dict(y=0x1000 + 256, dt=1), 1), (dict(M=65, dt=1), 2)]:
+        with pytest.raises(w4.W4Error) as e:
+            out(**kw)
+        assert e.value.status == code, kw
+    # a bf16 y of M*N*2 bytes that runs 16 bytes into x overlaps it
+    with pytest.raises(w4.W4Error) as e:
+        out(y=0x1000 - 4 * 256 * 2 + 16, dt=1)
+    assert e.value.status == 1
+    assert w4.W4_OUT_F32 == 0 and w4.W4_OUT_BF16 == 1
+
+
 def test_empty_calls_are_noops():
     # nothing to compute: returns OK without touching memory or the GPU
     _lin(M=0, x=0, q=0, s=0, z=0, y=0)
