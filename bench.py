@@ -72,6 +72,8 @@ def parse():
     p.add_argument("--m", default="1,2,4,5,8,16,32,48,64", help="M grid for --shapes")
     p.add_argument("--names", default="q,k,v,o,gate,up,down,lm_head", help="linears for --shapes")
     p.add_argument("--splits", type=int, default=0, help="force the K split count in --shapes (0 = planner)")
+    p.add_argument("--kwaves", type=int, default=0,
+                   help="force the waves splitting a chunk's K range in --shapes (0 = planner; M <= 16)")
     p.add_argument("--rotate-gib", type=float, default=2.0)
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="instead of running: turn two rocprofv3 --pmc runs of the sweep (FETCH_SIZE, WRITE_SIZE; "
@@ -497,6 +499,8 @@ def shapes_report(args):
     w4.w4_init()
     table = {name: (N, K, 1000 + i) for i, (name, N, K) in enumerate(synth.LAYER_LINEARS)}
     table["lm_head"] = (synth.LM_HEAD[1], synth.LM_HEAD[2], 20000)
+    table["qkv"] = (10240, 8192, 21000)      # the fused projections' shapes
+    table["gate_up"] = (57344, 8192, 22000)
     Ms = [int(v) for v in args.m.split(",")]
     if args.copy_calib:
         copy_calibration(torch, w4, args.copy_calib)
@@ -511,14 +515,14 @@ def shapes_report(args):
         x = torch.from_numpy(synth.gen_x(max(Ms), K).view(np.int16)).to(dev)
         y = torch.empty((max(Ms), N), dtype=torch.float32, device=dev)
         for M in Ms:
-            plan = w4.w4a16_plan(M, N, K, splits=args.splits)
+            plan = w4.w4a16_plan(M, N, K, splits=args.splits, kwaves=args.kwaves)
             for pk in copies[:2]:
-                w4.linear(x[:M], pk, y=y[:M], splits=args.splits)
+                w4.linear(x[:M], pk, y=y[:M], splits=args.splits, kwaves=args.kwaves)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for pk in copies:
-                    w4.linear(x[:M], pk, y=y[:M], splits=args.splits)
+                    w4.linear(x[:M], pk, y=y[:M], splits=args.splits, kwaves=args.kwaves)
             g.replay()
             torch.cuda.synchronize()
             best = float("inf")

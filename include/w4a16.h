@@ -135,11 +135,25 @@ int w4a16_linear_out(const uint16_t* x, const uint32_t* qweight_t, const uint16_
                      const uint16_t* zeros_t, int M, int N, int K, int group, void* y, int out_dtype, int kernel,
                      int splits, void* stream);
 
-/* The launch plan w4a16_linear_cfg would use (host outputs, any may be
- * NULL): kernel id, K splits, workgroups, threads per workgroup, LDS bytes
- * per workgroup.  No HIP call. */
-int w4a16_plan(int M, int N, int K, int group, int kernel, int splits, int* kernel_out, int* splits_out,
-               int* grid_out, int* block_out, int* lds_out);
+/* w4a16_linear_out with the work decomposition of the M <= 16 kernels
+ * forced as well, for tests and tuning sweeps.  kwaves: 0 = automatic; 1 =
+ * each wave of a workgroup streams its own 64-column chunk (four per
+ * workgroup) over the workgroup's K split; 2, 4 or 8 = a workgroup of that
+ * many waves streams one chunk, its waves splitting the K split's groups and
+ * summing their parts in LDS (no split-K workspace when splits is 1).
+ * Reduced when the smallest K split has fewer groups than waves; kwaves > 1
+ * with M > 16, or not 0/1/2/4/8: W4_ERR_UNSUPPORTED, negative:
+ * W4_ERR_INVALID.  Same result contract as w4a16_linear. */
+int w4a16_linear_tune(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                      const uint16_t* zeros_t, int M, int N, int K, int group, void* y, int out_dtype, int kernel,
+                      int splits, int kwaves, void* stream);
+
+/* The launch plan w4a16_linear_tune would use for (kernel, splits, kwaves)
+ * (host outputs, any may be NULL): kernel id, K splits, waves splitting a
+ * chunk's K range, workgroups, threads per workgroup, LDS bytes per
+ * workgroup.  No HIP call. */
+int w4a16_plan(int M, int N, int K, int group, int kernel, int splits, int kwaves, int* kernel_out,
+               int* splits_out, int* kwaves_out, int* grid_out, int* block_out, int* lds_out);
 
 /* One linear of a verify pass (host struct; pointers are device). */
 typedef struct {

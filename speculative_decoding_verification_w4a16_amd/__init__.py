@@ -62,7 +62,9 @@ _c = {
     "w4a16_linear": _sig("w4a16_linear", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "w4a16_linear_cfg": _sig("w4a16_linear_cfg", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _vp]),
     "w4a16_linear_out": _sig("w4a16_linear_out", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp]),
-    "w4a16_plan": _sig("w4a16_plan", [_i, _i, _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 5),
+    "w4a16_linear_tune": _sig("w4a16_linear_tune",
+                              [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _vp]),
+    "w4a16_plan": _sig("w4a16_plan", [_i, _i, _i, _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 6),
     "w4a16_verify_pass": _sig("w4a16_verify_pass", [ctypes.POINTER(W4LinearDesc), _i, _i, _i, _vp]),
     "w4_unpack": _sig("w4_unpack", [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     "w4_bench_read": _sig("w4_bench_read", [_vp, _sz, _vp, _vp]),
@@ -157,10 +159,18 @@ def w4a16_linear_out(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dty
                                   out_dtype, kernel, splits, st), "w4a16_linear_out")
 
 
-def w4a16_plan(M, N, K, group=GROUP, kernel=W4_KERNEL_AUTO, splits=0) -> dict:
-    outs = [_i() for _ in range(5)]
-    _check(_c["w4a16_plan"](M, N, K, group, kernel, splits, *[ctypes.byref(o) for o in outs]), "w4a16_plan")
-    return dict(zip(("kernel", "splits", "grid", "block", "lds"), (o.value for o in outs)))
+def w4a16_linear_tune(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype=W4_OUT_F32,
+                      kernel=W4_KERNEL_AUTO, splits=0, kwaves=0, stream=None):
+    st = _stream(stream, x, y)
+    _check(_c["w4a16_linear_tune"](_ptr(x), _ptr(qweight_t), _ptr(scales_t), _ptr(zeros_t), M, N, K, group,
+                                   _ptr(y), out_dtype, kernel, splits, kwaves, st), "w4a16_linear_tune")
+
+
+def w4a16_plan(M, N, K, group=GROUP, kernel=W4_KERNEL_AUTO, splits=0, kwaves=0) -> dict:
+    outs = [_i() for _ in range(6)]
+    _check(_c["w4a16_plan"](M, N, K, group, kernel, splits, kwaves, *[ctypes.byref(o) for o in outs]),
+           "w4a16_plan")
+    return dict(zip(("kernel", "splits", "kwaves", "grid", "block", "lds"), (o.value for o in outs)))
 
 
 def w4a16_verify_pass(linears, M, group=GROUP, stream=None):
@@ -222,7 +232,7 @@ def repack(qweight, scales, zeros, N, K, group=GROUP, stream=None) -> PackedLine
     return PackedLinear(qt, st, zt, N, K, group)
 
 
-def linear(x, w: PackedLinear, y=None, kernel=W4_KERNEL_AUTO, splits=0, stream=None, out_bf16=False):
+def linear(x, w: PackedLinear, y=None, kernel=W4_KERNEL_AUTO, splits=0, stream=None, out_bf16=False, kwaves=0):
     """y[M, N] = x[M, K] (bf16 tensor or int16 bf16 bits) . dequant(w): fp32,
     or bf16 bit patterns (int16 tensor) with out_bf16."""
     import torch
@@ -230,8 +240,8 @@ def linear(x, w: PackedLinear, y=None, kernel=W4_KERNEL_AUTO, splits=0, stream=N
     M = x.shape[0]
     if y is None:
         y = torch.empty((M, w.N), dtype=torch.int16 if out_bf16 else torch.float32, device=x.device)
-    w4a16_linear_out(x, w.qweight_t, w.scales_t, w.zeros_t, M, w.N, w.K, w.group, y,
-                     W4_OUT_BF16 if out_bf16 else W4_OUT_F32, kernel, splits, stream)
+    w4a16_linear_tune(x, w.qweight_t, w.scales_t, w.zeros_t, M, w.N, w.K, w.group, y,
+                      W4_OUT_BF16 if out_bf16 else W4_OUT_F32, kernel, splits, kwaves, stream)
     return y
 
 

@@ -14,6 +14,8 @@ constexpr int kGroup = 128;   // quantisation group along k
 constexpr int kWaves = 4;     // waves per workgroup (one chunk each)
 constexpr int kThreads = kWaves * 64;
 constexpr int kTileN = kWaves * kChunkN;  // output columns per workgroup
+constexpr int kMaxWaves = 8;              // waves per workgroup when they split one chunk's K range
+constexpr int kMaxThreads = kMaxWaves * 64;
 
 enum KernelId { kAuto = 0, kGemv = 1, kMfma = 2 };
 
@@ -27,6 +29,7 @@ struct Plan {
     int variant;  // Variant
     int mb;       // m-blocks of 16 rows (MFMA)
     int splits;   // K splits (workgroups per column tile)
+    int kw;       // waves per workgroup splitting one chunk's K range (1: four chunks per workgroup)
     int gps;      // groups per split
     int ntiles;   // column tiles of kTileN columns
     int grid;     // workgroups
@@ -45,7 +48,9 @@ constexpr int kLdsLimit = 160 * 1024 - 256;  // room for the small static LDS
 // Split-K workspace size (per device).
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;
 
-int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Plan* p);
+// kwaves: 0 = the planner's choice, else 1, 2, 4 or 8 (M <= 16 only; the
+// M > 16 kernel always uses 1).  Returns non-zero for an impossible request.
+int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t ws_bytes, Plan* p);
 
 hipError_t set_kernel_attributes();
 

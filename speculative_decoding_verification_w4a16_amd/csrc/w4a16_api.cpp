@@ -86,12 +86,13 @@ void tile_sizes(int N, int K, size_t* qb, size_t* sb, size_t* zb) {
 
 // Validation of one linear call; fills the plan on success.
 int check_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, const uint16_t* zt, int M, int N, int K,
-                 int group, const void* y, int out_dtype, int kernel, int splits, w4::Plan* plan) {
+                 int group, const void* y, int out_dtype, int kernel, int splits, int kwaves, w4::Plan* plan) {
     if (M < 0) return W4_ERR_INVALID;
     int rc = check_shape(N, K, group);
     if (rc != W4_OK) return rc;
     if (M > W4_MAX_M) return W4_ERR_UNSUPPORTED;
     if (kernel < W4_KERNEL_AUTO || kernel > W4_KERNEL_MFMA || splits < 0) return W4_ERR_INVALID;
+    if (kwaves < 0) return W4_ERR_INVALID;
     if (out_dtype != W4_OUT_F32 && out_dtype != W4_OUT_BF16) return W4_ERR_INVALID;
     if (kernel == W4_KERNEL_GEMV && M > 1) return W4_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return W4_OK;  // nothing to compute
@@ -107,7 +108,8 @@ int check_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, cons
         overlap(y, ybytes, zt, zb))
         return W4_ERR_INVALID;
     if (plan) {
-        if (w4::plan_linear(M, N, K, kernel, splits, w4::kWorkspaceBytes, plan) != 0) return W4_ERR_UNSUPPORTED;
+        if (w4::plan_linear(M, N, K, kernel, splits, kwaves, w4::kWorkspaceBytes, plan) != 0)
+            return W4_ERR_UNSUPPORTED;
     }
     return W4_OK;
 }
@@ -183,13 +185,21 @@ int w4_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* zer
                                                           (hipStream_t)stream));
 }
 
+int w4a16_linear_tune(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                      const uint16_t* zeros_t, int M, int N, int K, int group, void* y, int out_dtype, int kernel,
+                      int splits, int kwaves, void* stream) {
+    w4::Plan plan{};
+    int rc =
+        check_linear(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype, kernel, splits, kwaves, &plan);
+    if (rc != W4_OK) return rc;
+    return run_linear(x, qweight_t, scales_t, zeros_t, M, N, K, y, out_dtype, plan, (hipStream_t)stream);
+}
+
 int w4a16_linear_out(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
                      const uint16_t* zeros_t, int M, int N, int K, int group, void* y, int out_dtype, int kernel,
                      int splits, void* stream) {
-    w4::Plan plan{};
-    int rc = check_linear(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype, kernel, splits, &plan);
-    if (rc != W4_OK) return rc;
-    return run_linear(x, qweight_t, scales_t, zeros_t, M, N, K, y, out_dtype, plan, (hipStream_t)stream);
+    return w4a16_linear_tune(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype, kernel, splits, 0,
+                             stream);
 }
 
 int w4a16_linear_cfg(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
@@ -204,18 +214,19 @@ int w4a16_linear(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* s
     return w4a16_linear_cfg(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, W4_KERNEL_AUTO, 0, stream);
 }
 
-int w4a16_plan(int M, int N, int K, int group, int kernel, int splits, int* kernel_out, int* splits_out,
-               int* grid_out, int* block_out, int* lds_out) {
+int w4a16_plan(int M, int N, int K, int group, int kernel, int splits, int kwaves, int* kernel_out,
+               int* splits_out, int* kwaves_out, int* grid_out, int* block_out, int* lds_out) {
     if (M <= 0 || N <= 0 || K <= 0) return W4_ERR_INVALID;
     int rc = check_shape(N, K, group);
     if (rc != W4_OK) return rc;
     if (M > W4_MAX_M) return W4_ERR_UNSUPPORTED;
-    if (kernel < W4_KERNEL_AUTO || kernel > W4_KERNEL_MFMA || splits < 0) return W4_ERR_INVALID;
+    if (kernel < W4_KERNEL_AUTO || kernel > W4_KERNEL_MFMA || splits < 0 || kwaves < 0) return W4_ERR_INVALID;
     if (kernel == W4_KERNEL_GEMV && M > 1) return W4_ERR_UNSUPPORTED;
     w4::Plan p{};
-    if (w4::plan_linear(M, N, K, kernel, splits, w4::kWorkspaceBytes, &p) != 0) return W4_ERR_UNSUPPORTED;
+    if (w4::plan_linear(M, N, K, kernel, splits, kwaves, w4::kWorkspaceBytes, &p) != 0) return W4_ERR_UNSUPPORTED;
     if (kernel_out) *kernel_out = p.kernel;
     if (splits_out) *splits_out = p.splits;
+    if (kwaves_out) *kwaves_out = p.kw;
     if (grid_out) *grid_out = p.grid;
     if (block_out) *block_out = p.block;
     if (lds_out) *lds_out = p.lds;
@@ -228,14 +239,14 @@ int w4a16_verify_pass(const w4_linear_desc* linears, int n, int M, int group, vo
     for (int i = 0; i < n; ++i) {
         const w4_linear_desc& d = linears[i];
         int rc = check_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, group, d.y, W4_OUT_F32,
-                              W4_KERNEL_AUTO, 0, nullptr);
+                              W4_KERNEL_AUTO, 0, 0, nullptr);
         if (rc != W4_OK) return rc;
     }
     for (int i = 0; i < n; ++i) {
         const w4_linear_desc& d = linears[i];
         w4::Plan plan{};
         if (M > 0 && d.N > 0 && d.K > 0 &&
-            w4::plan_linear(M, d.N, d.K, W4_KERNEL_AUTO, 0, w4::kWorkspaceBytes, &plan) != 0)
+            w4::plan_linear(M, d.N, d.K, W4_KERNEL_AUTO, 0, 0, w4::kWorkspaceBytes, &plan) != 0)
             return W4_ERR_UNSUPPORTED;
         int rc = run_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, d.y, W4_OUT_F32, plan,
                             (hipStream_t)stream);

@@ -24,6 +24,7 @@
 #include "w4_internal.h"
 
 #include <algorithm>
+#include <cmath>
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -205,6 +206,7 @@ struct LinearArgs {
     int M, N, K;
     int NC, KB, G;
     int gps, splits, ntiles;
+    int kw;          // waves of a workgroup that split one chunk's K range (1: four chunks per workgroup)
     uint32_t mask;   // 0x000F000F (see unpack_biased)
     uint32_t magic;  // 0x43004300: bf16 128.0 in both halves
 };
@@ -281,6 +283,28 @@ __device__ __forceinline__ WaveStream wave_stream(const LinearArgs& a, int c, in
     return ws;
 }
 
+// The work of one wave of the streaming kernels (M <= 16).  With kw == 1 a
+// workgroup covers four chunks, one per wave, over the groups of its K split;
+// with kw > 1 it covers one chunk and its kw waves split the split's groups
+// between them (contiguous, as even as possible), to be summed in LDS.
+struct WaveWork {
+    int split, c, kidx, g0, ng;
+};
+
+__device__ __forceinline__ WaveWork wave_work(const LinearArgs& a, int wave) {
+    WaveWork w;
+    w.split = blockIdx.x / a.ntiles;
+    const int tile = blockIdx.x - w.split * a.ntiles;
+    const int gs = w.split * a.gps;
+    const int gwg = min(a.G, gs + a.gps) - gs;
+    w.kidx = a.kw == 1 ? 0 : wave;
+    w.c = a.kw == 1 ? tile * kWaves + wave : tile;
+    const int lo = gwg * w.kidx / a.kw, hi = gwg * (w.kidx + 1) / a.kw;
+    w.g0 = gs + lo;
+    w.ng = hi - lo;  // >= 1: the planner gives every wave a group
+    return w;
+}
+
 __device__ __forceinline__ void decode_scales(uint2 sv, float (&sj)[4]) {
     sj[0] = f16_bits_to_f32(sv.x & 0xFFFFu);
     sj[1] = f16_bits_to_f32(sv.x >> 16);
@@ -308,14 +332,11 @@ constexpr int kRingGemv = 4;
 constexpr int kRingDirect1 = 4;
 
 template <int R>
-__global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
+__global__ __launch_bounds__(kMaxThreads) void w4a16_gemv_kernel(LinearArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int split = blockIdx.x / a.ntiles;
-    const int tile = blockIdx.x - split * a.ntiles;
-    const int g0 = split * a.gps;
-    const int ng = min(a.G, g0 + a.gps) - g0;
-    const int c = tile * kWaves + wave;
+    const WaveWork wk = wave_work(a, wave);
+    const int split = wk.split, c = wk.c, g0 = wk.g0, ng = wk.ng;
     const int o = lane >> 4, t = lane & 15;
     const uint32_t mask = a.mask, magic = to_vgpr(a.magic);
     // waves past the last chunk stream the last chunk again (never stored):
@@ -380,7 +401,19 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
         yv[j] += __shfl_xor(yv[j], 16);
         yv[j] += __shfl_xor(yv[j], 32);
     }
-    if (c < a.NC && o == 0) {
+    if (a.kw > 1) {
+        // the K parts of the chunk, summed by wave 0 in wave order
+        __shared__ float red[kMaxWaves][kChunkN];
+        if (o == 0)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) red[wk.kidx][4 * t + j] = yv[j];
+        __syncthreads();
+        if (wk.kidx == 0)
+            for (int k2 = 1; k2 < a.kw; ++k2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) yv[j] += red[k2][4 * t + j];
+    }
+    if (c < a.NC && o == 0 && wk.kidx == 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int n = c * kChunkN + 16 * j + t;
@@ -406,14 +439,11 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemv_kernel(LinearArgs a) {
 // zero-point term needs, already in the result layout (rows 4(l/16) + r).
 
 template <int MB, int R>
-__global__ __launch_bounds__(kThreads) void w4a16_mfma_direct_kernel(LinearArgs a) {
+__global__ __launch_bounds__(kMaxThreads) void w4a16_mfma_direct_kernel(LinearArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int split = blockIdx.x / a.ntiles;
-    const int tile = blockIdx.x - split * a.ntiles;
-    const int g0 = split * a.gps;
-    const int ng = min(a.G, g0 + a.gps) - g0;
-    const int c = tile * kWaves + wave;
+    const WaveWork wk = wave_work(a, wave);
+    const int split = wk.split, c = wk.c, g0 = wk.g0, ng = wk.ng;
     const int o = lane >> 4, t = lane & 15;
     const uint32_t mask = a.mask, magic = to_vgpr(a.magic);
     const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
@@ -495,7 +525,20 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_direct_kernel(LinearArgs 
         }
     }
 
-    if (c < a.NC) {
+    if (a.kw > 1) {
+        // the K parts of the chunk, summed by wave 0 in wave order
+        static_assert(MB == 1, "the LDS sum holds one row block");
+        __shared__ f32x4 red[kMaxWaves - 1][4][64];
+        if (wk.kidx > 0)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) red[wk.kidx - 1][j][lane] = yv[0][j];
+        __syncthreads();
+        if (wk.kidx == 0)
+            for (int k2 = 1; k2 < a.kw; ++k2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) yv[0][j] += red[k2 - 1][j][lane];
+    }
+    if (c < a.NC && wk.kidx == 0) {
         const size_t npad = (size_t)a.NC * kChunkN;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -845,42 +888,74 @@ __global__ __launch_bounds__(256) void bench_copy_kernel(u32x4* __restrict__ dst
 
 static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
-int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Plan* p) {
+int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t ws_bytes, Plan* p) {
     if (kernel == kAuto) kernel = (M == 1) ? kGemv : kMfma;
     if (kernel == kGemv && M != 1) return -1;
+    if (kwaves < 0 || kwaves > kMaxWaves || (kwaves & (kwaves - 1)) != 0) return -1;
     const int NC = ceil_div(N, kChunkN);
     const int G = K / kGroup;
     const int mb = ceil_div(M, 16);
     const int variant = kernel == kGemv ? kVarGemv : (mb == 1 ? kVarDirect : kVarLds);
-    const int ntiles = ceil_div(NC, kWaves);
-    int S;
-    if (splits > 0) {
+    if (variant == kVarLds && kwaves > 1) return -1;
+    int kw = 1;
+    int S = 1;
+    if (variant != kVarLds) {
+        // Streaming kernels (M <= 16): the work decomposition (kw waves per
+        // chunk, S K splits) of least modelled time.  Model, fitted to
+        // MI355X sweeps of every decomposition on the Llama-3-70B shapes:
+        // a CU streams at most ~30 GB/s and the chip ~5.8 TB/s; a launch
+        // costs ~3 us before the stream runs at rate; a split K adds ~3.5 us
+        // (partials, then the reduction launch) plus the partial traffic;
+        // waves beyond what the CUs hold at once (12 per CU for the GEMV,
+        // 8 for the MFMA kernel) cost ~3 us per extra round.  Ties go to
+        // fewer splits, then fewer waves per chunk.  Left to the planner, a
+        // chunk gets 1 or 4 waves: with 2 too few loads are in flight per CU
+        // (gate at M = 1: 33 us with 2, 27 us with 4), and 8 gained nothing.
+        const double bytes = 0.52 * N * (double)K;
+        const double red_bytes = (double)M * NC * kChunkN * 8;
+        const int wmax = variant == kVarGemv ? 12 : 8;
+        double best = 1e30;
+        for (int kwc = 1; kwc <= kMaxWaves; kwc *= 2) {
+            if (kwaves > 0 ? kwc != kwaves : (kwc != 1 && kwc != 4)) continue;
+            const int smax = std::max(1, G / kwc);
+            for (int sc = 1; sc <= smax; ++sc) {
+                if (splits > 0 && sc != splits) continue;
+                const long wgs = (long)(kwc == 1 ? ceil_div(NC, kWaves) : NC) * sc;
+                const long waves = wgs * (kwc == 1 ? kWaves : kwc);
+                const double rounds = std::ceil((double)waves / (256.0 * wmax));
+                const double active = (double)std::min<long>(256, wgs);
+                const double bw = std::min(5.8e6, active * 3.0e4);  // bytes per us
+                double t = bytes / bw + 3.0 + (rounds - 1.0) * 3.0;
+                if (sc > 1) t += 3.5 + sc * red_bytes / 5e6;
+                if (t < best - 1e-9) {
+                    best = t;
+                    kw = kwc;
+                    S = sc;
+                }
+            }
+        }
+        if (splits > 0) S = splits;
+        if (kwaves > 0) kw = kwaves;
+    } else if (splits > 0) {
         S = splits;
     } else {
-        // Time model, calibrated on MI355X sweeps of forced split counts:
-        //   t(S) = rounds(S) * (G/S + 4) * t_group
-        //        + [S > 1] * (2 us + S * M * NCpad * 8 bytes / 5 TB/s)
-        // rounds: about one workgroup per CU streams best.  For the
-        // memory-bound M <= 16 kernels rounds = ceil(workgroups / 256) (a
-        // partly filled last round leaves CUs idle) and a workgroup keeps >= 4
-        // groups; the compute-bound M > 16 kernel fits two workgroups per CU
-        // side by side, which smooths a partial round: rounds = max(1,
-        // workgroups / 256), down to 2 groups per workgroup.  Every workgroup
-        // pays start-up worth ~4 groups; a split adds the reduction launch
-        // and its partial traffic (written, then read back).  t_group is one
-        // group of one workgroup: ~0.64 us for the M <= 16 kernels (16 KB of
-        // weights at a CU's share of HBM), ~0.375 us per row block of 16 for
-        // the M > 16 kernel.  The smallest S of least t wins.
-        const bool lds = variant == kVarLds;
-        const double t_group = lds ? 0.375 * mb : 0.64;
+        const int ntiles = ceil_div(NC, kWaves);
+        // M > 16: time model calibrated on MI355X sweeps of forced split
+        // counts,
+        //   t(S) = max(1, workgroups / 256) * (G/S + 4) * t_group
+        //        + [S > 1] * (2 us + S * M * NCpad * 8 bytes / 5 TB/s):
+        // two workgroups fit side by side per CU, which smooths a partly
+        // filled round; every workgroup pays start-up worth ~4 groups;
+        // t_group ~0.375 us per row block of 16; S <= G/2.  The smallest S
+        // of least t wins.
+        const double t_group = 0.375 * mb;
         const double red_bytes = (double)M * NC * kChunkN * 8;
-        const int smax = std::max(1, lds ? G / 2 : G / 4);
+        const int smax = std::max(1, G / 2);
         S = 1;
         double best = 1e30;
         for (int s = 1; s <= smax; ++s) {
             const double wgs = (double)ntiles * s;
-            const double rounds = lds ? std::max(1.0, wgs / 256.0) : (double)ceil_div((long)ntiles * s, 256);
-            double t = rounds * ((double)G / s + 4.0) * t_group;
+            double t = std::max(1.0, wgs / 256.0) * ((double)G / s + 4.0) * t_group;
             if (s > 1) t += 2.0 + s * red_bytes / 5e6;
             if (t < best - 1e-9) {
                 best = t;
@@ -896,14 +971,19 @@ int plan_linear(int M, int N, int K, int kernel, int splits, size_t ws_bytes, Pl
         ++gps;
         S = ceil_div(G, gps);
     }
+    // every wave of a K-splitting workgroup needs a group of its own (the
+    // last split holds the fewest groups)
+    while (kw > 1 && G - (S - 1) * gps < kw) kw >>= 1;
+    const int ntiles = kw == 1 ? ceil_div(NC, kWaves) : NC;
     p->kernel = kernel;
     p->variant = variant;
     p->mb = mb;
     p->splits = S;
+    p->kw = kw;
     p->gps = gps;
     p->ntiles = ntiles;
     p->grid = ntiles * S;
-    p->block = kThreads;
+    p->block = 64 * (kw == 1 ? kWaves : kw);
     p->lds = 0;
     if (variant == kVarLds) {
         p->lds = lds_ring_bytes(mb);
@@ -977,6 +1057,7 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
     a.gps = p.gps;
     a.splits = p.splits;
     a.ntiles = p.ntiles;
+    a.kw = p.kw;
     a.mask = kNibbleMask;
     a.magic = kBiasMagic;
     const dim3 grid(p.grid), block(p.block);

@@ -137,11 +137,17 @@ def test_bench_argument_errors():
 def test_plans_fit_the_hardware(M, N, K):
     p = w4.w4a16_plan(M, N, K)
     assert p["kernel"] == (w4.W4_KERNEL_GEMV if M == 1 else w4.W4_KERNEL_MFMA)
-    assert p["block"] == 256 and p["lds"] <= 160 * 1024 - 256  # gfx950 LDS per workgroup, less the static part
+    assert p["lds"] <= 160 * 1024 - 256  # gfx950 LDS per workgroup, less the static part
     assert 1 <= p["splits"] <= K // 128
+    kw = p["kwaves"]
+    assert kw in (1, 2, 4, 8) and (M <= 16 or kw == 1)
     chunks = -(-N // 64)
-    per_tile = 4  # four 64-column chunks per workgroup, one per wave
-    assert p["grid"] == -(-chunks // per_tile) * p["splits"]
+    if kw == 1:  # four 64-column chunks per workgroup, one per wave
+        assert p["block"] == 256 and p["grid"] == -(-chunks // 4) * p["splits"]
+    else:  # one chunk per workgroup, its kw waves splitting K
+        assert p["block"] == 64 * kw and p["grid"] == chunks * p["splits"]
+        gps = -(-(K // 128) // p["splits"])
+        assert K // 128 - (p["splits"] - 1) * gps >= kw  # every wave has a group
     # the split-K workspace (64 MiB) holds every partial
     assert p["splits"] == 1 or p["splits"] * M * (-(-N // 64) * 64) * 4 <= 64 << 20
 
@@ -151,3 +157,33 @@ def test_forced_plans():
     assert p["kernel"] == w4.W4_KERNEL_MFMA and p["splits"] == 3
     p = w4.w4a16_plan(4, 256, 512, splits=100)
     assert p["splits"] == 4
+    p = w4.w4a16_plan(1, 8192, 8192, splits=1, kwaves=8)
+    assert (p["kwaves"], p["block"], p["grid"]) == (8, 512, 128)
+    p = w4.w4a16_plan(5, 8192, 8192, splits=2, kwaves=2)
+    assert (p["kwaves"], p["block"], p["grid"]) == (2, 128, 256)
+    p = w4.w4a16_plan(1, 1024, 512, splits=1, kwaves=8)  # 4 groups: at most 4 waves
+    assert p["kwaves"] == 4
+    p = w4.w4a16_plan(1, 1024, 512, splits=4, kwaves=8)  # 1 group per split
+    assert (p["kwaves"], p["block"]) == (1, 256)
+    p = w4.w4a16_plan(1, 8192, 8192, splits=1, kwaves=1)
+    assert (p["kwaves"], p["block"], p["grid"]) == (1, 256, 32)
+    for bad, status in ((3, 2), (16, 2), (-1, 1)):
+        with pytest.raises(w4.W4Error) as e:
+            w4.w4a16_plan(1, 8192, 8192, kwaves=bad)
+        assert e.value.status == status
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4a16_plan(33, 8192, 8192, kwaves=2)  # the M > 16 kernel does not split K in a workgroup
+    assert e.value.status == 2
+
+
+def test_linear_tune_argument_errors():
+    # validation happens before any HIP call: fake device addresses never load
+    a = 0x10000
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4a16_linear_tune(a, a + 0x100000, a + 0x200000, a + 0x300000, 1, 256, 512, 128, a + 0x400000,
+                             kwaves=-1, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4a16_linear_tune(a, a + 0x100000, a + 0x200000, a + 0x300000, 1, 256, 512, 128, a + 0x400000,
+                             kwaves=5, stream=0)
+    assert e.value.status == 2
