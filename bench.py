@@ -213,9 +213,11 @@ def per_launch_durations(torch, w4, descs, M, reps=2):
 
 
 def source_digest():
+    """Digest of the sources that define the verify-linear kernels (what the
+    HBM byte counters in profiles/traffic.json were taken on)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_verification_w4a16_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ("w4_internal.h", "w4a16_kernels.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -402,6 +404,71 @@ def fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args):
         out["worst_err_over_bound"] = worst
     del fpk, yf, yb
     torch.cuda.empty_cache()
+    return out
+
+
+def acceptance_bench(torch, w4, args):
+    """The acceptance step on the lm_head's logits (vocabulary 128256) for a
+    sequence draft (K = 4, the M = 5 pass) and a 63-token chain (the M = 64
+    pass), greedy and sampled: microseconds per call (graph-replayed, 50 calls
+    per replay), the bytes it must read -- target rows (K+1)*V*4, draft rows
+    K*V*4 and the final row's target and draft logits again (sampled) -- and
+    the rate against the 8 TB/s roofline.  Synthetic logits: target N(0, 2),
+    draft = target + N(0, 0.7); drafted tokens drawn from the draft; uniforms
+    drawn until every decision clears its boundary; (accepted, next) checked
+    against the oracle."""
+    from oracle import accept_greedy, accept_sampled, decision_margins, softmax64
+
+    dev = "cuda:0"
+    V = 128256  # the lm_head's vocabulary
+    rng = np.random.default_rng(17)
+    out = {}
+    for K in (4, 63):
+        L = rng.normal(0.0, 2.0, (K + 1, V)).astype(np.float32)
+        Q = (L[:K] + rng.normal(0.0, 0.7, (K, V))).astype(np.float32)
+        q = softmax64(Q)
+        d = np.array([rng.choice(V, p=q[j]) for j in range(K)], np.int32)
+        for _ in range(200):
+            u = rng.random(K + 1).astype(np.float32)
+            m = decision_margins(L, Q, d, u.astype(np.float64))
+            if min(m[:-1]) > 1e-5 and m[-1] > 2e-6:
+                break
+        Ld, Qd = torch.from_numpy(L).to(dev), torch.from_numpy(Q).to(dev)
+        dd, ud = torch.from_numpy(d).to(dev), torch.from_numpy(u).to(dev)
+        res = torch.empty(2, dtype=torch.int32, device=dev)
+        ok = True
+        for mode in ("greedy", "sampled"):
+            def call():
+                if mode == "greedy":
+                    w4.w4_accept_greedy(Ld, dd, K, V, res)
+                else:
+                    w4.w4_accept_sample(Ld, Qd, dd, ud, K, V, res)
+            call()
+            torch.cuda.synchronize()
+            got = tuple(int(v) for v in res.cpu())
+            exp = accept_greedy(L, d) if mode == "greedy" else accept_sampled(L, Q, d, u.astype(np.float64))
+            ok = ok and got == exp
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                for _ in range(50):
+                    call()
+            g.replay()
+            torch.cuda.synchronize()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(3, args.steps)
+            s0.record()
+            for _ in range(reps):
+                g.replay()
+            s1.record()
+            torch.cuda.synchronize()
+            us = s0.elapsed_time(s1) * 1e3 / (reps * 50)
+            nbytes = (K + 1) * V * 4 + (K * V * 4 + 2 * V * 4 if mode == "sampled" else 0)
+            out[f"K{K}_{mode}"] = {"us_per_call": round(us, 2), "bytes": nbytes,
+                                   "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                   "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "oracle_match": got == exp}
+            del g
+        out[f"K{K}_accepted_sampled"] = int(exp[0])
     return out
 
 
@@ -743,6 +810,7 @@ def main():
                               "kernel plus splitk_reduce_kernel when its K is split"}
 
     fused = fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args)
+    acceptance = acceptance_bench(torch, w4, args)
 
     ceiling = hbm_read_ceiling(torch, w4)
     parity = None
@@ -778,6 +846,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "fused": fused,
+        "acceptance": acceptance,
         "cost_model": cost_table(us_per_pass),
         "cost_model_fused": cost_table(fused["us_per_pass"]),
         "cpu_baseline": cpu,

@@ -16,3 +16,11 @@ from .w4a16_ref import (  # noqa: F401
     unpack_qweight,
     unpack_zeros,
 )
+from .accept_ref import (  # noqa: F401
+    accept_greedy,
+    accept_sampled,
+    argmax_first,
+    decision_margins,
+    inverse_cdf,
+    softmax64,
+)

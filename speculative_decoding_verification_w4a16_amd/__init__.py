@@ -70,6 +70,8 @@ _c = {
     "w4_bench_read": _sig("w4_bench_read", [_vp, _sz, _vp, _vp]),
     "w4_bench_read_blocks": _sig("w4_bench_read_blocks", []),
     "w4_bench_copy": _sig("w4_bench_copy", [_vp, _vp, _sz, _vp]),
+    "w4_accept_greedy": _sig("w4_accept_greedy", [_vp, _vp, _i, _i, _vp, _vp]),
+    "w4_accept_sample": _sig("w4_accept_sample", [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]),
 }
 
 
@@ -196,6 +198,33 @@ def w4_bench_read_blocks() -> int:
 def w4_bench_read(buf, nbytes, sink, stream=None):
     st = _stream(stream, buf)
     _check(_c["w4_bench_read"](_ptr(buf), nbytes, _ptr(sink), st), "w4_bench_read")
+
+
+def w4_accept_greedy(logits, draft, K, V, out, stream=None):
+    st = _stream(stream, logits, out)
+    _check(_c["w4_accept_greedy"](_ptr(logits), _ptr(draft), K, V, _ptr(out), st), "w4_accept_greedy")
+
+
+def w4_accept_sample(logits, draft_logits, draft, u, K, V, out, stream=None):
+    st = _stream(stream, logits, out)
+    _check(_c["w4_accept_sample"](_ptr(logits), _ptr(draft_logits), _ptr(draft), _ptr(u), K, V, _ptr(out), st),
+           "w4_accept_sample")
+
+
+def accept(logits, draft, draft_logits=None, u=None, out=None, stream=None):
+    """Acceptance step on device tensors: logits [K+1, V] fp32, draft [K]
+    int32, and for the sampled step draft_logits [K, V] fp32 and u [K+1] fp32.
+    Returns an int32 tensor [2]: (drafted tokens accepted, next token)."""
+    import torch
+
+    K, V = logits.shape[0] - 1, logits.shape[1]
+    if out is None:
+        out = torch.empty(2, dtype=torch.int32, device=logits.device)
+    if draft_logits is None:
+        w4_accept_greedy(logits, draft, K, V, out, stream)
+    else:
+        w4_accept_sample(logits, draft_logits, draft, u, K, V, out, stream)
+    return out
 
 
 def w4_bench_copy(dst, src, nbytes, stream=None):

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <mutex>
 
+#include "../../include/w4_accept.h"
 #include "../../include/w4a16.h"
 #include "../../include/w4a16_bench.h"
 #include "w4_internal.h"
@@ -52,6 +53,11 @@ int device_state(w4::Workspace* out) {
         if (e != hipSuccess) return hip_fail("hipMalloc(workspace)", e);
         st.ws.partial = (float*)p;
         st.ws.partial_bytes = w4::kWorkspaceBytes;
+        p = nullptr;
+        e = hipMalloc(&p, w4::kAcceptWorkspaceBytes);
+        if (e != hipSuccess) return hip_fail("hipMalloc(acceptance workspace)", e);
+        st.ws.accept = p;
+        st.ws.accept_bytes = w4::kAcceptWorkspaceBytes;
         st.ready = true;
     }
     if (out) *out = st.ws;
@@ -59,6 +65,8 @@ int device_state(w4::Workspace* out) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool draft_logits_ok(int sampled, const void* p) { return !sampled || p != nullptr; }
 
 bool overlap(const void* a, size_t an, const void* b, size_t bn) {
     if (!a || !b || an == 0 || bn == 0) return false;
@@ -282,3 +290,42 @@ int w4_bench_copy(void* dst, const void* src, size_t bytes, void* stream) {
 }
 
 }  // extern "C"
+
+namespace {
+
+int accept_call(const float* logits, const float* draft_logits, const int32_t* draft, const float* u, int K, int V,
+                int sampled, int32_t* out, void* stream) {
+    if (K < 0 || V < 0) return W4_ERR_INVALID;
+    if (K > W4_ACCEPT_MAX_K || V > W4_ACCEPT_MAX_V || V % 4 != 0) return W4_ERR_UNSUPPORTED;
+    if (V < 4) return W4_ERR_UNSUPPORTED;
+    if (!logits || !draft_logits_ok(sampled, draft_logits) || !out || (K > 0 && !draft) || (sampled && !u))
+        return W4_ERR_INVALID;
+    if (!aligned(logits, 16) || (sampled && !aligned(draft_logits, 16)) || !aligned(out, 4) ||
+        (K > 0 && !aligned(draft, 4)) || (sampled && !aligned(u, 4)))
+        return W4_ERR_INVALID;
+    const size_t lb = (size_t)(K + 1) * V * 4, db = sampled ? (size_t)K * V * 4 : 0;
+    if (overlap(out, 8, logits, lb) || overlap(out, 8, draft_logits, db) || overlap(out, 8, draft, (size_t)K * 4) ||
+        (sampled && overlap(out, 8, u, (size_t)(K + 1) * 4)))
+        return W4_ERR_INVALID;
+    if (w4::accept_workspace_bytes(K, V) > w4::kAcceptWorkspaceBytes) return W4_ERR_UNSUPPORTED;
+    w4::Workspace ws{};
+    int rc = device_state(&ws);
+    if (rc != W4_OK) return rc;
+    return hip_status("acceptance launch", w4::launch_accept(logits, sampled ? draft_logits : logits, draft, u, K, V,
+                                                             sampled, out, ws.accept, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4_accept_greedy(const float* logits, const int32_t* draft, int K, int V, int32_t* out, void* stream) {
+    return accept_call(logits, nullptr, draft, nullptr, K, V, 0, out, stream);
+}
+
+int w4_accept_sample(const float* logits, const float* draft_logits, const int32_t* draft, const float* u, int K,
+                     int V, int32_t* out, void* stream) {
+    return accept_call(logits, draft_logits, draft, u, K, V, 1, out, stream);
+}
+
+}

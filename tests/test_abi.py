@@ -9,7 +9,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("w4a16.h", "w4a16_bench.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("w4a16.h", "w4a16_bench.h", "w4_accept.h")]
 
 w4 = pytest.importorskip("speculative_decoding_verification_w4a16_amd")
 
@@ -187,3 +187,25 @@ def test_linear_tune_argument_errors():
         w4.w4a16_linear_tune(a, a + 0x100000, a + 0x200000, a + 0x300000, 1, 256, 512, 128, a + 0x400000,
                              kwaves=5, stream=0)
     assert e.value.status == 2
+
+
+def test_accept_argument_errors():
+    # every check runs before a HIP call: fake device addresses never load
+    L, D, U, O, T = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    V = 128256
+    for args, code in [
+        (dict(K=-1), 1), (dict(V=-4), 1), (dict(K=65), 2), (dict(V=6), 2), (dict(V=0), 2), (dict(V=(1 << 24) + 4), 2),
+        (dict(logits=0), 1), (dict(out=0), 1), (dict(draft=0), 1), (dict(logits=L + 4), 1), (dict(out=O + 2), 1),
+        (dict(out=L + 16), 1),  # out inside the logits
+    ]:
+        a = dict(logits=L, draft=T, K=4, V=V, out=O)
+        a.update(args)
+        with pytest.raises(w4.W4Error) as e:
+            w4.w4_accept_greedy(a["logits"], a["draft"], a["K"], a["V"], a["out"], stream=0)
+        assert e.value.status == code, args
+    for args, code in [(dict(dl=0), 1), (dict(u=0), 1), (dict(dl=D + 8), 1), (dict(u=U + 2), 1), (dict(out=U), 1)]:
+        a = dict(dl=D, u=U, out=O)
+        a.update(args)
+        with pytest.raises(w4.W4Error) as e:
+            w4.w4_accept_sample(L, a["dl"], T, a["u"], 4, V, a["out"], stream=0)
+        assert e.value.status == code, args
