@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle on the host")
     p.add_argument("--no-parity", action="store_true", help="skip the oracle spot checks")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the fused-projection and acceptance measurements (profiling runs of the sweep)")
     p.add_argument("--shapes", action="store_true",
                    help="per-linear report instead of the sweep: each decoder shape and the lm_head at every M of "
                         "--m, graph-replayed over rotating weight copies (>= --rotate-gib) so HBM, not the 256 MB "
@@ -809,8 +811,10 @@ def main():
                               "linears of the pass; achieved = that / (graph pass time / 561); a linear is the "
                               "kernel plus splitk_reduce_kernel when its K is split"}
 
-    fused = fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args)
-    acceptance = acceptance_bench(torch, w4, args)
+    fused = acceptance = None
+    if not args.no_extras:
+        fused = fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args)
+        acceptance = acceptance_bench(torch, w4, args)
 
     ceiling = hbm_read_ceiling(torch, w4)
     parity = None
@@ -848,7 +852,7 @@ def main():
         "fused": fused,
         "acceptance": acceptance,
         "cost_model": cost_table(us_per_pass),
-        "cost_model_fused": cost_table(fused["us_per_pass"]),
+        "cost_model_fused": cost_table(fused["us_per_pass"]) if fused else None,
         "cpu_baseline": cpu,
         "parity": parity,
         "setup_s": round(t_model, 1),
