@@ -24,3 +24,4 @@ from .accept_ref import (  # noqa: F401
     inverse_cdf,
     softmax64,
 )
+from .tree_attn_ref import ancestor_masks, attention_weight_mass, tree_attention  # noqa: F401
