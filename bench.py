@@ -474,6 +474,70 @@ def acceptance_bench(torch, w4, args):
     return out
 
 
+def tree_attention_bench(torch, w4, args):
+    """Tree-draft verify attention of one layer (64 query heads over 8
+    key/value heads, head dim 128) over a 4096-position KV prefix, for the
+    pass M = 1, a 5-token chain (sequence draft) and a 64-token random tree
+    (tree draft): microseconds per call (graph-replayed, 20 calls per replay),
+    the KV bytes it must read, the flops it must do (q.k and p.v over every
+    visible key), and the rates against the 8 TB/s and 2.5 PFLOP/s rooflines.
+    Synthetic bf16 inputs N(0, 1); outputs checked against the oracle."""
+    from oracle import ancestor_masks, attention_weight_mass, tree_attention
+
+    dev = "cuda:0"
+    Hq, Hkv, D, L = 64, 8, 128, 4096
+    rng = np.random.default_rng(23)
+
+    def bf16(shape):
+        u = rng.normal(0.0, 1.0, shape).astype(np.float32).view(np.uint32).astype(np.uint64)
+        b = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+        return b, (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+    out = {"L": L, "heads": [Hq, Hkv, D]}
+    kcb, kc = bf16((L, Hkv, D))
+    vcb, vc = bf16((L, Hkv, D))
+    td = lambda b: torch.from_numpy(b.view(np.int16)).to(dev)
+    kcd, vcd = td(kcb), td(vcb)
+    for name, M, parents in (("M1", 1, [-1]), ("M5_chain", 5, list(range(-1, 4))),
+                             ("M64_tree", 64, [-1] + [int(rng.integers(-1, i)) for i in range(1, 64)])):
+        qb, q = bf16((M, Hq, D))
+        kdb, kd = bf16((M, Hkv, D))
+        vdb, vd = bf16((M, Hkv, D))
+        masks = ancestor_masks(parents)
+        qd, kdd, vdd = td(qb), td(kdb), td(vdb)
+        md = torch.from_numpy(masks.view(np.int64)).to(dev)
+        o = torch.empty((M, Hq, D), dtype=torch.float32, device=dev)
+        w4.tree_attention(qd, kcd, vcd, kdd, vdd, md, out=o)
+        torch.cuda.synchronize()
+        args_o = (q, kc, vc, kd, vd, masks)
+        ref, mass = tree_attention(*args_o), attention_weight_mass(*args_o)
+        worst = float(np.max(np.abs(o.cpu().numpy() - ref) / (1e-2 * mass + 1e-6)))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            for _ in range(20):
+                w4.tree_attention(qd, kcd, vcd, kdd, vdd, md, out=o)
+        g.replay()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(3, args.steps)
+        s0.record()
+        for _ in range(reps):
+            g.replay()
+        s1.record()
+        torch.cuda.synchronize()
+        us = s0.elapsed_time(s1) * 1e3 / (reps * 20)
+        visible = sum(bin(int(m)).count("1") for m in masks)
+        nbytes = 2 * L * Hkv * D * 2 + 2 * M * Hkv * D * 2 + M * Hq * D * 2 + M * Hq * D * 4
+        flops = 4.0 * Hq * D * (M * L + visible)
+        out[name] = {"M": M, "us_per_call": round(us, 2), "bytes": nbytes, "flops": flops,
+                     "TBps": round(nbytes / (us * 1e-6) / 1e12, 3), "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
+                     "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "frac_mfma": round(flops / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+                     "worst_err_over_bound": round(worst, 5)}
+        del g
+    return out
+
+
 def oracle_round_bf16(y):
     from oracle import round_to_bf16
 
@@ -811,10 +875,11 @@ def main():
                               "linears of the pass; achieved = that / (graph pass time / 561); a linear is the "
                               "kernel plus splitk_reduce_kernel when its K is split"}
 
-    fused = acceptance = None
+    fused = acceptance = tree = None
     if not args.no_extras:
         fused = fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args)
         acceptance = acceptance_bench(torch, w4, args)
+        tree = tree_attention_bench(torch, w4, args)
 
     ceiling = hbm_read_ceiling(torch, w4)
     parity = None
@@ -851,6 +916,7 @@ def main():
         "kernels": kernels,
         "fused": fused,
         "acceptance": acceptance,
+        "tree_attention": tree,
         "cost_model": cost_table(us_per_pass),
         "cost_model_fused": cost_table(fused["us_per_pass"]) if fused else None,
         "cpu_baseline": cpu,

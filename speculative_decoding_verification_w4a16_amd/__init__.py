@@ -72,6 +72,8 @@ _c = {
     "w4_bench_copy": _sig("w4_bench_copy", [_vp, _vp, _sz, _vp]),
     "w4_accept_greedy": _sig("w4_accept_greedy", [_vp, _vp, _i, _i, _vp, _vp]),
     "w4_accept_sample": _sig("w4_accept_sample", [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]),
+    "w4_tree_attention": _sig("w4_tree_attention",
+                              [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp, _vp]),
 }
 
 
@@ -224,6 +226,29 @@ def accept(logits, draft, draft_logits=None, u=None, out=None, stream=None):
         w4_accept_greedy(logits, draft, K, V, out, stream)
     else:
         w4_accept_sample(logits, draft_logits, draft, u, K, V, out, stream)
+    return out
+
+
+def w4_tree_attention(q, k_cache, v_cache, k_draft, v_draft, masks, M, L, num_heads, num_kv_heads, head_dim,
+                      scale, out, stream=None):
+    st = _stream(stream, q, out)
+    _check(_c["w4_tree_attention"](_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft), _ptr(v_draft), _ptr(masks),
+                                   M, L, num_heads, num_kv_heads, head_dim, scale, _ptr(out), st),
+           "w4_tree_attention")
+
+
+def tree_attention(q, k_cache, v_cache, k_draft, v_draft, masks, scale=0.0, out=None, stream=None):
+    """Tree-draft verify attention on device tensors: q [M, Hq, 128], caches
+    [L, Hkv, 128] and draft keys/values [M, Hkv, 128] as bf16 (or int16 bf16
+    bits), masks [M] int64 (uint64 bit patterns).  Returns fp32 [M, Hq, 128]."""
+    import torch
+
+    M, Hq, D = q.shape
+    L, Hkv = k_cache.shape[0], k_draft.shape[1]
+    if out is None:
+        out = torch.empty((M, Hq, D), dtype=torch.float32, device=q.device)
+    w4_tree_attention(q, k_cache if L else None, v_cache if L else None, k_draft, v_draft, masks, M, L, Hq, Hkv, D,
+                      scale, out, stream)
     return out
 
 

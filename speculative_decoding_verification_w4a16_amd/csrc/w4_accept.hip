@@ -20,7 +20,7 @@
 //   accept_draw_kernel    (stochastic only) the inverse-CDF draw: the slice
 //                         holding u * total, then a workgroup scan inside it.
 // Every reduction runs in a fixed order, so a call is deterministic.
-#include "w4_internal.h"
+#include "w4_aux.h"
 
 #include <algorithm>
 #include <cmath>

@@ -40,8 +40,6 @@ struct Plan {
 struct Workspace {
     float* partial;  // split-K partial sums, [S][M][NC*64] fp32
     size_t partial_bytes;
-    void* accept;    // acceptance step: row statistics, decision, draw partials
-    size_t accept_bytes;
 };
 
 // LDS budget per workgroup for the staged activation tile.
@@ -73,16 +71,5 @@ hipError_t launch_bench_read(const void* buf, size_t bytes, uint32_t* sink, int 
 hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 constexpr int kBenchReadBlocks = 256 * 8;
-
-// Acceptance step (w4_accept.hip).
-constexpr int kAcceptMaxK = 64;                     // drafted tokens per call
-constexpr int kAcceptMaxV = 1 << 24;                // vocabulary entries
-constexpr size_t kAcceptWorkspaceBytes = size_t(1) << 20;
-size_t accept_workspace_bytes(int K, int V);
-// lt: [K+1][V] target logits, ld: [K][V] draft logits (sampled only), draft:
-// [K] tokens, u: [K+1] uniforms (sampled only), out: [2] accepted count and
-// next token; ws: kAcceptWorkspaceBytes.
-hipError_t launch_accept(const float* lt, const float* ld, const int32_t* draft, const float* u, int K, int V,
-                         int sampled, int32_t* out, void* ws, hipStream_t stream);
 
 }  // namespace w4

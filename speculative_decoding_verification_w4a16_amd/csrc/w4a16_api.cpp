@@ -8,12 +8,15 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <mutex>
 
 #include "../../include/w4_accept.h"
+#include "../../include/w4_tree_attn.h"
 #include "../../include/w4a16.h"
 #include "../../include/w4a16_bench.h"
+#include "w4_aux.h"
 #include "w4_internal.h"
 
 namespace {
@@ -23,6 +26,8 @@ constexpr int kMaxDevices = 64;
 struct DeviceState {
     bool ready = false;
     w4::Workspace ws{};
+    void* accept = nullptr;  // acceptance step workspace
+    float* tree = nullptr;   // tree attention workspace
 };
 
 std::mutex g_mutex;
@@ -37,8 +42,8 @@ int hip_fail(const char* what, hipError_t e) {
 
 int hip_status(const char* what, hipError_t e) { return e == hipSuccess ? W4_OK : hip_fail(what, e); }
 
-// Workspace and kernel attributes of the current device, created once.
-int device_state(w4::Workspace* out) {
+// Workspaces and kernel attributes of the current device, created once.
+int device_state(w4::Workspace* out, void** accept = nullptr, float** tree = nullptr) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail("hipGetDevice", e);
@@ -56,11 +61,16 @@ int device_state(w4::Workspace* out) {
         p = nullptr;
         e = hipMalloc(&p, w4::kAcceptWorkspaceBytes);
         if (e != hipSuccess) return hip_fail("hipMalloc(acceptance workspace)", e);
-        st.ws.accept = p;
-        st.ws.accept_bytes = w4::kAcceptWorkspaceBytes;
+        st.accept = p;
+        p = nullptr;
+        e = hipMalloc(&p, w4::kTreeWorkspaceBytes);
+        if (e != hipSuccess) return hip_fail("hipMalloc(tree attention workspace)", e);
+        st.tree = (float*)p;
         st.ready = true;
     }
     if (out) *out = st.ws;
+    if (accept) *accept = st.accept;
+    if (tree) *tree = st.tree;
     return W4_OK;
 }
 
@@ -308,11 +318,11 @@ int accept_call(const float* logits, const float* draft_logits, const int32_t* d
         (sampled && overlap(out, 8, u, (size_t)(K + 1) * 4)))
         return W4_ERR_INVALID;
     if (w4::accept_workspace_bytes(K, V) > w4::kAcceptWorkspaceBytes) return W4_ERR_UNSUPPORTED;
-    w4::Workspace ws{};
-    int rc = device_state(&ws);
+    void* ws = nullptr;
+    int rc = device_state(nullptr, &ws);
     if (rc != W4_OK) return rc;
     return hip_status("acceptance launch", w4::launch_accept(logits, sampled ? draft_logits : logits, draft, u, K, V,
-                                                             sampled, out, ws.accept, (hipStream_t)stream));
+                                                             sampled, out, ws, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -328,4 +338,34 @@ int w4_accept_sample(const float* logits, const float* draft_logits, const int32
     return accept_call(logits, draft_logits, draft, u, K, V, 1, out, stream);
 }
 
+}
+
+extern "C" int w4_tree_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                 const uint16_t* k_draft, const uint16_t* v_draft, const uint64_t* masks, int M,
+                                 int L, int num_heads, int num_kv_heads, int head_dim, float scale, float* out,
+                                 void* stream) {
+    if (M < 0 || L < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return W4_ERR_INVALID;
+    if (!(scale >= 0.0f) || scale > 1e30f) return W4_ERR_INVALID;  // rejects NaN
+    if (head_dim != w4::kTreeHeadDim || M > W4_TREE_MAX_M || L > W4_TREE_MAX_L || num_heads % num_kv_heads != 0 ||
+        num_heads > 256)
+        return W4_ERR_UNSUPPORTED;
+    if (M == 0) return W4_OK;
+    if (!q || !k_draft || !v_draft || !masks || !out || (L > 0 && (!k_cache || !v_cache))) return W4_ERR_INVALID;
+    if (!aligned(q, 16) || !aligned(k_draft, 16) || !aligned(v_draft, 16) || !aligned(masks, 8) || !aligned(out, 16) ||
+        (L > 0 && (!aligned(k_cache, 16) || !aligned(v_cache, 16))))
+        return W4_ERR_INVALID;
+    const size_t ob = (size_t)M * num_heads * head_dim * 4;
+    const size_t qb = (size_t)M * num_heads * head_dim * 2, cb = (size_t)L * num_kv_heads * head_dim * 2,
+                 db = (size_t)M * num_kv_heads * head_dim * 2;
+    if (overlap(out, ob, q, qb) || overlap(out, ob, k_cache, cb) || overlap(out, ob, v_cache, cb) ||
+        overlap(out, ob, k_draft, db) || overlap(out, ob, v_draft, db) || overlap(out, ob, masks, (size_t)M * 8))
+        return W4_ERR_INVALID;
+    if (w4::tree_attn_plan(M, L, num_heads, num_kv_heads, nullptr, nullptr) != 0) return W4_ERR_UNSUPPORTED;
+    float* ws = nullptr;
+    int rc = device_state(nullptr, nullptr, &ws);
+    if (rc != W4_OK) return rc;
+    const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)head_dim);
+    return hip_status("tree attention launch",
+                      w4::launch_tree_attn(q, k_cache, v_cache, k_draft, v_draft, masks, M, L, num_heads,
+                                           num_kv_heads, sc, out, ws, (hipStream_t)stream));
 }

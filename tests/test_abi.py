@@ -9,7 +9,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("w4a16.h", "w4a16_bench.h", "w4_accept.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("w4a16.h", "w4a16_bench.h", "w4_accept.h", "w4_tree_attn.h")]
 
 w4 = pytest.importorskip("speculative_decoding_verification_w4a16_amd")
 
@@ -209,3 +209,21 @@ def test_accept_argument_errors():
         with pytest.raises(w4.W4Error) as e:
             w4.w4_accept_sample(L, a["dl"], T, a["u"], 4, V, a["out"], stream=0)
         assert e.value.status == code, args
+
+
+def test_tree_attention_argument_errors():
+    a = dict(q=0x100000, kc=0x200000, vc=0x300000, kd=0x400000, vd=0x500000, m=0x600000, M=5, L=64, H=64, Hkv=8,
+             D=128, scale=0.0, out=0x700000)
+
+    def call(**kw):
+        b = dict(a)
+        b.update(kw)
+        return w4.w4_tree_attention(b["q"], b["kc"], b["vc"], b["kd"], b["vd"], b["m"], b["M"], b["L"], b["H"],
+                                    b["Hkv"], b["D"], b["scale"], b["out"], stream=0)
+    for kw, code in [(dict(M=-1), 1), (dict(L=-1), 1), (dict(D=64), 2), (dict(M=65), 2), (dict(H=60), 2),
+                     (dict(q=0), 1), (dict(kc=0), 1), (dict(m=0x600004), 1), (dict(out=0x100000), 1),
+                     (dict(q=0x100008), 1), (dict(scale=-1.0), 1), (dict(scale=float("nan")), 1), (dict(Hkv=0), 1)]:
+        with pytest.raises(w4.W4Error) as e:
+            call(**kw)
+        assert e.value.status == code, kw
+    assert call(M=0) is None  # nothing to do: no launch, no error

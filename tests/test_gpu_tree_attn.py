@@ -1,0 +1,94 @@
+"""GPU parity of tree-draft verify attention (w4_tree_attention) against the
+oracle (oracle/tree_attn_ref.py).
+
+Inputs are bf16 (the oracle reads the same bf16 values in float64); the
+kernel multiplies on bf16 MFMA with fp32 accumulation and rounds the softmax
+probabilities to bf16 for the value product, so each output must lie within
+1e-2 * sum_k p_k |v_k| of the oracle (a bf16 probability is off by at most
+2^-9 of itself).  Cases: chains (sequence drafts), stars, random trees and
+the page's A -> B, C, D tree; prefixes that end inside a 64-key chunk and on
+its edge; the Llama-3-70B grouping (64 query heads over 8 key/value heads)
+and other groupings; a token that sees nothing; repeatability.
+"""
+import numpy as np
+import pytest
+
+from oracle import ancestor_masks, attention_weight_mass, tree_attention
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+w4 = pytest.importorskip("speculative_decoding_verification_w4a16_amd")
+DEV = "cuda:0"
+
+
+def _bf16(rng, shape, sigma=1.0):
+    """Random bf16 values: (bit patterns, the same values as float64)."""
+    u = rng.normal(0.0, sigma, shape).astype(np.float32).view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return bits, (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _case(seed, M, L, Hq, Hkv, parents, sigma_q=1.0):
+    rng = np.random.default_rng(seed)
+    D = 128
+    qb, q = _bf16(rng, (M, Hq, D), sigma_q)
+    kcb, kc = _bf16(rng, (L, Hkv, D))
+    vcb, vc = _bf16(rng, (L, Hkv, D))
+    kdb, kd = _bf16(rng, (M, Hkv, D))
+    vdb, vd = _bf16(rng, (M, Hkv, D))
+    masks = ancestor_masks(parents) if parents is not None else np.zeros(M, np.uint64)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).to(DEV)
+    out = w4.tree_attention(dev(qb), dev(kcb), dev(vcb), dev(kdb), dev(vdb),
+                            torch.from_numpy(masks.view(np.int64)).to(DEV))
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), (q, kc, vc, kd, vd, masks)
+
+
+def _check(got, args, where):
+    ref = tree_attention(*args)
+    mass = attention_weight_mass(*args)
+    err = np.abs(got - ref)
+    bound = 1e-2 * mass + 1e-6
+    assert np.all(err <= bound), (where, float(np.max(err / bound)))
+    return float(np.max(err / bound))
+
+
+def _random_tree(rng, M):
+    return [-1] + [int(rng.integers(-1, i)) for i in range(1, M)]
+
+
+@pytest.mark.parametrize("M,L,kind", [(1, 0, "chain"), (1, 200, "chain"), (5, 100, "chain"), (5, 128, "star"),
+                                      (4, 61, "page"), (16, 1000, "tree"), (64, 64, "chain"), (64, 1000, "tree"),
+                                      (64, 4096, "tree")])
+def test_tree_attention_matches_the_oracle(M, L, kind):
+    rng = np.random.default_rng(M * 1000 + L)
+    parents = {"chain": list(range(-1, M - 1)), "star": [-1] * M, "page": [-1, 0, 0, 0],
+               "tree": _random_tree(rng, M)}[kind]
+    got, args = _case(M + L, M, L, 64, 8, parents)
+    _check(got, args, (M, L, kind))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 16), (32, 4), (8, 1)])
+def test_other_head_groupings(Hq, Hkv):
+    rng = np.random.default_rng(Hq + Hkv)
+    got, args = _case(7, 9, 150, Hq, Hkv, _random_tree(rng, 9))
+    _check(got, args, (Hq, Hkv))
+
+
+def test_peaked_scores_and_unseen_tokens():
+    # large queries make the softmax nearly one-hot: the online max must carry it
+    got, args = _case(3, 12, 300, 64, 8, list(range(-1, 11)), sigma_q=8.0)
+    _check(got, args, "peaked")
+    # no prefix and empty masks: nothing to attend to, the output is 0
+    got, args = _case(4, 6, 0, 64, 8, None)
+    assert np.array_equal(got, np.zeros_like(got))
+
+
+def test_repeatable():
+    a, _ = _case(5, 33, 700, 64, 8, list(range(-1, 32)))
+    b, _ = _case(5, 33, 700, 64, 8, list(range(-1, 32)))
+    assert np.array_equal(a, b)
