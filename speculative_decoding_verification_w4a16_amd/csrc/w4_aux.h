@@ -24,9 +24,10 @@ hipError_t launch_accept(const float* lt, const float* ld, const int32_t* draft,
 // Tree-draft verify attention (w4_tree_attn.hip).
 constexpr int kTreeHeadDim = 128;
 constexpr int kTreeMaxM = 64;
-constexpr size_t kTreeWorkspaceBytes = size_t(48) << 20;
-// Key splits for (M, L, Hq, Hkv) and the workspace they need; non-zero when
-// even one split does not fit the workspace.
+constexpr size_t kTreeWorkspaceBytes = size_t(48) << 20;  // the key splits' partial results
+constexpr int kTreeMaxSplits = 64;
+// Key splits for (M, L, Hq, Hkv) and the workspace bytes they need; returns 0
+// (one split always fits: it writes the output directly).
 int tree_attn_plan(int M, int L, int Hq, int Hkv, int* nsplit, size_t* ws_bytes);
 hipError_t launch_tree_attn(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const uint16_t* kd,
                             const uint16_t* vd, const uint64_t* masks, int M, int L, int Hq, int Hkv, float scale,

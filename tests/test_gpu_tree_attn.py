@@ -8,7 +8,9 @@ probabilities to bf16 for the value product, so each output must lie within
 2^-9 of itself).  Cases: chains (sequence drafts), stars, random trees and
 the page's A -> B, C, D tree; prefixes that end inside a 64-key chunk and on
 its edge; the Llama-3-70B grouping (64 query heads over 8 key/value heads)
-and other groupings; a token that sees nothing; repeatability.
+and other groupings; a token that sees nothing; one key split and the most
+splits (M = 1 over 4096 and 12288 keys); repeatability, also with calls of
+other shapes in between (the split merge uses per-tile arrival counters).
 """
 import numpy as np
 import pytest
@@ -63,7 +65,8 @@ def _random_tree(rng, M):
 
 @pytest.mark.parametrize("M,L,kind", [(1, 0, "chain"), (1, 200, "chain"), (5, 100, "chain"), (5, 128, "star"),
                                       (4, 61, "page"), (16, 1000, "tree"), (64, 64, "chain"), (64, 1000, "tree"),
-                                      (64, 4096, "tree")])
+                                      (64, 4096, "tree"), (1, 4096, "chain"), (8, 2047, "tree"),
+                                      (2, 64 * 64 * 3, "chain"), (1, 1500, "chain")])
 def test_tree_attention_matches_the_oracle(M, L, kind):
     rng = np.random.default_rng(M * 1000 + L)
     parents = {"chain": list(range(-1, M - 1)), "star": [-1] * M, "page": [-1, 0, 0, 0],
@@ -92,3 +95,15 @@ def test_repeatable():
     a, _ = _case(5, 33, 700, 64, 8, list(range(-1, 32)))
     b, _ = _case(5, 33, 700, 64, 8, list(range(-1, 32)))
     assert np.array_equal(a, b)
+
+
+def test_repeatable_across_shapes():
+    # the key splits are merged by whichever workgroup arrives last at a
+    # per-tile counter; calls of other shapes in between must leave every
+    # counter ready for the next call
+    a, _ = _case(11, 1, 4096, 64, 8, [-1])
+    _case(12, 64, 1000, 64, 8, list(range(-1, 63)))
+    _case(13, 3, 30, 64, 8, [-1, 0, 1])
+    b, args = _case(11, 1, 4096, 64, 8, [-1])
+    assert np.array_equal(a, b)
+    _check(b, args, "after other shapes")
