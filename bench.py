@@ -71,6 +71,8 @@ def parse():
     p.add_argument("--floor", action="store_true",
                    help="instead of the sweep: plain streaming reads of each linear's packed bytes (one launch "
                         "each), an empty launch, and their sum over a pass")
+    p.add_argument("--tree", action="store_true",
+                   help="instead of the sweep: only the tree-draft verify attention measurement (one JSON line)")
     p.add_argument("--m", default="1,2,4,5,8,16,32,48,64", help="M grid for --shapes")
     p.add_argument("--names", default="q,k,v,o,gate,up,down,lm_head", help="linears for --shapes")
     p.add_argument("--splits", type=int, default=0, help="force the K split count in --shapes (0 = planner)")
@@ -762,6 +764,10 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.tree:
+        w4.w4_init()
+        print(json.dumps(tree_attention_bench(torch, w4, args)))
+        return
     t_start = time.time()
     w4.w4_init()
     rng = np.random.default_rng(0)
