@@ -13,7 +13,9 @@
 //
 // Layout of the work.  The rows of key/value head g are the M x G (token,
 // query head) pairs that read it, row = token * G + head-in-group; a
-// workgroup of 4 waves takes 64 rows (16 per wave) over a contiguous run of
+// workgroup of W waves takes 16W rows (16 per wave; W = 4 when the rows of a
+// head fit one wave, else 8, which halves the chunk copies per row) over a
+// contiguous run of
 // 64-key chunks of the key sequence (the L prefix positions, then the M draft
 // tokens).  The workgroup copies each chunk's keys and values into LDS once
 // (registers -> LDS, the next chunk's loads in flight meanwhile; two
@@ -55,7 +57,6 @@ namespace {
 
 constexpr int kHd = kTreeHeadDim;              // 128
 constexpr int kChunk = 64;                     // keys per chunk
-constexpr int kRowsWg = 64;                    // query rows per workgroup (16 per wave)
 constexpr int kKPitch = kHd * 2 + 16;          // bytes per key row of the K copy
 constexpr int kKBytes = kChunk * kKPitch;      // one chunk's K copy
 constexpr int kVtPitch = kChunk * 2 + 8;       // bytes per head-dim column of the V copy
@@ -90,7 +91,9 @@ __device__ __forceinline__ u32x4 kv_load(const uint16_t* cache, const uint16_t* 
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__global__ __launch_bounds__(256) void tree_attn_kernel(TreeArgs a) {
+template <int W>
+__global__ __launch_bounds__(64 * W) void tree_attn_kernel(TreeArgs a) {
+    constexpr int kRowsWg = 16 * W;  // query rows per workgroup
     __shared__ __align__(16) char smem[2 * kBufBytes];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int o = lane >> 4, t = lane & 15;
@@ -115,10 +118,13 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(TreeArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     // Chunk loads: thread (lt, lq) = (tid / 16, tid % 16) fetches head-dim octet
-    // lq of keys lt + 16r (r < 4) and of the value key pairs lt and lt + 16.
+    // lq of keys lt + 4W r (r < 16/W) and of the value key pairs lt + 4W i
+    // (i < 8/W).
+    static_assert(W == 4 || W == 8, "4 or 8 waves per workgroup");
+    constexpr int KI = 16 / W, VI = 8 / W, TS = 4 * W;  // TS: thread rows (lt) per workgroup
     const int lt = tid >> 4, lq = tid & 15;
     struct ChunkRegs {
-        u32x4 k[4], v[4];  // v[2i], v[2i+1]: keys 2(lt + 16i) and 2(lt + 16i) + 1
+        u32x4 k[KI], v[2 * VI];  // v[2i], v[2i+1]: keys 2(lt + TS i) and 2(lt + TS i) + 1
     };
     // a chunk inside the prefix: one wave-uniform base and fixed lane offsets
     const uint32_t pos_bytes = (uint32_t)a.Hkv * kHd * 2;  // between consecutive positions
@@ -130,16 +136,16 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(TreeArgs a) {
             const char* kb = (const char*)a.kc + (size_t)key0 * pos_bytes;
             const char* vb = (const char*)a.vc + (size_t)key0 * pos_bytes;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) cr.k[r] = *(const u32x4*)(kb + (lane_k + 16 * r * pos_bytes));
+            for (int r = 0; r < KI; ++r) cr.k[r] = *(const u32x4*)(kb + (lane_k + TS * r * pos_bytes));
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                cr.v[r] = *(const u32x4*)(vb + (lane_v + (32 * (r >> 1) + (r & 1)) * pos_bytes));
+            for (int r = 0; r < 2 * VI; ++r)
+                cr.v[r] = *(const u32x4*)(vb + (lane_v + (2 * TS * (r >> 1) + (r & 1)) * pos_bytes));
         } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) cr.k[r] = kv_load(a.kc, a.kd, a, min(key0 + lt + 16 * r, a.T - 1), g, 8 * lq);
+            for (int r = 0; r < KI; ++r) cr.k[r] = kv_load(a.kc, a.kd, a, min(key0 + lt + TS * r, a.T - 1), g, 8 * lq);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                cr.v[r] = kv_load(a.vc, a.vd, a, min(key0 + 2 * (lt + 16 * (r >> 1)) + (r & 1), a.T - 1), g, 8 * lq);
+            for (int r = 0; r < 2 * VI; ++r)
+                cr.v[r] = kv_load(a.vc, a.vd, a, min(key0 + 2 * (lt + TS * (r >> 1)) + (r & 1), a.T - 1), g, 8 * lq);
         }
     };
     // ... into LDS buffer b.  Keys past the end keep a valid (clamped) K row,
@@ -149,15 +155,15 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(TreeArgs a) {
         char* kbuf = smem + b * kBufBytes;
         char* vbuf = kbuf + kKBytes;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) *(u32x4*)(kbuf + (lt + 16 * r) * kKPitch + 16 * lq) = cr.k[r];
+        for (int r = 0; r < KI; ++r) *(u32x4*)(kbuf + (lt + TS * r) * kKPitch + 16 * lq) = cr.k[r];
         if (c * kChunk + kChunk > a.T) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (c * kChunk + 2 * (lt + 16 * (r >> 1)) + (r & 1) >= a.T) cr.v[r] = u32x4{0, 0, 0, 0};
+            for (int r = 0; r < 2 * VI; ++r)
+                if (c * kChunk + 2 * (lt + TS * (r >> 1)) + (r & 1) >= a.T) cr.v[r] = u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int p = (lt + 16 * i) ^ vsw;
+        for (int i = 0; i < VI; ++i) {
+            const int p = (lt + TS * i) ^ vsw;
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) {
                 const uint32_t lo = __builtin_amdgcn_perm(cr.v[2 * i + 1][w2], cr.v[2 * i][w2], 0x05040100u);
@@ -385,18 +391,25 @@ hipError_t launch(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t st
 
 size_t partial_bytes(int nsplit, int Hkv, int R) { return (size_t)nsplit * Hkv * R * (kHd + 2) * sizeof(float); }
 
+// Waves per workgroup for R rows per head: 4 (64 rows) when the rows fit one
+// wave, else 8 (128 rows).
+int tree_waves(int R) { return R > 16 ? 8 : 4; }
+
 }  // namespace
 
 int tree_attn_plan(int M, int L, int Hq, int Hkv, int* nsplit_out, size_t* ws_bytes) {
     const int G = Hq / Hkv, R = M * G, T = L + M;
     const int nchunks = (T + kChunk - 1) / kChunk;
-    const int nrt = (R + kRowsWg - 1) / kRowsWg;
+    const int W = tree_waves(R), rows_wg = 16 * W;
+    const int nrt = (R + rows_wg - 1) / rows_wg;
     const int tiles = nrt * Hkv;
-    // two workgroups fit a CU (LDS): about 512 at once.  Chunks per split:
-    // at least two (a workgroup overlaps a chunk's loads with the previous
-    // chunk's work), else the fewest that keep to one such round; then at
-    // most kTreeMaxSplits splits and what the workspace holds
-    const int cps = std::max(2, (int)(((long long)nchunks * tiles + 511) / 512));
+    // workgroups at once: two of four waves per CU (LDS), one of eight
+    // (registers).  Chunks per split: at least two (a workgroup overlaps a
+    // chunk's loads with the previous chunk's work), else the fewest that
+    // keep to one such round; then at most kTreeMaxSplits splits and what
+    // the workspace holds
+    const long long slots = W == 4 ? 512 : 256;
+    const int cps = std::max(2, (int)(((long long)nchunks * tiles + slots - 1) / slots));
     int nsplit = std::max(1, std::min(kTreeMaxSplits, (nchunks + cps - 1) / cps));
     while (nsplit > 1 && partial_bytes(nsplit, Hkv, R) > kTreeWorkspaceBytes) --nsplit;
     if (nsplit_out) *nsplit_out = nsplit;
@@ -421,7 +434,8 @@ hipError_t launch_tree_attn(const uint16_t* q, const uint16_t* kc, const uint16_
     a.G = Hq / Hkv;
     a.R = M * a.G;
     a.T = L + M;
-    a.nrt = (a.R + kRowsWg - 1) / kRowsWg;
+    const int W = tree_waves(a.R);
+    a.nrt = (a.R + 16 * W - 1) / (16 * W);
     a.nchunks = (a.T + kChunk - 1) / kChunk;
     if (tree_attn_plan(M, L, Hq, Hkv, &a.nsplit, nullptr) != 0) return hipErrorInvalidValue;
     a.c = scale * kLog2e;
@@ -430,7 +444,8 @@ hipError_t launch_tree_attn(const uint16_t* q, const uint16_t* kc, const uint16_
     a.mpart = a.opart + plane * kHd;
     a.lpart = a.mpart + plane;
     a.out = out;
-    hipError_t e = launch(tree_attn_kernel, dim3(a.nsplit, a.nrt, Hkv), dim3(256), stream, a);
+    hipError_t e = W == 4 ? launch(tree_attn_kernel<4>, dim3(a.nsplit, a.nrt, Hkv), dim3(256), stream, a)
+                          : launch(tree_attn_kernel<8>, dim3(a.nsplit, a.nrt, Hkv), dim3(512), stream, a);
     if (e != hipSuccess || a.nsplit == 1) return e;
     a.cng = 1;
     while (a.cng < 8 && a.cng * 8 < a.nsplit) a.cng *= 2;
