@@ -810,8 +810,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // the fix-up chain (counter round trip, then S*M/32 dependent partial loads
 // by 256 threads) sits after all the streaming, while the second launch
 // spreads the same reads over the chip.  One thread per 4 output columns of a
-// row keeps its S partial vectors in flight together and adds them in split
-// order (deterministic).
+// row keeps its S partial vectors in flight together (KB >= S loads issued
+// before the first add, so the whole sum costs one memory round trip: with
+// batches of 8, S = 11..22 took two or three and the launch ~4.5 us even for
+// a single workgroup) and adds them in split order (deterministic; the same
+// bits for every KB).
+template <int KB>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, float* __restrict__ y,
                                                           uint16_t* __restrict__ yb, int M, int N, int npad,
                                                           int splits) {
@@ -824,13 +828,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         const int n = 4 * (int)(idx - (size_t)m * nq);
         const f32x4* src = (const f32x4*)(ws + (size_t)m * npad + n);
         f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        constexpr int kB = 8;
-        for (int s0 = 0; s0 < splits; s0 += kB) {
-            f32x4 v[kB];
+        for (int s0 = 0; s0 < splits; s0 += KB) {
+            f32x4 v[KB];
 #pragma unroll
-            for (int i = 0; i < kB; ++i) v[i] = src[(size_t)min(s0 + i, splits - 1) * (plane / 4)];
+            for (int i = 0; i < KB; ++i) v[i] = src[(size_t)min(s0 + i, splits - 1) * (plane / 4)];
 #pragma unroll
-            for (int i = 0; i < kB; ++i)
+            for (int i = 0; i < KB; ++i)
                 if (s0 + i < splits) acc += v[i];
         }
         const size_t o = (size_t)m * N + n;
@@ -955,12 +958,14 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
         const int ntiles = ceil_div(NC, kWaves);
         // M > 16: time model calibrated on MI355X sweeps of forced split
         // counts,
-        //   t(S) = max(1, workgroups / 256) * (G/S + 4) * t_group
+        //   t(S) = R(workgroups) * (G/S + 4) * t_group
         //        + [S > 1] * (2 us + S * M * NCpad * 8 bytes / 5 TB/s):
-        // two workgroups fit side by side per CU, which smooths a partly
-        // filled round; every workgroup pays start-up worth ~4 groups;
-        // t_group ~0.375 us per row block of 16; S <= G/2.  The smallest S
-        // of least t wins.
+        // a CU holds two workgroups side by side, and a CU running two takes
+        // ~1.4x as long as one running one (down at M = 64: S = 16, 512
+        // workgroups, 53 us against 57 us for S = 8, 256 workgroups), so
+        // R = 1 up to 256 workgroups, else 1.4 per started round of 512;
+        // every workgroup pays start-up worth ~4 groups; t_group ~0.375 us
+        // per row block of 16; S <= G/2.  The smallest S of least t wins.
         const double t_group = 0.375 * mb;
         const double red_bytes = (double)M * NC * kChunkN * 8;
         const int smax = std::max(1, G / 2);
@@ -968,7 +973,8 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
         double best = 1e30;
         for (int s = 1; s <= smax; ++s) {
             const double wgs = (double)ntiles * s;
-            double t = std::max(1.0, wgs / 256.0) * ((double)G / s + 4.0) * t_group;
+            const double rounds = wgs <= 256.0 ? 1.0 : 1.4 * std::ceil(wgs / 512.0);
+            double t = rounds * ((double)G / s + 4.0) * t_group;
             if (s > 1) t += 2.0 + s * red_bytes / 5e6;
             if (t < best - 1e-9) {
                 best = t;
@@ -1088,8 +1094,14 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
     }
     if (e != hipSuccess || p.splits == 1) return e;
     const size_t total = (size_t)M * (N / 4);
-    return launch(splitk_reduce_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, (const float*)ws.partial,
-                  a.y, a.yb, M, N, a.NC * kChunkN, p.splits);
+    const dim3 rgrid(grid_for(total, 256)), rblock(256);
+    const float* part = ws.partial;
+    const int npad = a.NC * kChunkN;
+    if (p.splits <= 2) return launch(splitk_reduce_kernel<2>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
+    if (p.splits <= 4) return launch(splitk_reduce_kernel<4>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
+    if (p.splits <= 8) return launch(splitk_reduce_kernel<8>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
+    if (p.splits <= 16) return launch(splitk_reduce_kernel<16>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
+    return launch(splitk_reduce_kernel<32>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
 }
 
 hipError_t launch_zero(float* y, size_t n, hipStream_t stream) {
