@@ -151,7 +151,9 @@ int w4a16_linear_tune(const uint16_t* x, const uint32_t* qweight_t, const uint16
 /* The launch plan w4a16_linear_tune would use for (kernel, splits, kwaves)
  * (host outputs, any may be NULL): kernel id, K splits, waves splitting a
  * chunk's K range, workgroups, threads per workgroup, LDS bytes per
- * workgroup.  No HIP call. */
+ * workgroup.  With kwaves 1 each wave streams its own chunk and the
+ * workgroup holds threads/64 of them: four, or for M > 16 four or eight
+ * (the planner's choice, also when splits is forced).  No HIP call. */
 int w4a16_plan(int M, int N, int K, int group, int kernel, int splits, int kwaves, int* kernel_out,
                int* splits_out, int* kwaves_out, int* grid_out, int* block_out, int* lds_out);
 

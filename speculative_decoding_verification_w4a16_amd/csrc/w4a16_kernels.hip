@@ -637,8 +637,10 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory", "m0");
 }
 
-template <int MB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void w4a16_mfma_lds_kernel(LinearArgs a) {
+template <int MB, int WV>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2))) void w4a16_mfma_lds_kernel(LinearArgs a) {
+    static_assert(WV == 4 || WV == 8, "four or eight chunks per workgroup");
+    constexpr int XD = (4 * MB + WV - 1) / WV;  // activation lines (4 rows each) this wave copies per group
     constexpr int R = kLdsRing;
     constexpr int XB = lds_ring_xbuf(MB);  // bytes per activation buffer
     constexpr int XS = R * XB;             // first sum slot
@@ -651,27 +653,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int tile = blockIdx.x - split * a.ntiles;
     const int g0 = split * a.gps;
     const int ng = min(a.G, g0 + a.gps) - g0;
-    const int c = tile * kWaves + wave;
+    const int c = tile * WV + wave;
     const int o = lane >> 4, t = lane & 15;
     const uint32_t mask = a.mask, magic = to_vgpr(a.magic);
     const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2});
 
-    // DMA sources.  Wave w fills lines w + 4ii (ii < MB) of a buffer; line i
-    // holds rows 4i..4i+3 and lane l lands in row 4i + l/16, slot l%16, which
-    // holds k-octet (l%16) ^ (row & 15).  Rows past M repeat row M-1 (their
-    // results are never stored), groups past the split repeat its last group.
-    int xoff[MB];
+    // DMA sources.  A buffer holds 4 MB lines; wave w fills lines w + WV ii
+    // (ii < XD; a line past the last is replaced by the wave's previous one,
+    // a second copy of the same bytes to the same place).  Line i holds rows
+    // 4i..4i+3 and lane l lands in row 4i + l/16, slot l%16, which holds
+    // k-octet (l%16) ^ (row & 15).  Rows past M repeat row M-1 (their results
+    // are never stored), groups past the split repeat its last group.
+    int xoff[XD], xline[XD];
 #pragma unroll
-    for (int ii = 0; ii < MB; ++ii) {
-        const int r = 4 * (wave + 4 * ii) + o;
+    for (int ii = 0; ii < XD; ++ii) {
+        int line = wave + WV * ii;
+        if (line >= 4 * MB) line -= WV;
+        xline[ii] = line;
+        const int r = 4 * line + o;
         xoff[ii] = min(r, a.M - 1) * a.K + 8 * (t ^ (r & 15));
     }
     const uint16_t* xg = a.x + (size_t)g0 * kGroup;
     auto issue_x = [&](int buf, int gl) {
         const uint16_t* src = xg + (size_t)min(gl, ng - 1) * kGroup;
 #pragma unroll
-        for (int ii = 0; ii < MB; ++ii) lds_dma16(src + xoff[ii], smem + buf * XB + 1024 * (wave + 4 * ii));
+        for (int ii = 0; ii < XD; ++ii) lds_dma16(src + xoff[ii], smem + buf * XB + 1024 * xline[ii]);
     };
 
     // A operand of (row block mb, k-block kk) in buffer b: row 16mb + t, octet
@@ -706,7 +713,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     // groups 0 and 1 landed: after them only the ring slot of group 1, then
     // the DMA and ring slot of group 2 may still be in flight
-    wait_vmcnt<2 * kRingOps + MB>();
+    wait_vmcnt<2 * kRingOps + XD>();
     lds_barrier();
     compute_xs(0);
     lds_barrier();
@@ -912,6 +919,7 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
     const int G = K / kGroup;
     const int mb = ceil_div(M, 16);
     const int variant = kernel == kGemv ? kVarGemv : (mb == 1 ? kVarDirect : kVarLds);
+    int lds_wv = kWaves;  // chunks per workgroup of the M > 16 kernel
     if (variant == kVarLds && kwaves > 1) return -1;
     int kw = 1;
     int S = 1;
@@ -952,35 +960,44 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
         }
         if (splits > 0) S = splits;
         if (kwaves > 0) kw = kwaves;
-    } else if (splits > 0) {
-        S = splits;
     } else {
-        const int ntiles = ceil_div(NC, kWaves);
         // M > 16: time model calibrated on MI355X sweeps of forced split
-        // counts,
-        //   t(S) = R(workgroups) * (G/S + 4) * t_group
-        //        + [S > 1] * (2 us + S * M * NCpad * 8 bytes / 5 TB/s):
-        // a CU holds two workgroups side by side, and a CU running two takes
-        // ~1.4x as long as one running one (down at M = 64: S = 16, 512
-        // workgroups, 53 us against 57 us for S = 8, 256 workgroups), so
-        // R = 1 up to 256 workgroups, else 1.4 per started round of 512;
-        // every workgroup pays start-up worth ~4 groups; t_group ~0.375 us
-        // per row block of 16; S <= G/2.  The smallest S of least t wins.
+        // counts and workgroup widths (WV = 4 or 8 chunks, one wave each),
+        //   t(S, WV) = R(workgroups) * (G/S + 4) * t_group
+        //            + [S > 1] * (2 us + S * M * NCpad * 8 bytes / 5 TB/s):
+        // a CU holds two 4-wave workgroups side by side, and a CU running two
+        // takes ~1.4x as long as one running one (down at M = 64: S = 16,
+        // 512 workgroups, 53 us against 57 us for S = 8, 256 workgroups), so
+        // for WV = 4, R = 1 up to 256 workgroups, else 1.4 per started round
+        // of 512; an 8-wave workgroup fills a CU alone (two waves per SIMD)
+        // and shares one activation copy between twice the chunks, R = 1.3
+        // per round of 256 (gate at M = 64: 53.6 us against 58.6 us; q and k,
+        // with few chunks, stay faster at WV = 4); every workgroup pays
+        // start-up worth ~4 groups; t_group ~0.375 us per row block of 16;
+        // S <= G/2.  The least t wins, ties to the smaller S and WV; a forced
+        // split count keeps S and still chooses WV.
         const double t_group = 0.375 * mb;
         const double red_bytes = (double)M * NC * kChunkN * 8;
         const int smax = std::max(1, G / 2);
-        S = 1;
         double best = 1e30;
-        for (int s = 1; s <= smax; ++s) {
-            const double wgs = (double)ntiles * s;
-            const double rounds = wgs <= 256.0 ? 1.0 : 1.4 * std::ceil(wgs / 512.0);
-            double t = rounds * ((double)G / s + 4.0) * t_group;
-            if (s > 1) t += 2.0 + s * red_bytes / 5e6;
-            if (t < best - 1e-9) {
-                best = t;
-                S = s;
+        int bs = 1;
+        for (int wv = kWaves; wv <= kMaxWaves; wv *= 2) {
+            const int ntiles = ceil_div(NC, wv);
+            for (int s = 1; s <= smax || (splits > 0 && s <= splits); ++s) {
+                if (splits > 0 && s != splits) continue;
+                const double wgs = (double)ntiles * s;
+                const double rounds = wv == kWaves ? (wgs <= 256.0 ? 1.0 : 1.4 * std::ceil(wgs / 512.0))
+                                                   : 1.3 * std::ceil(wgs / 256.0);
+                double t = rounds * ((double)G / s + 4.0) * t_group;
+                if (s > 1) t += 2.0 + s * red_bytes / 5e6;
+                if (t < best - 1e-9) {
+                    best = t;
+                    bs = s;
+                    lds_wv = wv;
+                }
             }
         }
+        S = bs;
     }
     S = std::max(1, std::min(S, G));
     int gps = ceil_div(G, S);
@@ -993,7 +1010,8 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
     // every wave of a K-splitting workgroup needs a group of its own (the
     // last split holds the fewest groups)
     while (kw > 1 && G - (S - 1) * gps < kw) kw >>= 1;
-    const int ntiles = kw == 1 ? ceil_div(NC, kWaves) : NC;
+    const int wg_chunks = variant == kVarLds ? lds_wv : kWaves;
+    const int ntiles = kw == 1 ? ceil_div(NC, wg_chunks) : NC;
     p->kernel = kernel;
     p->variant = variant;
     p->mb = mb;
@@ -1002,7 +1020,7 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
     p->gps = gps;
     p->ntiles = ntiles;
     p->grid = ntiles * S;
-    p->block = 64 * (kw == 1 ? kWaves : kw);
+    p->block = 64 * (kw == 1 ? wg_chunks : kw);
     p->lds = 0;
     if (variant == kVarLds) {
         p->lds = lds_ring_bytes(mb);
@@ -1085,12 +1103,20 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
         case kVarGemv: e = launch(w4a16_gemv_kernel<kRingGemv>, grid, block, 0, stream, a); break;
         case kVarDirect: e = launch(w4a16_mfma_direct_kernel<1, kRingDirect1>, grid, block, 0, stream, a); break;
         default:
-            if (p.mb == 2)
-                e = launch(w4a16_mfma_lds_kernel<2>, grid, block, p.lds, stream, a);
-            else if (p.mb == 3)
-                e = launch(w4a16_mfma_lds_kernel<3>, grid, block, p.lds, stream, a);
-            else
-                e = launch(w4a16_mfma_lds_kernel<4>, grid, block, p.lds, stream, a);
+            if (p.block == 64 * kMaxWaves) {
+                if (p.mb == 2)
+                    e = launch(w4a16_mfma_lds_kernel<2, kMaxWaves>, grid, block, p.lds, stream, a);
+                else if (p.mb == 3)
+                    e = launch(w4a16_mfma_lds_kernel<3, kMaxWaves>, grid, block, p.lds, stream, a);
+                else
+                    e = launch(w4a16_mfma_lds_kernel<4, kMaxWaves>, grid, block, p.lds, stream, a);
+            } else if (p.mb == 2) {
+                e = launch(w4a16_mfma_lds_kernel<2, kWaves>, grid, block, p.lds, stream, a);
+            } else if (p.mb == 3) {
+                e = launch(w4a16_mfma_lds_kernel<3, kWaves>, grid, block, p.lds, stream, a);
+            } else {
+                e = launch(w4a16_mfma_lds_kernel<4, kWaves>, grid, block, p.lds, stream, a);
+            }
     }
     if (e != hipSuccess || p.splits == 1) return e;
     const size_t total = (size_t)M * (N / 4);

@@ -142,8 +142,10 @@ def test_plans_fit_the_hardware(M, N, K):
     kw = p["kwaves"]
     assert kw in (1, 2, 4, 8) and (M <= 16 or kw == 1)
     chunks = -(-N // 64)
-    if kw == 1:  # four 64-column chunks per workgroup, one per wave
-        assert p["block"] == 256 and p["grid"] == -(-chunks // 4) * p["splits"]
+    if kw == 1:  # four (or, for M > 16, eight) 64-column chunks per workgroup, one per wave
+        wv = p["block"] // 64
+        assert wv == 4 or (M > 16 and wv == 8)
+        assert p["grid"] == -(-chunks // wv) * p["splits"]
     else:  # one chunk per workgroup, its kw waves splitting K
         assert p["block"] == 64 * kw and p["grid"] == chunks * p["splits"]
         gps = -(-(K // 128) // p["splits"])

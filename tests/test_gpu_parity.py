@@ -118,6 +118,23 @@ def test_ragged_shapes_every_m_block_boundary(N, K):
     _check(run_linear(x[:1], pk, w4.W4_KERNEL_MFMA, 0), Y[:1], A[:1], (N, K, 1, "mfma"))
 
 
+@pytest.mark.parametrize("M", [1, 5, 40])
+def test_every_split_reduction_width(M):
+    # The split-K reduction launch loads up to 2, 4, 8, 16 or 32 partials in
+    # one batch and loops over batches of 32 beyond that: force split counts
+    # in every width and past it (K = 64 groups, so each count below splits
+    # the groups exactly) for each streaming kernel.
+    N, K = 200, 8192
+    lin = synth.gen_linear(81, N, K)
+    x = synth.gen_x(M, K, seed_base=900)
+    Y, A = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+    pk = packed(lin, N, K)
+    for splits in (2, 3, 4, 5, 8, 13, 16, 22, 32, 64):
+        plan = w4.w4a16_plan(M, N, K, splits=splits)
+        assert plan["splits"] == splits, plan
+        _check(run_linear(x, pk, 0, splits), Y, A, (M, splits))
+
+
 @pytest.mark.parametrize("M,kernel", [(1, 1), (1, 2), (16, 0), (40, 0)])
 def test_one_hot_rows_bit_exact(M, kernel):
     # GP2: x = e_k at nibble positions, group edges and the first/last k
@@ -198,6 +215,28 @@ def test_verify_pass_equals_separate_calls():
 # ---------------------------------------------------------------------------
 # Llama-3-70B-shaped linears (plain decode, sequence and tree drafts)
 # ---------------------------------------------------------------------------
+
+def test_eight_chunk_workgroups_ragged():
+    # Wide linears at M > 16 run eight chunks per workgroup.  N here leaves
+    # the last workgroup half empty (436 chunks, 4 past a multiple of 8) and
+    # its last chunk partly padded; M = 17, 40 and 64 cover one, three (the
+    # activation copy duplicates a line) and four row blocks; sampled columns
+    # include the first, a middle and the last chunk; the planner's split
+    # count and a forced odd one both run eight-chunk workgroups.
+    N, K = 27896, 8192
+    lin = synth.gen_linear(83, N, K)
+    pk = packed(lin, N, K)
+    x = synth.gen_x(64, K, seed_base=950)
+    slices = [(0, 64), (13824, 13888), (N - 120, N)]
+    refs = [linear64_columns(x, lin["qweight"], lin["scales"], lin["zeros"], 128, a, b) for a, b in slices]
+    for M in (17, 40, 64):
+        for splits in (0, 3):
+            plan = w4.w4a16_plan(M, N, K, splits=splits)
+            assert plan["block"] == 512, plan
+            y = run_linear(x[:M], pk, 0, splits)
+            for (a, b), (Y, A) in zip(slices, refs):
+                _check(y[:, a:b], Y[:M], A[:M], (M, splits, a))
+
 
 VERIFY_M = [1, 2, 4, 5, 8, 16, 32, 48, 64]
 
