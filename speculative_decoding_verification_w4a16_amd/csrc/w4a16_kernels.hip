@@ -974,11 +974,14 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
         // per round of 256 (gate at M = 64: 53.6 us against 58.6 us; q and k,
         // with few chunks, stay faster at WV = 4); every workgroup pays
         // start-up worth ~4 groups; t_group ~0.375 us per row block of 16;
-        // S <= G/2.  The least t wins, ties to the smaller S and WV; a forced
-        // split count keeps S and still chooses WV.
+        // S <= G/4: at least four groups per workgroup, below which start-up
+        // and the partial traffic win over the model (k at M = 64: S = 16
+        // 15.8 us, S = 22 16.7 us; at M = 32 12.2 against 13.7 us).  The least
+        // t wins, ties to the smaller S and WV; a forced split count keeps S
+        // and still chooses WV.
         const double t_group = 0.375 * mb;
         const double red_bytes = (double)M * NC * kChunkN * 8;
-        const int smax = std::max(1, G / 2);
+        const int smax = std::max(1, G / 4);
         double best = 1e30;
         int bs = 1;
         for (int wv = kWaves; wv <= kMaxWaves; wv *= 2) {
