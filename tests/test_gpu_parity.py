@@ -238,6 +238,24 @@ def test_eight_chunk_workgroups_ragged():
                 _check(y[:, a:b], Y[:M], A[:M], (M, splits, a))
 
 
+def test_lm_head_full_size_sampled_columns():
+    # The widest linear of the sweep at full size (N = 128256 = 2004 chunks, so
+    # the last eight-chunk workgroup is half empty), its seed as in the sweep,
+    # through every kernel path the planner picks for M = 1 .. 64; columns
+    # sampled at the start, the middle and the end.
+    N, K = synth.LM_HEAD[1], synth.LM_HEAD[2]
+    lin = synth.gen_linear(20000, N, K)
+    pk = packed(lin, N, K)
+    x = synth.gen_x(64, K)
+    slices = [(0, 64), (64128, 64192), (N - 64, N)]
+    refs = [linear64_columns(x, lin["qweight"], lin["scales"], lin["zeros"], 128, a, b) for a, b in slices]
+    del lin
+    for M in (1, 5, 16, 17, 40, 64):
+        y = run_linear(x[:M], pk)
+        for (a, b), (Y, A) in zip(slices, refs):
+            _check(y[:, a:b], Y[:M], A[:M], ("lm_head", M, a))
+
+
 VERIFY_M = [1, 2, 4, 5, 8, 16, 32, 48, 64]
 
 
