@@ -2,7 +2,7 @@
  * w4a16_bench.h -- measurement kernels shipped with the W4A16 library.
  *
  * Not part of the method: these give the achievable HBM read bandwidth of
- * the device (the ceiling the verify linear is judged against) and a plain
+ * the device (the ceiling the verify linear is measured against) and a plain
  * copy of known size whose hardware byte counters calibrate the FETCH_SIZE
  * and WRITE_SIZE readings of the verify kernels.  The pages ask that
  * throughput be profiled before it is trusted (ordoresearch.ai review,
