@@ -47,4 +47,6 @@ if __name__ == "__main__":
     path = build(verbose=True)
     print(path)
     if "--asm" in sys.argv:
-        dump_asm(os.path.join(os.path.dirname(HERE), "_work", "w4a16_kernels.s"))
+        out_dir = os.path.join(os.path.dirname(HERE), "_build")
+        os.makedirs(out_dir, exist_ok=True)
+        dump_asm(os.path.join(out_dir, "w4a16_kernels.s"))
