@@ -229,3 +229,20 @@ def test_tree_attention_argument_errors():
             call(**kw)
         assert e.value.status == code, kw
     assert call(M=0) is None  # nothing to do: no launch, no error
+
+
+def test_size_limits():
+    # the declared limits are accepted (the plan's sizes do not overflow) and
+    # one step past either is rejected before any HIP call
+    big = 1 << 24
+    for M in (1, 5, 17, 64):
+        for N, K in ((8, big), (big, 128)):
+            p = w4.w4a16_plan(M, N, K)
+            assert 1 <= p["splits"] <= K // 128 and p["grid"] >= 1, (M, N, K, p)
+            # the split-K workspace (64 MiB) holds every partial
+            assert p["splits"] == 1 or p["splits"] * M * (-(-N // 64) * 64) * 4 <= 64 << 20
+    for N, K in ((big + 8, 128), (8, big + 128)):
+        with pytest.raises(w4.W4Error):
+            w4.w4a16_plan(1, N, K)
+        rc = w4._c["w4a16_linear"](None, None, None, None, 1, N, K, 128, None, None)
+        assert rc == w4.W4_ERR_UNSUPPORTED

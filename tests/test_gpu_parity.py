@@ -256,6 +256,20 @@ def test_lm_head_full_size_sampled_columns():
             _check(y[:, a:b], Y[:M], A[:M], ("lm_head", M, a))
 
 
+def test_largest_k_one_chunk():
+    # K at the library's limit (2**24, 131072 groups) on one padded chunk: the
+    # planner splits K 194 or 512 ways (the reduction loops over batches of
+    # partials), and row offsets into x reach 16 * 2**24 elements.
+    N, K = 8, 1 << 24
+    lin = synth.gen_linear(85, N, K)
+    pk = packed(lin, N, K)
+    x = synth.gen_x(17, K, seed_base=990)
+    Y, A = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+    del lin
+    for M in (1, 5, 17):
+        _check(run_linear(x[:M], pk), Y[:M], A[:M], ("K=2**24", M))
+
+
 VERIFY_M = [1, 2, 4, 5, 8, 16, 32, 48, 64]
 
 
