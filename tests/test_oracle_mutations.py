@@ -1,14 +1,15 @@
 """Planted mistakes in the oracle, each caught by at least one pin (CPU only).
 
-Each case replaces one step of the oracle (module ``oracle.w4a16_ref``) with a
+Each case replaces one step of an oracle with a
 plausible wrong version -- a dropped zero-point term, a sign flip, nibbles in
 the wrong order or shifted by one, a wrong group index, the scale applied per
 column of the wrong group, a wrong bf16 decode, an absolute-value bound with
-a signed factor -- and runs the pins of ``test_oracle_exact`` and
-``test_oracle_invariants`` against it.  ``linear64`` looks its steps up in the
-module at call time, so the planted step is what every pin that goes through
-``linear64`` exercises.  The unmodified oracle passes the same pins in their
-own modules.
+a signed factor; in the acceptance step the wrong tie-break, draw, count,
+test or residual; in tree attention an ignored mask, a missing scale or a
+wrong head grouping -- and runs the pins against it until one fails.  The
+steps are replaced where the pins look them up (``linear64`` finds its own
+steps in ``oracle.w4a16_ref`` at call time).  The unmodified oracles pass the
+same pins in their own modules.
 """
 import numpy as np
 import pytest
@@ -109,4 +110,134 @@ def test_planted_mistake_fails_a_pin(name, monkeypatch):
             pin()
         except Exception:  # an assertion, or a shape error the mistake causes
             caught.append(pin.__name__)
+            break
+    assert caught, f"no pin caught: {name}"
+
+
+# ---------------------------------------------------------------------------
+# the acceptance step and tree attention oracles
+# ---------------------------------------------------------------------------
+
+import functools  # noqa: E402
+
+import oracle.accept_ref as acc  # noqa: E402
+import test_oracle_accept as accept_pins  # noqa: E402
+import test_oracle_tree_attn as tree_pins  # noqa: E402
+
+_orig_inverse_cdf = acc.inverse_cdf
+
+
+def _argmax_last(row):
+    r = np.asarray(row)
+    return int(len(r) - 1 - np.argmax(r[::-1]))
+
+
+def _inverse_cdf_ge(r, u):
+    c = np.cumsum(np.asarray(r, dtype=np.float64))
+    return min(int(np.searchsorted(c, u * c[-1], side="left")), len(c) - 1)
+
+
+def _greedy_off_by_one(target_logits, draft_tokens):
+    L = np.asarray(target_logits)
+    K = len(draft_tokens)
+    for j in range(K):
+        a = acc.argmax_first(L[j])
+        if int(draft_tokens[j]) != a:
+            return j + 1, a
+    return K, acc.argmax_first(L[K])
+
+
+def _sampled_variant(kind, target_logits, draft_logits, draft_tokens, u):
+    p, q = acc.softmax64(target_logits), acc.softmax64(draft_logits)
+    K = len(draft_tokens)
+    for j in range(K):
+        d = int(draft_tokens[j])
+        alpha = 1.0 if q[j, d] == 0.0 else min(1.0, p[j, d] / q[j, d])
+        keep = u[j] > alpha if kind == "flipped test" else u[j] < alpha
+        if keep:
+            continue
+        residual = p[j] if kind == "target row at rejection" else np.maximum(p[j] - q[j], 0.0)
+        return j, _orig_inverse_cdf(residual, u[K])
+    return K, _orig_inverse_cdf(p[K] if kind != "draft row at the end" else q[K - 1], u[K])
+
+
+def _tree_variant(kind, q, k_cache, v_cache, k_draft, v_draft, masks, scale=None):
+    q = np.asarray(q, dtype=np.float64)
+    kc, vc = np.asarray(k_cache, dtype=np.float64), np.asarray(v_cache, dtype=np.float64)
+    kd, vd = np.asarray(k_draft, dtype=np.float64), np.asarray(v_draft, dtype=np.float64)
+    M, Hq, D = q.shape
+    Hkv = kc.shape[1] if kc.shape[0] else kd.shape[1]
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 if kind == "no 1/sqrt(d) scale" else 1.0 / np.sqrt(D)
+    out = np.zeros((M, Hq, D))
+    for i in range(M):
+        if kind == "mask ignored":
+            vis = list(range(M))
+        elif kind == "own token not seen":
+            vis = [j for j in range(M) if j != i and (int(masks[i]) >> j) & 1]
+        else:
+            vis = [j for j in range(M) if (int(masks[i]) >> j) & 1]
+        for h in range(Hq):
+            g = h % Hkv if kind == "head h reads h % Hkv" else h // group
+            keys = np.concatenate([kc[:, g, :], kd[vis, g, :]], axis=0)
+            vals = np.concatenate([vc[:, g, :], vd[vis, g, :]], axis=0)
+            if keys.shape[0] == 0:
+                continue
+            s = keys @ q[i, h] * scale
+            p = np.exp(s - s.max())
+            out[i, h] = (p / p.sum()) @ vals
+    return out
+
+
+# (module the pins look the name up in, name, mutant)
+MUTANTS_F = {
+    "greedy: last index of equal maxima": [(acc, "argmax_first", _argmax_last),
+                                           (accept_pins, "argmax_first", _argmax_last)],
+    "draw: cumulative weight >= u total": [(acc, "inverse_cdf", _inverse_cdf_ge),
+                                           (accept_pins, "inverse_cdf", _inverse_cdf_ge)],
+    "greedy: one token too many accepted": [(accept_pins, "accept_greedy", _greedy_off_by_one)],
+    "sampled: acceptance test flipped": [(accept_pins, "accept_sampled",
+                                          functools.partial(_sampled_variant, "flipped test"))],
+    "sampled: target row, not the residual": [(accept_pins, "accept_sampled",
+                                               functools.partial(_sampled_variant, "target row at rejection"))],
+    "sampled: last draft row at the end": [(accept_pins, "accept_sampled",
+                                            functools.partial(_sampled_variant, "draft row at the end"))],
+    "tree: mask ignored": [(tree_pins, "tree_attention", functools.partial(_tree_variant, "mask ignored"))],
+    "tree: own token not seen": [(tree_pins, "tree_attention",
+                                  functools.partial(_tree_variant, "own token not seen"))],
+    "tree: no 1/sqrt(d) scale": [(tree_pins, "tree_attention",
+                                  functools.partial(_tree_variant, "no 1/sqrt(d) scale"))],
+    "tree: head h reads h % Hkv": [(tree_pins, "tree_attention",
+                                    functools.partial(_tree_variant, "head h reads h % Hkv"))],
+}
+
+PINS_F = [
+    accept_pins.test_inverse_cdf_hand_cases,
+    accept_pins.test_toy_example_from_the_page,
+    functools.partial(accept_pins.test_greedy_emits_the_targets_own_decode, 0),
+    functools.partial(accept_pins.test_greedy_emits_the_targets_own_decode, 7),
+    accept_pins.test_greedy_ties_take_the_first_index,
+    functools.partial(accept_pins.test_sampling_is_lossless, 1),
+    functools.partial(accept_pins.test_sampling_is_lossless, 3),
+    accept_pins.test_draft_equal_to_target_accepts_everything,
+    accept_pins.test_one_hot_draft,
+    functools.partial(tree_pins.test_tree_equals_each_path_as_a_sequence, 0),
+    functools.partial(tree_pins.test_tree_equals_each_path_as_a_sequence, 3),
+    tree_pins.test_one_visible_key_and_identical_keys,
+    tree_pins.test_invariances_and_head_grouping,
+]
+
+
+@pytest.mark.parametrize("name", list(MUTANTS_F))
+def test_planted_mistake_in_accept_or_tree_oracle_fails_a_pin(name, monkeypatch):
+    for module, attr, fn in MUTANTS_F[name]:
+        monkeypatch.setattr(module, attr, fn)
+    caught = []
+    for pin in PINS_F:
+        try:
+            pin()
+        except Exception:
+            caught.append(pin)
+            break
     assert caught, f"no pin caught: {name}"
