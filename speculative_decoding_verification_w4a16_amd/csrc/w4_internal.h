@@ -13,7 +13,6 @@ constexpr int kKBlock = 32;   // k per MFMA k-block (one 16x16x32 bf16 MFMA)
 constexpr int kGroup = 128;   // quantisation group along k
 constexpr int kWaves = 4;     // waves per workgroup (one chunk each)
 constexpr int kThreads = kWaves * 64;
-constexpr int kTileN = kWaves * kChunkN;  // output columns per workgroup
 constexpr int kMaxWaves = 8;              // waves per workgroup when they split one chunk's K range
 constexpr int kMaxThreads = kMaxWaves * 64;
 
@@ -29,9 +28,9 @@ struct Plan {
     int variant;  // Variant
     int mb;       // m-blocks of 16 rows (MFMA)
     int splits;   // K splits (workgroups per column tile)
-    int kw;       // waves per workgroup splitting one chunk's K range (1: four chunks per workgroup)
+    int kw;       // waves per workgroup splitting one chunk's K range (1: one chunk per wave)
     int gps;      // groups per split
-    int ntiles;   // column tiles of kTileN columns
+    int ntiles;   // column tiles (one workgroup's chunks each)
     int grid;     // workgroups
     int block;    // threads per workgroup
     int lds;      // dynamic LDS bytes per workgroup

@@ -206,7 +206,7 @@ struct LinearArgs {
     int M, N, K;
     int NC, KB, G;
     int gps, splits, ntiles;
-    int kw;          // waves of a workgroup that split one chunk's K range (1: four chunks per workgroup)
+    int kw;          // waves of a workgroup that split one chunk's K range (1: one chunk per wave)
     uint32_t mask;   // 0x000F000F (see unpack_biased)
     uint32_t magic;  // 0x43004300: bf16 128.0 in both halves
 };
@@ -579,10 +579,12 @@ __global__ __launch_bounds__(kMaxThreads) void w4a16_mfma_direct_kernel(LinearAr
 //
 // Each wave owns one chunk and every row block of 16, so each unpacked weight
 // feeds MB MFMAs and each A operand read from LDS feeds four: the LDS traffic
-// is four bytes of activations per byte of weights at M = 64.  Two waves per
-// SIMD (two workgroups per CU) overlap one wave's MFMAs with the other's
-// unpack and epilogue VALU work; a wave raises its priority while it issues
-// MFMAs, so the matrix pipe is fed first whenever both waves are ready.
+// is four bytes of activations per byte of weights at M = 64.  A workgroup
+// holds WV = 4 or 8 chunks (the planner's choice per shape) that share one
+// activation copy; two waves per SIMD (two 4-wave workgroups per CU, or one
+// 8-wave workgroup) overlap one wave's MFMAs with the other's unpack and
+// epilogue VALU work; a wave raises its priority while it issues MFMAs, so
+// the matrix pipe is fed first whenever both waves are ready.
 //
 // Activations never pass through VGPRs: global_load_lds_dwordx4 writes a
 // lane's 16 bytes straight to byte 16*lane of a 1 KB LDS line, and the
