@@ -136,7 +136,9 @@ int w4a16_linear_out(const uint16_t* x, const uint32_t* qweight_t, const uint16_
                      int splits, void* stream);
 
 /* w4a16_linear_out with the work decomposition of the M <= 16 kernels
- * forced as well, for tests and tuning sweeps.  kwaves: 0 = automatic; 1 =
+ * forced as well, for tests and tuning sweeps.  kwaves: 0 = automatic (at
+ * M = 15, 16 with N >= 4096 the LDS-ring kernel of M > 16, one chunk per
+ * wave); any other value keeps M <= 16 on the streaming MFMA kernel; 1 =
  * each wave of a workgroup streams its own 64-column chunk (four per
  * workgroup) over the workgroup's K split; 2, 4 or 8 = a workgroup of that
  * many waves streams one chunk, its waves splitting the K split's groups and
@@ -152,8 +154,9 @@ int w4a16_linear_tune(const uint16_t* x, const uint32_t* qweight_t, const uint16
  * (host outputs, any may be NULL): kernel id, K splits, waves splitting a
  * chunk's K range, workgroups, threads per workgroup, LDS bytes per
  * workgroup.  With kwaves 1 each wave streams its own chunk and the
- * workgroup holds threads/64 of them: four, or for M > 16 four or eight
- * (the planner's choice, also when splits is forced).  No HIP call. */
+ * workgroup holds threads/64 of them: four, or in the LDS-ring kernel
+ * (lds_out > 0: M > 16, or M = 15, 16 with N >= 4096 and kwaves 0) four or
+ * eight (the planner's choice, also when splits is forced).  No HIP call. */
 int w4a16_plan(int M, int N, int K, int group, int kernel, int splits, int kwaves, int* kernel_out,
                int* splits_out, int* kwaves_out, int* grid_out, int* block_out, int* lds_out);
 

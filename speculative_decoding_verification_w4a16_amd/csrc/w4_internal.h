@@ -20,7 +20,8 @@ enum KernelId { kAuto = 0, kGemv = 1, kMfma = 2 };
 
 // Kernel variants behind the ids: the VALU GEMV (M = 1), the MFMA kernel
 // with A operands loaded straight from global memory (M <= 16), and the MFMA
-// kernel with activations copied into an LDS ring (M = 17..64).
+// kernel with activations copied into an LDS ring (M = 17..64, and M = 15, 16
+// on linears of 4096 or more columns).
 enum Variant { kVarGemv = 0, kVarDirect = 1, kVarLds = 2 };
 
 struct Plan {

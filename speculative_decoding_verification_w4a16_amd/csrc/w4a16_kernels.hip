@@ -573,8 +573,9 @@ __global__ __launch_bounds__(kMaxThreads) void w4a16_mfma_direct_kernel(LinearAr
 }
 
 // ---------------------------------------------------------------------------
-// M = 17..64: bf16 MFMA, one wave per 64-column chunk over all rows,
-// activations copied into a three-deep LDS ring by the LDS DMA path
+// M = 17..64 (and M = 15, 16 on linears of 4096 or more columns): bf16
+// MFMA, one wave per 64-column chunk over all rows, activations copied into
+// a three-deep LDS ring by the LDS DMA path
 // ---------------------------------------------------------------------------
 //
 // Each wave owns one chunk and every row block of 16, so each unpacked weight
@@ -663,7 +664,8 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     // DMA sources.  A buffer holds 4 MB lines; wave w fills lines w + WV ii
     // (ii < XD; a line past the last is replaced by the wave's previous one,
-    // a second copy of the same bytes to the same place).  Line i holds rows
+    // or with fewer lines than waves by line w % 4MB: a second copy of the
+    // same bytes to the same place).  Line i holds rows
     // 4i..4i+3 and lane l lands in row 4i + l/16, slot l%16, which holds
     // k-octet (l%16) ^ (row & 15).  Rows past M repeat row M-1 (their results
     // are never stored), groups past the split repeat its last group.
@@ -671,7 +673,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int ii = 0; ii < XD; ++ii) {
         int line = wave + WV * ii;
-        if (line >= 4 * MB) line -= WV;
+        if (line >= 4 * MB) line = 4 * MB >= WV ? line - WV : line % (4 * MB);
         xline[ii] = line;
         const int r = 4 * line + o;
         xoff[ii] = min(r, a.M - 1) * a.K + 8 * (t ^ (r & 15));
@@ -776,7 +778,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 }
                 if (gl + 1 < ng) compute_xs((d + 1) % R);
 #pragma unroll
-                for (int mb = MB - 2; mb < MB; ++mb) epi(mb);
+                for (int mb = MB >= 2 ? MB - 2 : 0; mb < MB; ++mb) epi(mb);
                 wait_vmcnt<kRingOps>();  // this wave's DMA of group gl+2 (its ring slot may still fly)
                 lds_barrier();
                 issue_x(d, gl + R);
@@ -920,7 +922,13 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
     const int NC = ceil_div(N, kChunkN);
     const int G = K / kGroup;
     const int mb = ceil_div(M, 16);
-    const int variant = kernel == kGemv ? kVarGemv : (mb == 1 ? kVarDirect : kVarLds);
+    // One row block (M <= 16) streams through the direct MFMA kernel, except
+    // at M >= 15 on linears of 4096 or more columns, where the LDS kernel's
+    // shared activation copy wins (measured at M = 16: q 16.5 -> 13.9 us,
+    // lm_head 114.7 -> 103.5, gate 32.9 -> 32.1, down 30.0 -> 29.4; k and v,
+    // 1024 columns, and M <= 14 on gate and down are faster direct).
+    const bool lds_one_block = M >= 15 && N >= 4096 && kwaves == 0;
+    const int variant = kernel == kGemv ? kVarGemv : ((mb == 1 && !lds_one_block) ? kVarDirect : kVarLds);
     int lds_wv = kWaves;  // chunks per workgroup of the M > 16 kernel
     if (variant == kVarLds && kwaves > 1) return -1;
     int kw = 1;
@@ -963,7 +971,7 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
         if (splits > 0) S = splits;
         if (kwaves > 0) kw = kwaves;
     } else {
-        // M > 16: time model calibrated on MI355X sweeps of forced split
+        // LDS kernel (M > 16, or M = 15, 16 on wide linears): time model calibrated on MI355X sweeps of forced split
         // counts and workgroup widths (WV = 4 or 8 chunks, one wave each),
         //   t(S, WV) = R(workgroups) * (G/S + 4) * t_group
         //            + [S > 1] * (2 us + S * M * NCpad * 8 bytes / 5 TB/s):
@@ -1109,12 +1117,16 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
         case kVarDirect: e = launch(w4a16_mfma_direct_kernel<1, kRingDirect1>, grid, block, 0, stream, a); break;
         default:
             if (p.block == 64 * kMaxWaves) {
-                if (p.mb == 2)
+                if (p.mb == 1)
+                    e = launch(w4a16_mfma_lds_kernel<1, kMaxWaves>, grid, block, p.lds, stream, a);
+                else if (p.mb == 2)
                     e = launch(w4a16_mfma_lds_kernel<2, kMaxWaves>, grid, block, p.lds, stream, a);
                 else if (p.mb == 3)
                     e = launch(w4a16_mfma_lds_kernel<3, kMaxWaves>, grid, block, p.lds, stream, a);
                 else
                     e = launch(w4a16_mfma_lds_kernel<4, kMaxWaves>, grid, block, p.lds, stream, a);
+            } else if (p.mb == 1) {
+                e = launch(w4a16_mfma_lds_kernel<1, kWaves>, grid, block, p.lds, stream, a);
             } else if (p.mb == 2) {
                 e = launch(w4a16_mfma_lds_kernel<2, kWaves>, grid, block, p.lds, stream, a);
             } else if (p.mb == 3) {

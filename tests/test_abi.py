@@ -131,7 +131,7 @@ def test_bench_argument_errors():
     assert w4.w4_bench_read_blocks() > 0
 
 
-@pytest.mark.parametrize("M", [1, 2, 5, 8, 16, 17, 33, 64])
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 14, 15, 16, 17, 33, 64])
 @pytest.mark.parametrize("N,K", [(256, 512), (8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672),
                                  (128256, 8192), (200, 384)])
 def test_plans_fit_the_hardware(M, N, K):
@@ -142,9 +142,11 @@ def test_plans_fit_the_hardware(M, N, K):
     kw = p["kwaves"]
     assert kw in (1, 2, 4, 8) and (M <= 16 or kw == 1)
     chunks = -(-N // 64)
-    if kw == 1:  # four (or, for M > 16, eight) 64-column chunks per workgroup, one per wave
+    lds_kernel = M > 16 or (M >= 15 and N >= 4096)  # the LDS-ring kernel
+    assert (p["lds"] > 0) == lds_kernel
+    if kw == 1:  # four (or, in the LDS kernel, eight) 64-column chunks per workgroup, one per wave
         wv = p["block"] // 64
-        assert wv == 4 or (M > 16 and wv == 8)
+        assert wv == 4 or (lds_kernel and wv == 8)
         assert p["grid"] == -(-chunks // wv) * p["splits"]
     else:  # one chunk per workgroup, its kw waves splitting K
         assert p["block"] == 64 * kw and p["grid"] == chunks * p["splits"]
@@ -169,6 +171,9 @@ def test_forced_plans():
     assert (p["kwaves"], p["block"]) == (1, 256)
     p = w4.w4a16_plan(1, 8192, 8192, splits=1, kwaves=1)
     assert (p["kwaves"], p["block"], p["grid"]) == (1, 256, 32)
+    # M = 16 on a wide linear: the LDS kernel, unless the waves are forced
+    assert w4.w4a16_plan(16, 8192, 8192)["lds"] > 0
+    assert w4.w4a16_plan(16, 8192, 8192, kwaves=1)["lds"] == 0
     for bad, status in ((3, 2), (16, 2), (-1, 1)):
         with pytest.raises(w4.W4Error) as e:
             w4.w4a16_plan(1, 8192, 8192, kwaves=bad)

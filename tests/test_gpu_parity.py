@@ -217,10 +217,11 @@ def test_verify_pass_equals_separate_calls():
 # ---------------------------------------------------------------------------
 
 def test_eight_chunk_workgroups_ragged():
-    # Wide linears at M > 16 run eight chunks per workgroup.  N here leaves
+    # Wide linears at M >= 15 run eight chunks per workgroup.  N here leaves
     # the last workgroup half empty (436 chunks, 4 past a multiple of 8) and
-    # its last chunk partly padded; M = 17, 40 and 64 cover one, three (the
-    # activation copy duplicates a line) and four row blocks; sampled columns
+    # its last chunk partly padded; M = 15 and 16 (one row block: each line
+    # of the activation copy is written by two waves), 17, 40 (three row
+    # blocks: the copy duplicates a line) and 64 (four); sampled columns
     # include the first, a middle and the last chunk; the planner's split
     # count and a forced odd one both run eight-chunk workgroups.
     N, K = 27896, 8192
@@ -229,13 +230,33 @@ def test_eight_chunk_workgroups_ragged():
     x = synth.gen_x(64, K, seed_base=950)
     slices = [(0, 64), (13824, 13888), (N - 120, N)]
     refs = [linear64_columns(x, lin["qweight"], lin["scales"], lin["zeros"], 128, a, b) for a, b in slices]
-    for M in (17, 40, 64):
+    for M in (15, 16, 17, 40, 64):
         for splits in (0, 3):
             plan = w4.w4a16_plan(M, N, K, splits=splits)
-            assert plan["block"] == 512, plan
+            assert plan["block"] == 512 and plan["lds"] > 0, plan
             y = run_linear(x[:M], pk, 0, splits)
             for (a, b), (Y, A) in zip(slices, refs):
                 _check(y[:, a:b], Y[:M], A[:M], (M, splits, a))
+
+
+def test_one_row_block_lds_kernel_ragged():
+    # M = 15 and 16 on a linear of 4096 or more columns run the LDS kernel
+    # with one row block, here four chunks per workgroup: 128 chunks, the
+    # last 8 columns short; every column checked, with the planner's split
+    # count, none, and three splits of 16 groups (a short last split).
+    N, K = 8136, 2048
+    lin = synth.gen_linear(87, N, K)
+    pk = packed(lin, N, K)
+    x = synth.gen_x(16, K, seed_base=960)
+    Y, A = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+    for M in (15, 16):
+        for splits in (0, 1, 3):
+            plan = w4.w4a16_plan(M, N, K, splits=splits)
+            assert plan["block"] == 256 and plan["lds"] > 0, plan
+            _check(run_linear(x[:M], pk, 0, splits), Y[:M], A[:M], (M, splits))
+    # M = 14 stays on the streaming kernel
+    assert w4.w4a16_plan(14, N, K)["lds"] == 0
+    _check(run_linear(x[:14], pk), Y[:14], A[:14], (14, 0))
 
 
 def test_lm_head_full_size_sampled_columns():
@@ -250,7 +271,7 @@ def test_lm_head_full_size_sampled_columns():
     slices = [(0, 64), (64128, 64192), (N - 64, N)]
     refs = [linear64_columns(x, lin["qweight"], lin["scales"], lin["zeros"], 128, a, b) for a, b in slices]
     del lin
-    for M in (1, 5, 16, 17, 40, 64):
+    for M in (1, 5, 14, 16, 17, 40, 64):
         y = run_linear(x[:M], pk)
         for (a, b), (Y, A) in zip(slices, refs):
             _check(y[:, a:b], Y[:M], A[:M], ("lm_head", M, a))
@@ -270,7 +291,7 @@ def test_largest_k_one_chunk():
         _check(run_linear(x[:M], pk), Y[:M], A[:M], ("K=2**24", M))
 
 
-VERIFY_M = [1, 2, 4, 5, 8, 16, 32, 48, 64]
+VERIFY_M = [1, 2, 4, 5, 8, 15, 16, 32, 48, 64]
 
 
 @pytest.fixture(scope="module")
