@@ -27,7 +27,8 @@ enum Variant { kVarGemv = 0, kVarDirect = 1, kVarLds = 2 };
 struct Plan {
     int kernel;   // kGemv or kMfma
     int variant;  // Variant
-    int mb;       // m-blocks of 16 rows (MFMA)
+    int mb;       // m-blocks of 16 rows (MFMA) per workgroup
+    int rs;       // row slices: workgroups per column tile and split along M (LDS kernel), mb blocks each
     int splits;   // K splits (workgroups per column tile)
     int kw;       // waves per workgroup splitting one chunk's K range (1: one chunk per wave)
     int gps;      // groups per split

@@ -207,6 +207,7 @@ struct LinearArgs {
     int NC, KB, G;
     int gps, splits, ntiles;
     int kw;          // waves of a workgroup that split one chunk's K range (1: one chunk per wave)
+    int rs;          // row slices of the LDS kernel (workgroups along M, 16 MB rows each)
     uint32_t mask;   // 0x000F000F (see unpack_biased)
     uint32_t magic;  // 0x43004300: bf16 128.0 in both halves
 };
@@ -578,9 +579,11 @@ __global__ __launch_bounds__(kMaxThreads) void w4a16_mfma_direct_kernel(LinearAr
 // a three-deep LDS ring by the LDS DMA path
 // ---------------------------------------------------------------------------
 //
-// Each wave owns one chunk and every row block of 16, so each unpacked weight
-// feeds MB MFMAs and each A operand read from LDS feeds four: the LDS traffic
-// is four bytes of activations per byte of weights at M = 64.  A workgroup
+// Each wave owns one chunk and every row block of 16 of its workgroup's row
+// slice (all rows, or, on narrow linears, MB row blocks starting at row
+// 16 MB * slice), so each unpacked weight feeds MB MFMAs and each A operand
+// read from LDS feeds four: the LDS traffic is four bytes of activations per
+// byte of weights at M = 64.  A workgroup
 // holds WV = 4 or 8 chunks (the planner's choice per shape) that share one
 // activation copy; two waves per SIMD (two 4-wave workgroups per CU, or one
 // 8-wave workgroup) overlap one wave's MFMAs with the other's unpack and
@@ -652,11 +655,16 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     extern __shared__ __align__(16) char smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int split = blockIdx.x / a.ntiles;
-    const int tile = blockIdx.x - split * a.ntiles;
+    // workgroup = (row slice, K split, column tile), the tile fastest
+    const int per_slice = a.splits * a.ntiles;
+    const int slice = blockIdx.x / per_slice;
+    const int split = (blockIdx.x - slice * per_slice) / a.ntiles;
+    const int tile = blockIdx.x - slice * per_slice - split * a.ntiles;
     const int g0 = split * a.gps;
     const int ng = min(a.G, g0 + a.gps) - g0;
     const int c = tile * WV + wave;
+    const int m0 = slice * 16 * MB;            // first row of this slice
+    const int ml = min(a.M - m0, 16 * MB);     // its rows (>= 1)
     const int o = lane >> 4, t = lane & 15;
     const uint32_t mask = a.mask, magic = to_vgpr(a.magic);
     const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
@@ -665,10 +673,11 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // DMA sources.  A buffer holds 4 MB lines; wave w fills lines w + WV ii
     // (ii < XD; a line past the last is replaced by the wave's previous one,
     // or with fewer lines than waves by line w % 4MB: a second copy of the
-    // same bytes to the same place).  Line i holds rows
-    // 4i..4i+3 and lane l lands in row 4i + l/16, slot l%16, which holds
-    // k-octet (l%16) ^ (row & 15).  Rows past M repeat row M-1 (their results
-    // are never stored), groups past the split repeat its last group.
+    // same bytes to the same place).  Line i holds rows m0 + 4i..4i+3 of the
+    // slice and lane l lands in row 4i + l/16, slot l%16, which holds
+    // k-octet (l%16) ^ (row & 15).  Rows past the slice's last repeat it
+    // (their results are never stored), groups past the split repeat its
+    // last group.
     int xoff[XD], xline[XD];
 #pragma unroll
     for (int ii = 0; ii < XD; ++ii) {
@@ -676,7 +685,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (line >= 4 * MB) line = 4 * MB >= WV ? line - WV : line % (4 * MB);
         xline[ii] = line;
         const int r = 4 * line + o;
-        xoff[ii] = min(r, a.M - 1) * a.K + 8 * (t ^ (r & 15));
+        xoff[ii] = (m0 + min(r, ml - 1)) * a.K + 8 * (t ^ (r & 15));
     }
     const uint16_t* xg = a.x + (size_t)g0 * kGroup;
     auto issue_x = [&](int buf, int gl) {
@@ -797,8 +806,8 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 const int n = c * kChunkN + 16 * j + t;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int m = 16 * mb + 4 * o + r;
-                    if (m < a.M && n < a.N) {
+                    const int m = m0 + 16 * mb + 4 * o + r;
+                    if (m - m0 < ml && n < a.N) {
                         if (a.splits == 1)
                             store_y(a, (size_t)m * a.N + n, yv[mb][j][r]);
                         else
@@ -930,6 +939,7 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
     const bool lds_one_block = M >= 15 && N >= 4096 && kwaves == 0;
     const int variant = kernel == kGemv ? kVarGemv : ((mb == 1 && !lds_one_block) ? kVarDirect : kVarLds);
     int lds_wv = kWaves;  // chunks per workgroup of the M > 16 kernel
+    int rs = 1;           // its row slices
     if (variant == kVarLds && kwaves > 1) return -1;
     int kw = 1;
     int S = 1;
@@ -971,8 +981,9 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
         if (splits > 0) S = splits;
         if (kwaves > 0) kw = kwaves;
     } else {
-        // LDS kernel (M > 16, or M = 15, 16 on wide linears): time model calibrated on MI355X sweeps of forced split
-        // counts and workgroup widths (WV = 4 or 8 chunks, one wave each),
+        // LDS kernel (M > 16, or M = 15, 16 on wide linears): time model
+        // calibrated on MI355X sweeps of forced split counts and workgroup
+        // widths (WV = 4 or 8 chunks, one wave each),
         //   t(S, WV) = R(workgroups) * (G/S + 4) * t_group
         //            + [S > 1] * (2 us + S * M * NCpad * 8 bytes / 5 TB/s):
         // a CU holds two 4-wave workgroups side by side, and a CU running two
@@ -989,16 +1000,30 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
         // 15.8 us, S = 22 16.7 us; at M = 32 12.2 against 13.7 us).  The least
         // t wins, ties to the smaller S and WV; a forced split count keeps S
         // and still chooses WV.
-        const double t_group = 0.375 * mb;
+        //
+        // Row slices: where even the most splits leave at least half the CUs
+        // without a workgroup (k and v: 16 chunks, 64 workgroups at S = 16),
+        // the row blocks are shared out between up to four workgroups per
+        // column tile and split, each copying and multiplying only its own
+        // rows (the weights are read once per slice, the later reads from
+        // L2 or the MALL).  k at M = 64: 15.8 us in one slice, 12.3 in two,
+        // 10.7 in four; at M = 32 12.2 against 10.1 in two.  Wider linears
+        // lose (q at M = 64 equal in two, gate and down 5-20 % slower).
         const double red_bytes = (double)M * NC * kChunkN * 8;
         const int smax = std::max(1, G / 4);
+        const long wgs_one = (long)ceil_div(NC, kWaves) * (splits > 0 ? splits : smax);
+        int rs_cap = 1;
+        while (rs_cap < 4 && rs_cap < mb && wgs_one * rs_cap * 2 <= 256) rs_cap *= 2;
+        const int mbw = ceil_div(mb, rs_cap);
+        rs = ceil_div(mb, mbw);
         double best = 1e30;
         int bs = 1;
+        const double t_group = 0.375 * mbw;
         for (int wv = kWaves; wv <= kMaxWaves; wv *= 2) {
             const int ntiles = ceil_div(NC, wv);
             for (int s = 1; s <= smax || (splits > 0 && s <= splits); ++s) {
                 if (splits > 0 && s != splits) continue;
-                const double wgs = (double)ntiles * s;
+                const double wgs = (double)ntiles * s * rs;
                 const double rounds = wv == kWaves ? (wgs <= 256.0 ? 1.0 : 1.4 * std::ceil(wgs / 512.0))
                                                    : 1.3 * std::ceil(wgs / 256.0);
                 double t = rounds * ((double)G / s + 4.0) * t_group;
@@ -1027,16 +1052,17 @@ int plan_linear(int M, int N, int K, int kernel, int splits, int kwaves, size_t 
     const int ntiles = kw == 1 ? ceil_div(NC, wg_chunks) : NC;
     p->kernel = kernel;
     p->variant = variant;
-    p->mb = mb;
+    p->mb = ceil_div(mb, rs);
+    p->rs = rs;
     p->splits = S;
     p->kw = kw;
     p->gps = gps;
     p->ntiles = ntiles;
-    p->grid = ntiles * S;
+    p->grid = ntiles * S * rs;
     p->block = 64 * (kw == 1 ? wg_chunks : kw);
     p->lds = 0;
     if (variant == kVarLds) {
-        p->lds = lds_ring_bytes(mb);
+        p->lds = lds_ring_bytes(p->mb);
     }
     return 0;
 }
@@ -1108,6 +1134,7 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
     a.splits = p.splits;
     a.ntiles = p.ntiles;
     a.kw = p.kw;
+    a.rs = p.rs;
     a.mask = kNibbleMask;
     a.magic = kBiasMagic;
     const dim3 grid(p.grid), block(p.block);

@@ -131,7 +131,7 @@ def test_bench_argument_errors():
     assert w4.w4_bench_read_blocks() > 0
 
 
-@pytest.mark.parametrize("M", [1, 2, 5, 8, 14, 15, 16, 17, 33, 64])
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 14, 15, 16, 17, 32, 33, 48, 64])
 @pytest.mark.parametrize("N,K", [(256, 512), (8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672),
                                  (128256, 8192), (200, 384)])
 def test_plans_fit_the_hardware(M, N, K):
@@ -147,7 +147,15 @@ def test_plans_fit_the_hardware(M, N, K):
     if kw == 1:  # four (or, in the LDS kernel, eight) 64-column chunks per workgroup, one per wave
         wv = p["block"] // 64
         assert wv == 4 or (lds_kernel and wv == 8)
-        assert p["grid"] == -(-chunks // wv) * p["splits"]
+        # the LDS kernel may share the row blocks out between 2..4 workgroups
+        tiles = -(-chunks // wv) * p["splits"]
+        assert p["grid"] % tiles == 0
+        rs = p["grid"] // tiles
+        mb = -(-M // 16)
+        assert rs == 1 or (lds_kernel and rs <= min(4, mb) and tiles * rs <= 256)
+        # the narrow k/v projection at M > 16 gets its rows shared out
+        if (N, K) == (1024, 8192) and M > 16:
+            assert rs == min(mb, 4) if mb != 3 else rs == 3
     else:  # one chunk per workgroup, its kw waves splitting K
         assert p["block"] == 64 * kw and p["grid"] == chunks * p["splits"]
         gps = -(-(K // 128) // p["splits"])

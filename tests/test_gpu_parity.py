@@ -259,6 +259,29 @@ def test_one_row_block_lds_kernel_ragged():
     _check(run_linear(x[:14], pk), Y[:14], A[:14], (14, 0))
 
 
+def test_row_slices_ragged():
+    # Narrow linears at M > 16 share their row blocks out between two to four
+    # workgroups per column tile and split (row slices of one or two blocks;
+    # the last slice short or a single row).  16 chunks, the last 24 columns
+    # short; every column checked at every slice boundary, with the
+    # planner's split count, none, an odd forced count, and 20 requested
+    # (16 run), which leaves room for two slices of two blocks at M > 32.
+    N, K = 1000, 8192
+    lin = synth.gen_linear(89, N, K)
+    pk = packed(lin, N, K)
+    x = synth.gen_x(64, K, seed_base=970)
+    Y, A = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+    chunks = -(-N // 64)
+    for M in (17, 31, 32, 33, 47, 48, 49, 63, 64):
+        for splits in (0, 1, 5, 20):
+            plan = w4.w4a16_plan(M, N, K, splits=splits)
+            rs = plan["grid"] // (-(-chunks // (plan["block"] // 64)) * plan["splits"])
+            assert rs > 1 and plan["lds"] > 0, plan
+            if splits == 20 and M > 32:
+                assert rs == 2 and plan["lds"] == 24960, plan  # two row blocks per workgroup
+            _check(run_linear(x[:M], pk, 0, splits), Y[:M], A[:M], (M, splits, rs))
+
+
 def test_lm_head_full_size_sampled_columns():
     # The widest linear of the sweep at full size (N = 128256 = 2004 chunks, so
     # the last eight-chunk workgroup is half empty), its seed as in the sweep,
