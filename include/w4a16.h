@@ -156,7 +156,11 @@ int w4a16_linear_tune(const uint16_t* x, const uint32_t* qweight_t, const uint16
  * workgroup.  With kwaves 1 each wave streams its own chunk and the
  * workgroup holds threads/64 of them: four, or in the LDS-ring kernel
  * (lds_out > 0: M > 16, or M = 15, 16 with N >= 4096 and kwaves 0) four or
- * eight (the planner's choice, also when splits is forced).  No HIP call. */
+ * eight (the planner's choice, also when splits is forced).  Workgroups =
+ * column tiles x K splits x row slices: the LDS-ring kernel shares the row
+ * blocks of a narrow linear out between two to four workgroups (row slices)
+ * where even its most splits would leave half of the 256 CUs idle; the
+ * slice count is grid_out / (tiles x splits).  No HIP call. */
 int w4a16_plan(int M, int N, int K, int group, int kernel, int splits, int kwaves, int* kernel_out,
                int* splits_out, int* kwaves_out, int* grid_out, int* block_out, int* lds_out);
 

@@ -249,8 +249,9 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
 // weight, scale and zero byte is read once per call, while the activation
 // rows are re-read by every wave from L2; marking the one-pass stream
 // non-temporal keeps it from evicting them.  Measured on MI355X: 5-12 % off
-// the M = 1 and M = 5 linears (lm_head at M = 1: 101 -> 89 us).  The M > 16
-// kernel keeps ordinary loads (no gain there: its activations sit in LDS).
+// the M = 1 and M = 5 linears (lm_head at M = 1: 101 -> 89 us).  The LDS-ring
+// kernel keeps ordinary loads (no gain there: its activations sit in LDS, and
+// its row slices re-read a tile's weights from L2).
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ uint2 load_stream(const uint2* p) {
     const uint64_t v = __builtin_nontemporal_load((const uint64_t*)p);
