@@ -190,9 +190,14 @@ def test_determinism_and_row_independence():
         assert worst <= 1.0
 
 
-def test_verify_pass_equals_separate_calls():
-    shapes = [(256, 512), (1024, 512), (512, 1024)]
-    M = 5
+@pytest.mark.parametrize("M", [1, 5, 16, 40, 64])
+def test_verify_pass_equals_separate_calls(M):
+    # every kernel path in one pass: the GEMV (M = 1), the streaming MFMA
+    # kernel, the one-row-block LDS kernel (M = 16 on the 4096-column linear),
+    # row slices (M > 16 on the narrow ones) and the full LDS kernel
+    shapes = [(256, 512), (1024, 512), (512, 1024), (4096, 512)]
+    if M == 16:
+        assert w4.w4a16_plan(M, 4096, 512)["lds"] > 0 and w4.w4a16_plan(M, 1024, 512)["lds"] == 0
     lins, descs, ys = [], [], []
     xs = {}
     for i, (N, K) in enumerate(shapes):
