@@ -110,7 +110,7 @@ def test_fused_projection_contract(parts, fused):
         Y, A = linear64_columns(x, lin["qweight"], lin["scales"], lin["zeros"], 128, a, a + 64)
         checks.append((n0 + a, Y, A, n))
         n0 += N
-    for M in (1, 5, 17, 64):
+    for M in (1, 5, 16, 17, 48, 64):
         y = _run(x[:M], pk, False)
         yb = _run(x[:M], pk, True).view(np.uint16)
         assert np.array_equal(yb, round_to_bf16(y).astype(np.uint16))

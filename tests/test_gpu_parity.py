@@ -319,7 +319,10 @@ def test_largest_k_one_chunk():
         _check(run_linear(x[:M], pk), Y[:M], A[:M], ("K=2**24", M))
 
 
-VERIFY_M = [1, 2, 4, 5, 8, 15, 16, 32, 48, 64]
+# plain decode, sequence drafts, and tree drafts at every row-block count
+# (17, 33, 49 open a row block; on k and v they start two, three and four
+# row slices)
+VERIFY_M = [1, 2, 4, 5, 8, 15, 16, 17, 32, 33, 48, 49, 63, 64]
 
 
 @pytest.fixture(scope="module")
