@@ -848,13 +848,14 @@ def main():
         torch.cuda.synchronize()
         us_eager[M] = s.elapsed_time(e) * 1e3
 
-    # per-kernel roofline: every linear of a pass runs one kernel instantiation
+    # per-kernel roofline: every linear of a pass runs one kernel
     # (M=1 -> the GEMV, M=5 -> the direct MFMA kernel with one m-block,
-    # M=64 -> the LDS-ring MFMA kernel with four m-blocks), followed, when its
+    # M=64 -> the LDS-ring MFMA kernel with four m-blocks, on k and v four row
+    # slices of one m-block each), followed, when its
     # K is split, by splitk_reduce_kernel; the unit of the figures below is
     # the linear, i.e. that kernel plus its reduction.
     kernel_of = {1: "w4a16_gemv_kernel<4>", 5: "w4a16_mfma_direct_kernel<1, 4>",
-                 64: "w4a16_mfma_lds_kernel<4, 4 or 8>"}
+                 64: "w4a16_mfma_lds_kernel<4 (k, v: 1), 4 or 8>"}
     # The graph of a pass holds nothing but those launches (the gaps between
     # them measure ~0 in the kernel trace), so the pass time per linear is the
     # mean duration of a linear; events around single eager linears are
