@@ -48,6 +48,26 @@ def test_k_splitting_workgroups_meet_the_contract(N, K, M, kernel):
             assert ok, (N, K, M, kernel, kwaves, splits, plan, worst)
 
 
+@pytest.mark.parametrize("M", [15, 16])
+def test_forced_waves_keep_wide_m16_on_the_streaming_kernel(M):
+    # Left to the planner, M = 15 and 16 on 4096 or more columns run the LDS
+    # kernel; a forced kwaves keeps them on the streaming MFMA kernel.  Both
+    # meet the contract on a ragged N (65 chunks, the last 8 columns wide).
+    N, K = 4104, 1024
+    lin = synth.gen_linear(94, N, K)
+    pk = packed(lin, N, K)
+    x = synth.gen_x(M, K, seed_base=730)
+    Y, A = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+    assert w4.w4a16_plan(M, N, K)["lds"] > 0
+    ok, worst = check_contract(_run(x, pk, 0, 0), Y, A)
+    assert ok, ("lds", worst)
+    for kwaves in (1, 4):
+        for splits in (1, 3):
+            assert w4.w4a16_plan(M, N, K, splits=splits, kwaves=kwaves)["lds"] == 0
+            ok, worst = check_contract(_run(x, pk, kwaves, splits), Y, A)
+            assert ok, (kwaves, splits, worst)
+
+
 @pytest.mark.parametrize("M,kernel", [(1, 1), (5, 0)])
 def test_k_splitting_bf16_is_the_rounded_fp32_output(M, kernel):
     N, K = 1000, 1152
