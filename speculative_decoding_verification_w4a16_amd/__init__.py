@@ -219,9 +219,30 @@ def accept(logits, draft, draft_logits=None, u=None, out=None, stream=None):
     Returns an int32 tensor [2]: (drafted tokens accepted, next token)."""
     import torch
 
+    if logits.dim() != 2 or logits.shape[0] < 1:
+        raise ValueError(f"logits: expected [K+1, V], got shape {tuple(logits.shape)}")
     K, V = logits.shape[0] - 1, logits.shape[1]
+    dev = logits.device
+    _require("logits", logits, (K + 1, V), (4,))
+    if logits.dtype != torch.float32:
+        raise ValueError(f"logits: expected float32, got {logits.dtype}")
+    _require("draft", draft, (K,), (4,))
+    if draft.dtype != torch.int32:
+        raise ValueError(f"draft: expected int32, got {draft.dtype}")
+    if (draft_logits is None) != (u is None):
+        raise ValueError("the sampled step needs both draft_logits and u")
+    if draft_logits is not None:
+        _require("draft_logits", draft_logits, (K, V), (4,))
+        _require("u", u, (K + 1,), (4,))
+        if draft_logits.dtype != torch.float32 or u.dtype != torch.float32:
+            raise ValueError("draft_logits and u must be float32")
+        _on_device(dev, draft_logits=draft_logits, u=u)
+    if out is not None:
+        _require("out", out, (2,), (4,))
+        _on_device(dev, out=out)
+    _on_device(dev, logits=logits, draft=draft)
     if out is None:
-        out = torch.empty(2, dtype=torch.int32, device=logits.device)
+        out = torch.empty(2, dtype=torch.int32, device=dev)
     if draft_logits is None:
         w4_accept_greedy(logits, draft, K, V, out, stream)
     else:
@@ -243,10 +264,25 @@ def tree_attention(q, k_cache, v_cache, k_draft, v_draft, masks, scale=0.0, out=
     bits), masks [M] int64 (uint64 bit patterns).  Returns fp32 [M, Hq, 128]."""
     import torch
 
+    if q.dim() != 3 or k_cache.dim() != 3 or k_draft.dim() != 3:
+        raise ValueError("q [M, Hq, D], caches [L, Hkv, D] and draft keys/values [M, Hkv, D] are 3-D")
     M, Hq, D = q.shape
     L, Hkv = k_cache.shape[0], k_draft.shape[1]
+    dev = q.device
+    _require("q", q, (M, Hq, D), (2,))
+    _require("k_cache", k_cache, (L, Hkv, D), (2,))
+    _require("v_cache", v_cache, (L, Hkv, D), (2,))
+    _require("k_draft", k_draft, (M, Hkv, D), (2,))
+    _require("v_draft", v_draft, (M, Hkv, D), (2,))
+    _require("masks", masks, (M,), (8,))
+    if out is not None:
+        _require("out", out, (M, Hq, D), (4,))
+        if out.dtype != torch.float32:
+            raise ValueError(f"out: expected float32, got {out.dtype}")
+        _on_device(dev, out=out)
+    _on_device(dev, q=q, k_cache=k_cache, v_cache=v_cache, k_draft=k_draft, v_draft=v_draft, masks=masks)
     if out is None:
-        out = torch.empty((M, Hq, D), dtype=torch.float32, device=q.device)
+        out = torch.empty((M, Hq, D), dtype=torch.float32, device=dev)
     w4_tree_attention(q, k_cache if L else None, v_cache if L else None, k_draft, v_draft, masks, M, L, Hq, Hkv, D,
                       scale, out, stream)
     return out
@@ -260,6 +296,32 @@ def w4_bench_copy(dst, src, nbytes, stream=None):
 # ---------------------------------------------------------------------------
 # torch-tensor conveniences (allocation + the calls above)
 # ---------------------------------------------------------------------------
+
+def _require(name, t, shape, itemsizes):
+    """Raise ValueError unless `t` is a contiguous tensor of `shape` whose
+    element size is one of `itemsizes`.  The C ABI takes raw addresses and
+    trusts the sizes it is given, so the conveniences check every tensor
+    they hand over (then _on_device checks where they live)."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.element_size() not in itemsizes:
+        raise ValueError(f"{name}: {t.dtype} has {t.element_size()}-byte elements, expected {itemsizes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _on_device(device, **tensors):
+    """Raise ValueError unless every tensor is a GPU tensor on `device`."""
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name}: expected a GPU tensor, got one on {t.device}")
+        if t.device != device:
+            raise ValueError(f"{name}: on {t.device}, expected {device}")
+
 
 class PackedLinear:
     """Tile-layout weights of one (N, K) linear on a device."""
@@ -277,8 +339,12 @@ def repack(qweight, scales, zeros, N, K, group=GROUP, stream=None) -> PackedLine
     """Device canonical tensors (int32, int16/uint16 bits, int32) -> PackedLinear."""
     import torch
 
-    qb, sb, zb = w4_repacked_sizes(N, K, group)
     dev = qweight.device
+    _require("qweight", qweight, (K // 8, N), (4,))
+    _require("scales", scales, (K // group, N), (2,))
+    _require("zeros", zeros, (K // group, N // 8), (4,))
+    _on_device(dev, qweight=qweight, scales=scales, zeros=zeros)
+    qb, sb, zb = w4_repacked_sizes(N, K, group)
     qt = torch.empty(qb // 4, dtype=torch.int32, device=dev)
     st = torch.empty(sb // 2, dtype=torch.int16, device=dev)
     zt = torch.empty(zb // 2, dtype=torch.int16, device=dev)
@@ -291,9 +357,23 @@ def linear(x, w: PackedLinear, y=None, kernel=W4_KERNEL_AUTO, splits=0, stream=N
     or bf16 bit patterns (int16 tensor) with out_bf16."""
     import torch
 
+    if x.dim() != 2:
+        raise ValueError(f"x: expected [M, K], got shape {tuple(x.shape)}")
     M = x.shape[0]
+    _require("x", x, (M, w.K), (2,))
+    qb, sb, zb = w4_repacked_sizes(w.N, w.K, w.group)
+    _require("qweight_t", w.qweight_t, (qb // 4,), (4,))
+    _require("scales_t", w.scales_t, (sb // 2,), (2,))
+    _require("zeros_t", w.zeros_t, (zb // 2,), (2,))
+    if y is not None:
+        _require("y", y, (M, w.N), (2,) if out_bf16 else (4,))
+        if not out_bf16 and y.dtype != torch.float32:
+            raise ValueError(f"y: fp32 output needs a float32 tensor, got {y.dtype}")
+    _on_device(x.device, x=x, qweight_t=w.qweight_t, scales_t=w.scales_t, zeros_t=w.zeros_t)
     if y is None:
         y = torch.empty((M, w.N), dtype=torch.int16 if out_bf16 else torch.float32, device=x.device)
+    else:
+        _on_device(x.device, y=y)
     w4a16_linear_tune(x, w.qweight_t, w.scales_t, w.zeros_t, M, w.N, w.K, w.group, y,
                       W4_OUT_BF16 if out_bf16 else W4_OUT_F32, kernel, splits, kwaves, stream)
     return y

@@ -232,6 +232,12 @@ __device__ float block_scan(float v, float* sh) {
     return sh[tid];
 }
 
+// The draw selects, at each of its two levels (slice, then element), the
+// lowest thread whose scan interval [exclusive, inclusive) holds the target:
+// rounding can make neighbouring intervals overlap, and an LDS atomicMin makes
+// the choice unique and the same on every run.  Every thread reads the
+// winner into a register after a barrier and branches on that copy, so all
+// waves take the same path and meet the same barriers.
 __global__ __launch_bounds__(kAccThreads) void accept_draw_kernel(const AcceptState* __restrict__ stp,
                                                                     const float* __restrict__ lt,
                                                                     const float* __restrict__ ld,
@@ -239,6 +245,7 @@ __global__ __launch_bounds__(kAccThreads) void accept_draw_kernel(const AcceptSt
                                                                     const float* __restrict__ part, int nparts,
                                                                     int32_t* __restrict__ out) {
     __shared__ float sh[kAccThreads];
+    __shared__ int win;
     __shared__ int pick_slice, pick;
     __shared__ float base;
     const AcceptState st = *stp;
@@ -250,35 +257,38 @@ __global__ __launch_bounds__(kAccThreads) void accept_draw_kernel(const AcceptSt
     const float incl = block_scan(mine, sh);
     const float total = sh[kAccThreads - 1];
     const float target = u[K] * total;
-    if (tid == 0) pick_slice = -1;
+    if (tid == 0) win = kAccThreads;
     __syncthreads();
-    // the thread whose range of slices crosses the target finds the slice
     const float excl = incl - mine;
-    if (mine > 0.0f && excl <= target && target < incl) {
-        float acc = excl;
-        int b = tid * c;
-        for (; b < min(nparts, (tid + 1) * c) - 1; ++b) {
-            if (acc + part[b] > target) break;
-            acc += part[b];
+    if (mine > 0.0f && excl <= target && target < incl) atomicMin(&win, tid);
+    __syncthreads();
+    const int w1 = win;  // uniform
+    if (w1 < kAccThreads) {
+        // the winning thread walks its slices to the one that crosses the target
+        if (tid == w1) {
+            float acc = excl;
+            int b = tid * c;
+            for (; b < min(nparts, (tid + 1) * c) - 1; ++b) {
+                if (acc + part[b] > target) break;
+                acc += part[b];
+            }
+            pick_slice = b;
+            base = acc;
         }
+    } else if (tid == 0) {
+        // rounding put the target at (or past) the total: the last slice with weight
+        int b = nparts - 1;
+        while (b > 0 && part[b] <= 0.0f) --b;
+        float acc = 0.0f;
+        for (int i = 0; i < b; ++i) acc += part[i];
         pick_slice = b;
         base = acc;
     }
     __syncthreads();
-    if (pick_slice < 0) {
-        // rounding put the target at (or past) the total: the last slice with weight
-        if (tid == 0) {
-            int b = nparts - 1;
-            while (b > 0 && part[b] <= 0.0f) --b;
-            float acc = 0.0f;
-            for (int i = 0; i < b; ++i) acc += part[i];
-            pick_slice = b;
-            base = acc;
-        }
-        __syncthreads();
-    }
+    const int ps = pick_slice;
+    const float b0 = base;
     // scan inside the slice: thread t holds its 4 consecutive elements
-    const int lo = pick_slice * kDrawSlice + 4 * tid;
+    const int lo = ps * kDrawSlice + 4 * tid;
     float w4v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float s = 0.0f;
     for (int k = 0; k < 4; ++k)
@@ -286,30 +296,32 @@ __global__ __launch_bounds__(kAccThreads) void accept_draw_kernel(const AcceptSt
             w4v[k] = draw_weight(st, lt, ld, V, lo + k);
             s += w4v[k];
         }
-    const float in2 = block_scan(s, sh) + base;
-    if (tid == 0) pick = -1;
+    const float in2 = block_scan(s, sh) + b0;
+    if (tid == 0) win = kAccThreads;
     __syncthreads();
     const float ex2 = in2 - s;
-    if (s > 0.0f && ex2 <= target && target < in2) {
-        float acc = ex2;
-        int k = 0;
-        for (; k < 3; ++k) {
-            if (w4v[k] > 0.0f && acc + w4v[k] > target) break;
-            acc += w4v[k];
+    if (s > 0.0f && ex2 <= target && target < in2) atomicMin(&win, tid);
+    __syncthreads();
+    const int w2 = win;  // uniform
+    if (w2 < kAccThreads) {
+        if (tid == w2) {
+            float acc = ex2;
+            int k = 0;
+            for (; k < 3; ++k) {
+                if (w4v[k] > 0.0f && acc + w4v[k] > target) break;
+                acc += w4v[k];
+            }
+            while (k > 0 && w4v[k] <= 0.0f) --k;
+            pick = lo + k;
         }
-        while (k > 0 && w4v[k] <= 0.0f) --k;
-        pick = lo + k;
+    } else if (tid == 0) {
+        // rounding: the last element of the slice with weight
+        int k = min(V, (ps + 1) * kDrawSlice) - 1;
+        while (k > ps * kDrawSlice && draw_weight(st, lt, ld, V, k) <= 0.0f) --k;
+        pick = k;
     }
     __syncthreads();
-    if (tid == 0) {
-        if (pick < 0) {
-            // rounding: the last element of the slice with weight
-            int k = min(V, (pick_slice + 1) * kDrawSlice) - 1;
-            while (k > pick_slice * kDrawSlice && draw_weight(st, lt, ld, V, k) <= 0.0f) --k;
-            pick = k;
-        }
-        out[1] = pick;
-    }
+    if (tid == 0) out[1] = pick;
 }
 
 int stats_slices(int rows, int V) {

@@ -131,3 +131,37 @@ def test_large_logit_offsets_and_determinism():
 def test_errors_before_any_launch():
     with pytest.raises(w4.W4Error):
         w4.w4_accept_greedy(0x1000, 0x2000, 65, 1024, 0x3000, stream=0)
+
+
+@pytest.mark.parametrize("V", [1000, VOCAB])
+def test_final_draw_at_the_top_of_the_distribution(V):
+    # u just below 1 puts u * total at (or, after fp32 rounding, past) the last
+    # inclusive sum: the draw must still return the last token with weight.
+    # The last token carries a large weight, so the oracle's float64 decision
+    # is the same token, far from any boundary.  Also u = 0: the first token
+    # with weight; and the draft equal to the target (all kept, row K drawn).
+    rng = np.random.default_rng(44 + V)
+    K = 3
+    L = rng.normal(0.0, 1.0, (K + 1, V)).astype(np.float32)
+    L[:, V - 1] = 8.0
+    L[:, V - 2] = -1e4  # the second-to-last token has no weight (exp underflows to 0 in fp32 and float64)
+    L[:, 0] = 6.0
+    d = np.array([V - 1] * K, np.int32)
+    top = np.float32(1.0) - np.float32(2.0 ** -24)
+    for uK in (top, np.float32(0.0)):
+        u = np.array([0.5] * K + [uK], np.float32)
+        exp = accept_sampled(L, L[:K], d, u.astype(np.float64))
+        assert exp == (K, V - 1 if uK > 0 else 0)
+        for _ in range(3):  # the same answer on every run
+            assert _sampled(L, L[:K], d, u) == exp, (V, float(uK))
+    # rejected at token 0 (the draft puts almost all its mass there): the residual
+    # max(0, p - q) keeps the last token, where the draft has less mass than the
+    # target, and the draw at u -> 1 returns it
+    Q = L[:K].copy()
+    Q[0, V - 1] = 6.0
+    Q[0, 0] = 20.0
+    d0 = np.array([0, V - 1, V - 1], np.int32)
+    u = np.array([0.99, 0.5, 0.5, top], np.float32)
+    exp = accept_sampled(L, Q, d0, u.astype(np.float64))
+    assert exp == (0, V - 1)
+    assert _sampled(L, Q, d0, u) == exp

@@ -135,25 +135,22 @@ def test_every_split_reduction_width(M):
         _check(run_linear(x, pk, 0, splits), Y, A, (M, splits))
 
 
-@pytest.mark.parametrize("M,kernel", [(1, 1), (1, 2), (16, 0), (40, 0)])
+@pytest.mark.parametrize("M,kernel", [(1, 1), (1, 2), (16, 0), (40, 0), (64, 0)])
 def test_one_hot_rows_bit_exact(M, kernel):
-    # GP2: x = e_k at nibble positions, group edges and the first/last k
+    # GP2: x = e_k for every k of the K = 512 linear (all nibble positions,
+    # group edges, the first and last k), M rows per call through each
+    # kernel path, unsplit and split three ways: y equals the dequantised
+    # weight row (q - z) * s exactly
     N, K = 136, 512
     lin = synth.gen_linear(60, N, K)
-    ks = [0, 1, 2, 3, 4, 5, 6, 7, 8, 31, 32, 127, 128, 129, 255, 256, 300, 383, 384, 511]
-    W64 = None
     pk = packed(lin, N, K)
-    for i0 in range(0, len(ks), M):
-        rows = ks[i0:i0 + M]
-        x = np.zeros((len(rows), K), np.float32)
-        for i, k in enumerate(rows):
-            x[i, k] = 1.0
-        xb = synth.f32_to_bf16_bits(x)
-        Y, _ = linear64(xb, lin["qweight"], lin["scales"], lin["zeros"])
+    x = synth.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    Y, _ = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+    for i0 in range(0, K, M):
+        rows = slice(i0, min(K, i0 + M))
         for splits in (1, 3):
-            y = run_linear(xb, pk, kernel, splits)
-            assert np.array_equal(y.astype(np.float64), Y), (rows, splits)
-    del W64
+            y = run_linear(x[rows], pk, kernel, splits)
+            assert np.array_equal(y.astype(np.float64), Y[rows]), (i0, splits)
 
 
 def test_empty_and_degenerate_calls():

@@ -10,7 +10,8 @@ the page's A -> B, C, D tree; prefixes that end inside a 64-key chunk and on
 its edge; the Llama-3-70B grouping (64 query heads over 8 key/value heads)
 and other groupings; a token that sees nothing; one key split and the most
 splits (M = 1 over 4096 and 12288 keys); repeatability, also with calls of
-other shapes in between (the split merge uses per-tile arrival counters).
+other shapes in between (the key splits' partial results share one
+workspace, merged by a second launch).
 """
 import numpy as np
 import pytest
@@ -98,9 +99,9 @@ def test_repeatable():
 
 
 def test_repeatable_across_shapes():
-    # the key splits are merged by whichever workgroup arrives last at a
-    # per-tile counter; calls of other shapes in between must leave every
-    # counter ready for the next call
+    # the key splits' partial results go through one shared workspace and
+    # are merged by a second launch; calls of other shapes in between (other
+    # split counts and workspace extents) must not change the next result
     a, _ = _case(11, 1, 4096, 64, 8, [-1])
     _case(12, 64, 1000, 64, 8, list(range(-1, 63)))
     _case(13, 3, 30, 64, 8, [-1, 0, 1])

@@ -9,7 +9,9 @@ oracle's own formulas:
   token is distributed as the target's p, estimated by Monte Carlo;
 * closed forms: draft equal to the target accepts everything; a one-hot
   draft is accepted with probability p(d) and its residual is p without d;
-* the inverse-CDF draw on hand-computed cases.
+* the inverse-CDF draw on hand-computed cases;
+* the decision margins (distance of each stochastic decision from its
+  boundary) on a hand-computed three-token case and an all-accepted case.
 """
 import json
 import os
@@ -148,3 +150,33 @@ def test_decision_margins_cover_every_decision():
     m = decision_margins(L, Q, d, u)
     n, _ = accept_sampled(L, Q, d, u)
     assert len(m) == min(n + 1, K) + 1 and all(x >= 0 for x in m)
+
+
+def _logits_of(probs):
+    return np.log(np.asarray(probs, dtype=np.float64))
+
+
+def test_decision_margins_hand_computed():
+    # V = 4, K = 3; probabilities chosen so every decision is worked by hand
+    p = [[0.4, 0.3, 0.2, 0.1],      # row 0: d = 0, alpha = min(1, 0.4 / 0.25) = 1
+         [0.1, 0.2, 0.3, 0.4],      # row 1: d = 0, alpha = 0.1 / 0.5 = 0.2
+         [0.25, 0.25, 0.25, 0.25],  # row 2: d = 1, alpha = 0.25 / 0.6 = 5/12
+         [0.7, 0.1, 0.1, 0.1]]      # row 3: only drawn from when all three are kept
+    q = [[0.25, 0.25, 0.25, 0.25],
+         [0.5, 0.2, 0.2, 0.1],
+         [0.1, 0.6, 0.2, 0.1]]
+    d = [0, 0, 1]
+    # u0 = 0.3 < 1 kept (margin 0.7); u1 = 0.15 < 0.2 kept (0.05); u2 = 0.5 >= 5/12
+    # rejected (1/12).  Residual of row 2: max(0, p - q) = [0.15, 0, 0.05, 0.15],
+    # total 0.35, cumulative [0.15, 0.15, 0.20, 0.35]; u3 * total = 0.21, nearest
+    # cumulative sum 0.20: margin 0.01 / 0.35.
+    u = [0.3, 0.15, 0.5, 0.6]
+    m = decision_margins(_logits_of(p), _logits_of(q), d, u)
+    assert accept_sampled(_logits_of(p), _logits_of(q), d, u) == (2, 3)
+    assert np.allclose(m, [0.7, 0.05, 1.0 / 12.0, 0.01 / 0.35], rtol=1e-12, atol=1e-13), m
+    # all three kept: the final draw is from row 3, cumulative [0.7, 0.8, 0.9, 1.0];
+    # u3 = 0.84 lands 0.04 from 0.8 (total 1)
+    u = [0.3, 0.15, 0.4, 0.84]
+    m = decision_margins(_logits_of(p), _logits_of(q), d, u)
+    assert accept_sampled(_logits_of(p), _logits_of(q), d, u) == (3, 2)
+    assert np.allclose(m, [0.7, 0.05, 5.0 / 12.0 - 0.4, 0.04], rtol=1e-12, atol=1e-13), m

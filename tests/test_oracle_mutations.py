@@ -5,8 +5,10 @@ plausible wrong version -- a dropped zero-point term, a sign flip, nibbles in
 the wrong order or shifted by one, a wrong group index, the scale applied per
 column of the wrong group, a wrong bf16 decode, an absolute-value bound with
 a signed factor; in the acceptance step the wrong tie-break, draw, count,
-test or residual; in tree attention an ignored mask, a missing scale or a
-wrong head grouping -- and runs the pins against it until one fails.  The
+test or residual, and decision margins measured from the wrong boundary; in
+tree attention an ignored mask, a missing scale or a wrong head grouping, and a
+weight mass without the probabilities, with signed values or with
+unnormalised weights -- and runs the pins against it until one fails.  The
 steps are replaced where the pins look them up (``linear64`` finds its own
 steps in ``oracle.w4a16_ref`` at call time).  The unmodified oracles pass the
 same pins in their own modules.
@@ -190,6 +192,55 @@ def _tree_variant(kind, q, k_cache, v_cache, k_draft, v_draft, masks, scale=None
     return out
 
 
+def _mass_variant(kind, q, k_cache, v_cache, k_draft, v_draft, masks, scale=None):
+    q = np.asarray(q, dtype=np.float64)
+    kc, vc = np.asarray(k_cache, dtype=np.float64), np.asarray(v_cache, dtype=np.float64)
+    kd, vd = np.asarray(k_draft, dtype=np.float64), np.asarray(v_draft, dtype=np.float64)
+    M, Hq, D = q.shape
+    Hkv = kc.shape[1] if kc.shape[0] else kd.shape[1]
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((M, Hq, D))
+    for i in range(M):
+        vis = [j for j in range(M) if (int(masks[i]) >> j) & 1]
+        for h in range(Hq):
+            g = h // group
+            keys = np.concatenate([kc[:, g, :], kd[vis, g, :]], axis=0)
+            vals = np.concatenate([vc[:, g, :], vd[vis, g, :]], axis=0)
+            if keys.shape[0] == 0:
+                continue
+            s = keys @ q[i, h] * scale
+            p = np.exp(s - s.max())
+            if kind == "sum |v| without p":
+                out[i, h] = np.abs(vals).sum(axis=0)
+            elif kind == "signed v":
+                out[i, h] = (p / p.sum()) @ vals
+            else:  # unnormalised weights
+                out[i, h] = p @ np.abs(vals)
+    return out
+
+
+def _margins_variant(kind, target_logits, draft_logits, draft_tokens, u):
+    p, q = acc.softmax64(target_logits), acc.softmax64(draft_logits)
+    K = len(draft_tokens)
+    out, row = [], None
+    for j in range(K):
+        d = int(draft_tokens[j])
+        ratio = 1.0 if q[j, d] == 0.0 else p[j, d] / q[j, d]
+        alpha = min(1.0, ratio)
+        out.append(abs(u[j] - (ratio if kind == "uncapped ratio" else alpha)))
+        if not u[j] < alpha:
+            row = p[j] if kind == "target row" else np.maximum(p[j] - q[j], 0.0)
+            break
+    if row is None:
+        row = p[K]
+    c = np.cumsum(row)
+    v = u[K] if kind == "u, not u * total" else u[K] * c[-1]
+    out.append(float(np.min(np.abs(c - v)) / c[-1]))
+    return out
+
+
 # (module the pins look the name up in, name, mutant)
 MUTANTS_F = {
     "greedy: last index of equal maxima": [(acc, "argmax_first", _argmax_last),
@@ -210,6 +261,17 @@ MUTANTS_F = {
                                   functools.partial(_tree_variant, "no 1/sqrt(d) scale"))],
     "tree: head h reads h % Hkv": [(tree_pins, "tree_attention",
                                     functools.partial(_tree_variant, "head h reads h % Hkv"))],
+    "mass: sum |v| without p": [(tree_pins, "attention_weight_mass",
+                                 functools.partial(_mass_variant, "sum |v| without p"))],
+    "mass: signed v": [(tree_pins, "attention_weight_mass", functools.partial(_mass_variant, "signed v"))],
+    "mass: unnormalised weights": [(tree_pins, "attention_weight_mass",
+                                    functools.partial(_mass_variant, "unnormalised weights"))],
+    "margins: test measured from p/q, not min(1, p/q)": [
+        (accept_pins, "decision_margins", functools.partial(_margins_variant, "uncapped ratio"))],
+    "margins: final draw measured from u, not u * total": [
+        (accept_pins, "decision_margins", functools.partial(_margins_variant, "u, not u * total"))],
+    "margins: final draw on the target row, not the residual": [
+        (accept_pins, "decision_margins", functools.partial(_margins_variant, "target row"))],
 }
 
 PINS_F = [
@@ -226,6 +288,9 @@ PINS_F = [
     functools.partial(tree_pins.test_tree_equals_each_path_as_a_sequence, 3),
     tree_pins.test_one_visible_key_and_identical_keys,
     tree_pins.test_invariances_and_head_grouping,
+    functools.partial(tree_pins.test_weight_mass_brute_force, 0),
+    tree_pins.test_weight_mass_closed_forms,
+    accept_pins.test_decision_margins_hand_computed,
 ]
 
 

@@ -9,14 +9,18 @@ that the pages and the mathematics fix, not to its own formula:
   the visible values;
 * invariants: a shift of every key by the same vector, and a permutation of
   the prefix, leave the output unchanged; query heads read the key/value head
-  h // (Hq / Hkv).
+  h // (Hq / Hkv);
+* the weight mass sum_k p_k |v_k| (the tolerance scale of the GPU checks):
+  against a brute-force loop, one visible key (= |v|), identical keys (= the
+  mean of |v|), non-negative values (= the attention output itself) and the
+  triangle inequality |output| <= mass.
 """
 import math
 
 import numpy as np
 import pytest
 
-from oracle import ancestor_masks, tree_attention
+from oracle import ancestor_masks, attention_weight_mass, tree_attention
 
 
 def test_ancestor_masks_of_hand_built_trees():
@@ -105,3 +109,67 @@ def test_invariances_and_head_grouping():
     out = tree_attention(q2, kc, vc, kd, vd, masks)
     assert np.allclose(out[:, 1], out[:, 0]) and np.allclose(out[:, 3], out[:, 0])
     assert not np.allclose(out[:, 4], out[:, 0])
+
+
+def _brute_path_mass(q, keys, vals, scale):
+    s = [scale * sum(a * b for a, b in zip(k, q)) for k in keys]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    z = sum(w)
+    return [sum(wi * abs(v[d]) for wi, v in zip(w, vals)) / z for d in range(len(vals[0]))]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_weight_mass_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    M, L, Hq, Hkv, D = 6, 4, 4, 2, 8
+    parents = [-1] + [int(rng.integers(-1, i)) for i in range(1, M)]
+    masks = ancestor_masks(parents)
+    q, kc, vc, kd, vd = _rand(rng, M, L, Hq, Hkv, D)
+    mass = attention_weight_mass(q, kc, vc, kd, vd, masks)
+    for i in range(M):
+        vis = [j for j in range(M) if (int(masks[i]) >> j) & 1]
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            keys = [list(kc[t, g]) for t in range(L)] + [list(kd[t, g]) for t in vis]
+            vals = [list(vc[t, g]) for t in range(L)] + [list(vd[t, g]) for t in vis]
+            exp = _brute_path_mass(list(q[i, h]), keys, vals, 1 / math.sqrt(D))
+            assert np.allclose(mass[i, h], exp, rtol=1e-12, atol=1e-12)
+
+
+def test_weight_mass_closed_forms():
+    rng = np.random.default_rng(7)
+    M, Hq, Hkv, D = 5, 4, 2, 8
+    q, _, _, kd, vd = _rand(rng, M, 0, Hq, Hkv, D)
+    empty = np.zeros((0, Hkv, D))
+    # one visible key (each token sees only itself, no prefix): the mass is |v|
+    mass = attention_weight_mass(q, empty, empty, kd, vd, ancestor_masks([-1] * M))
+    for i in range(M):
+        for h in range(Hq):
+            assert np.array_equal(mass[i, h], np.abs(vd[i, h // 2]))
+    # identical keys: every visible key has weight 1/n, the mass is the mean of |v|
+    L = 6
+    kc = np.ones((L, Hkv, D))
+    vc = rng.normal(size=(L, Hkv, D))
+    kd1 = np.ones((M, Hkv, D))
+    masks = ancestor_masks([-1, 0, 1, 1, 3])
+    mass = attention_weight_mass(q, kc, vc, kd1, vd, masks)
+    for i in range(M):
+        vis = [j for j in range(M) if (int(masks[i]) >> j) & 1]
+        for h in range(Hq):
+            g = h // 2
+            mean_abs = (np.abs(vc[:, g]).sum(0) + np.abs(vd[vis, g]).sum(0)) / (L + len(vis))
+            assert np.allclose(mass[i, h], mean_abs, rtol=1e-12, atol=1e-12)
+    # random keys: |output| <= mass, with equality when every value is >= 0
+    q, kc, vc, kd, vd = _rand(rng, M, 7, Hq, Hkv, D)
+    masks = ancestor_masks([-1, 0, 0, 2, 1])
+    out = tree_attention(q, kc, vc, kd, vd, masks)
+    mass = attention_weight_mass(q, kc, vc, kd, vd, masks)
+    assert np.all(np.abs(out) <= mass * (1 + 1e-12) + 1e-15)
+    assert np.any(np.abs(out) < 0.5 * mass)  # signed values cancel; the mass does not
+    out_pos = tree_attention(q, kc, np.abs(vc), kd, np.abs(vd), masks)
+    mass_pos = attention_weight_mass(q, kc, np.abs(vc), kd, np.abs(vd), masks)
+    assert np.allclose(out_pos, mass_pos, rtol=1e-12, atol=1e-14)
+    # a token that sees nothing has zero mass
+    mass0 = attention_weight_mass(q[:1], empty, empty, kd[:1], vd[:1], np.zeros(1, dtype=np.uint64))
+    assert np.array_equal(mass0, np.zeros_like(mass0))
