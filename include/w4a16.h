@@ -86,7 +86,8 @@ int w4_repacked_sizes(int N, int K, int group, size_t* qweight_bytes, size_t* sc
  * 64 columns, KB = K/32 k-blocks, G = K/128 groups:
  *   qweight_t uint32 [NC][KB][64 lanes][4]: word (c, kb, l, j) holds the 8
  *     codes of column 64c + 16j + (l % 16), k = 32kb + 8(l / 16) + e,
- *     e = 0..7, code e at nibble e/2 (e even) or 4 + (e-1)/2 (e odd);
+ *     e = 0..7, code e at nibble e/2 (e even) or 4 + (e-1)/2 (e odd), the
+ *     word then rotated left by 3 bits;
  *   scales_t uint16 [NC][G][16][4]: s[G][64c + 16j + t] at (c, G, t, j);
  *   zeros_t  uint16 [NC][G][16]: nibble j of (c, G, t) is z[G][64c + 16j + t].
  * Not in place; outputs must not overlap inputs.  Stateless. */

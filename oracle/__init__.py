@@ -11,6 +11,7 @@ from .w4a16_ref import (  # noqa: F401
     dequant64,
     linear64,
     linear64_columns,
+    linear64_gemm,
     round_to_bf16,
     scales_to_f64,
     unpack_qweight,

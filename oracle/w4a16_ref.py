@@ -111,6 +111,17 @@ def linear64_columns(x_bits, qweight, scales, zeros, group: int, n0: int, n1: in
     return _rows(x_bits, W64)
 
 
+def linear64_gemm(x_bits, qweight, scales, zeros, group: int, n0: int, n1: int):
+    """O6 over output columns [n0, n1) (8-aligned) as two matrix products,
+    Y64 = X64 @ W64 and A64 = |X64| @ |W64| (float64 BLAS), for checks at full
+    width where the row-by-row form would read every weight once per row.
+    The same definition as ``linear64``; only the float64 summation order
+    differs (within K * 2**-52 * A64 of it, pinned in tests)."""
+    W64 = _weights64(qweight, scales, zeros, group, n0, n1)
+    X64 = bf16_bits_to_f64(np.atleast_2d(x_bits))
+    return X64 @ W64, np.abs(X64) @ np.abs(W64)
+
+
 def _rows(x_bits, W64):
     X64 = bf16_bits_to_f64(np.atleast_2d(x_bits))
     M = X64.shape[0]

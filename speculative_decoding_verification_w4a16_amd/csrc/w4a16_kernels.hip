@@ -16,11 +16,16 @@
 // v_mfma_f32_16x16x32_bf16 for n-tile j, so one 128-bit load feeds four
 // MFMAs that share one A operand (the activation tile).
 //
-// Exact operands.  Code e sits at nibble e/2 (even e) or 4 + (e-1)/2 (odd e),
-// so  (word >> 4d) & 0x000F000F | 0x43004300  is the bf16 pair
-// (128 + q[2d], 128 + q[2d+1]) -- exact integers in bf16.  The kernels
-// accumulate x . (128 + q) per group in fp32 and subtract (128 + z) * sum(x)
-// per group before the fp32 group scale, so no weight is ever rounded.
+// Exact operands.  Code e sits at nibble e/2 (even e) or 4 + (e-1)/2 (odd e)
+// and the word is stored rotated left by 3 bits, so that
+//     rotr(word, 4d) & 0x00780078 | 0x41804180
+// is the bf16 pair (16 + q[2d], 16 + q[2d+1]): each code lands in the top
+// four mantissa bits of a bf16 whose exponent is that of 16.0, a step of
+// exactly 1.  The kernels accumulate x . (16 + q) per group in fp32 and
+// subtract (16 + z) * sum(x) per group before the fp32 group scale, so no
+// weight is ever rounded.  The bias (16, the smallest a 4-bit code in a
+// 7-bit bf16 mantissa allows) is what the subtraction cancels: the fp32
+// partial sums carry about (16 + q) * sum|x| instead of |x . (q - z)|.
 #include "w4_internal.h"
 
 #include <algorithm>
@@ -47,17 +52,19 @@ __device__ __forceinline__ uint32_t to_vgpr(uint32_t s) {
     return v;
 }
 
-// 8 packed codes -> 4 bf16 pairs (128 + q): dword d holds k offsets 2d, 2d+1.
-// `mask` (0x000F000F) and `magic` (0x43004300) arrive as kernel arguments so
-// that the compiler keeps them in registers and forms one v_and_or_b32 per
-// pair (with literal constants it emits a separate AND and OR).  Plain C, not
-// inline asm, so the compiler's MFMA operand hazard checks see every write.
+// 8 packed codes -> 4 bf16 pairs (16 + q): dword d holds k offsets 2d, 2d+1.
+// One v_alignbit_b32 (a rotate) and one v_and_or_b32 per pair, 7 VALU ops
+// per word.  `mask` (0x00780078) and `magic` (0x41804180) arrive as kernel
+// arguments so that the compiler keeps them in registers and forms one
+// v_and_or_b32 per pair (with literal constants it emits a separate AND and
+// OR).  Plain C, not inline asm, so the compiler's MFMA operand hazard checks
+// see every write.
 __device__ __forceinline__ u32x4 unpack_biased(uint32_t w, uint32_t mask, uint32_t magic) {
     u32x4 r;
     r[0] = (w & mask) | magic;
-    r[1] = ((w >> 4) & mask) | magic;
-    r[2] = ((w >> 8) & mask) | magic;
-    r[3] = ((w >> 12) & mask) | magic;
+    r[1] = (__builtin_amdgcn_alignbit(w, w, 4) & mask) | magic;
+    r[2] = (__builtin_amdgcn_alignbit(w, w, 8) & mask) | magic;
+    r[3] = (__builtin_amdgcn_alignbit(w, w, 12) & mask) | magic;
     return r;
 }
 
@@ -67,9 +74,12 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// 128 + z for nibble j of a packed zero word, exact in fp32.
+// The bias of the unpacked operands (bf16 16 + q).
+constexpr float kCodeBias = 16.0f;
+
+// 16 + z for nibble j of a packed zero word, exact in fp32.
 __device__ __forceinline__ float biased_zero(uint32_t zw, int j) {
-    return (float)(128u + ((zw >> (4 * j)) & 15u));
+    return (float)(16u + ((zw >> (4 * j)) & 15u));
 }
 
 // a . b + acc over one bf16 pair each, fp32 accumulation (v_dot2_f32_bf16).
@@ -85,7 +95,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
 // ---------------------------------------------------------------------------
 
 // Moves canonical nibble e (k offset e) to tile nibble e/2 (even e) or
-// 4 + (e-1)/2 (odd e).
+// 4 + (e-1)/2 (odd e), then rotates the word left by 3 bits (see
+// unpack_biased).
 __device__ __forceinline__ uint32_t to_tile_nibbles(uint32_t w) {
     uint32_t out = 0;
 #pragma unroll
@@ -93,7 +104,7 @@ __device__ __forceinline__ uint32_t to_tile_nibbles(uint32_t w) {
         const int p = (e & 1) ? 4 + (e >> 1) : (e >> 1);
         out |= ((w >> (4 * e)) & 15u) << (4 * p);
     }
-    return out;
+    return (out << 3) | (out >> 29);
 }
 
 // One thread per tile word.  Thread order (c, kb, o, j, t) keeps canonical
@@ -165,8 +176,8 @@ __global__ void unpack_qweight_kernel(const uint32_t* __restrict__ qt, int N, in
         const size_t k0 = (size_t)kb * kKBlock + 8 * (lane >> 4);
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const float lo = bf16_bits_to_f32(b[d] & 0xFFFFu) - 128.0f;
-            const float hi = bf16_bits_to_f32(b[d] >> 16) - 128.0f;
+            const float lo = bf16_bits_to_f32(b[d] & 0xFFFFu) - kCodeBias;
+            const float hi = bf16_bits_to_f32(b[d] >> 16) - kCodeBias;
             q_out[(k0 + 2 * d) * N + n] = (uint8_t)lo;
             q_out[(k0 + 2 * d + 1) * N + n] = (uint8_t)hi;
         }
@@ -186,7 +197,7 @@ __global__ void unpack_zeros_kernel(const uint16_t* __restrict__ zt, int N, int 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const size_t n = c * kChunkN + 16 * j + t;
-            if (n < (size_t)N) z_out[(size_t)g * N + n] = (uint8_t)(biased_zero(zw, j) - 128.0f);
+            if (n < (size_t)N) z_out[(size_t)g * N + n] = (uint8_t)(biased_zero(zw, j) - kCodeBias);
         }
     }
 }
@@ -208,8 +219,8 @@ struct LinearArgs {
     int gps, splits, ntiles;
     int kw;          // waves of a workgroup that split one chunk's K range (1: one chunk per wave)
     int rs;          // row slices of the LDS kernel (workgroups along M, 16 MB rows each)
-    uint32_t mask;   // 0x000F000F (see unpack_biased)
-    uint32_t magic;  // 0x43004300: bf16 128.0 in both halves
+    uint32_t mask;   // 0x00780078 (see unpack_biased)
+    uint32_t magic;  // 0x41804180: bf16 16.0 in both halves
 };
 
 // fp32 -> bf16, round to nearest, ties to even (NaN stays a quiet NaN).
@@ -1073,8 +1084,8 @@ hipError_t set_kernel_attributes() {
     return hipSuccess;
 }
 
-static constexpr uint32_t kNibbleMask = 0x000F000Fu;
-static constexpr uint32_t kBiasMagic = 0x43004300u;
+static constexpr uint32_t kNibbleMask = 0x00780078u;
+static constexpr uint32_t kBiasMagic = 0x41804180u;
 
 static int grid_for(size_t total, int block) {
     size_t g = (total + block - 1) / block;

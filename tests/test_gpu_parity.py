@@ -47,7 +47,7 @@ def _layout_words(qweight, N, K):
                         for e in range(8):
                             p = e // 2 if e % 2 == 0 else 4 + (e - 1) // 2
                             word |= int(q[32 * kb + 8 * o + e, n]) << (4 * p)
-                        out[c, kb, 16 * o + t, j] = word
+                        out[c, kb, 16 * o + t, j] = ((word << 3) | (word >> 29)) & 0xFFFFFFFF
     return out.reshape(-1)
 
 
@@ -188,28 +188,32 @@ def test_determinism_and_row_independence():
 
 
 @pytest.mark.parametrize("M", [1, 5, 16, 40, 64])
-def test_verify_pass_equals_separate_calls(M):
+def test_verify_pass_against_the_oracle(M):
     # every kernel path in one pass: the GEMV (M = 1), the streaming MFMA
     # kernel, the one-row-block LDS kernel (M = 16 on the 4096-column linear),
-    # row slices (M > 16 on the narrow ones) and the full LDS kernel
+    # row slices (M > 16 on the narrow ones) and the full LDS kernel; every
+    # output against the oracle, and bit for bit against separate calls
     shapes = [(256, 512), (1024, 512), (512, 1024), (4096, 512)]
     if M == 16:
         assert w4.w4a16_plan(M, 4096, 512)["lds"] > 0 and w4.w4a16_plan(M, 1024, 512)["lds"] == 0
     lins, descs, ys = [], [], []
-    xs = {}
+    xs, xh = {}, {}
     for i, (N, K) in enumerate(shapes):
         lin = synth.gen_linear(90 + i, N, K)
         pk = packed(lin, N, K)
         if K not in xs:
-            xs[K] = to_dev(synth.gen_x(M, K, seed_base=950 + K))
-        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
-        lins.append((pk, xs[K]))
+            xh[K] = synth.gen_x(M, K, seed_base=950 + K)
+            xs[K] = to_dev(xh[K])
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        lins.append((lin, pk, K))
         descs.append(dict(x=xs[K], qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t, y=y, N=N, K=K))
         ys.append(y)
     w4.w4a16_verify_pass(descs, M)
     torch.cuda.synchronize()
-    for (pk, x), y in zip(lins, ys):
-        ref = w4.linear(x, pk)
+    for (lin, pk, K), y in zip(lins, ys):
+        Y, A = linear64(xh[K], lin["qweight"], lin["scales"], lin["zeros"])
+        _check(y.cpu().numpy(), Y, A, ("verify pass", M, pk.N, K))
+        ref = w4.linear(xs[K], pk)
         torch.cuda.synchronize()
         assert torch.equal(ref, y)
 

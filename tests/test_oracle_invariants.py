@@ -57,3 +57,33 @@ def test_column_slice_matches_full():
     Y, A = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
     Ys, As = linear64_columns(x, lin["qweight"], lin["scales"], lin["zeros"], 128, 40, 96)
     assert np.array_equal(Ys, Y[:, 40:96]) and np.array_equal(As, A[:, 40:96])
+
+
+def test_matrix_product_form_matches_rows_and_the_exact_sum():
+    # linear64_gemm is O6 as one matrix product per column block: the same
+    # definition as linear64 in another float64 summation order.  Checked
+    # against the row-by-row form and against the correctly rounded exact
+    # sum (math.fsum of the exact products) within K * 2**-52 * A64, and exact
+    # on one-hot rows (one nonzero product per element).
+    import math
+
+    from oracle import linear64_gemm
+
+    lin, x = _case(seed=5, M=5, K=384, N=64)
+    K = 384
+    Y, A = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+    Yg, Ag = linear64_gemm(x, lin["qweight"], lin["scales"], lin["zeros"], 128, 0, 64)
+    bound = K * 2.0 ** -52 * A
+    assert np.all(np.abs(Yg - Y) <= bound) and np.all(np.abs(Ag - A) <= K * 2.0 ** -52 * A)
+    W64 = _weights64(lin["qweight"], lin["scales"], lin["zeros"], 128)
+    X64 = bf16_bits_to_f64(x)
+    for m in range(5):
+        for n in range(0, 64, 7):
+            exact = math.fsum(float(X64[m, k]) * float(W64[k, n]) for k in range(K))
+            assert abs(Yg[m, n] - exact) <= K * 2.0 ** -53 * A[m, n]
+    # a column block is the same block of the full product
+    Yb, Ab = linear64_gemm(x, lin["qweight"], lin["scales"], lin["zeros"], 128, 16, 48)
+    assert np.allclose(Yb, Yg[:, 16:48], rtol=0, atol=0) or np.all(np.abs(Yb - Yg[:, 16:48]) <= bound[:, 16:48])
+    e = synth.f32_to_bf16_bits(np.eye(K, dtype=np.float32)[[0, 7, 127, 128, 383]])
+    Ye, _ = linear64_gemm(e, lin["qweight"], lin["scales"], lin["zeros"], 128, 0, 64)
+    assert np.array_equal(Ye, W64[[0, 7, 127, 128, 383]])
