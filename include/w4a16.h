@@ -136,6 +136,24 @@ int w4a16_linear_out(const uint16_t* x, const uint32_t* qweight_t, const uint16_
                      const uint16_t* zeros_t, int M, int N, int K, int group, void* y, int out_dtype, int kernel,
                      int splits, void* stream);
 
+/* w4a16_linear_out for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, plans, kernels and result (bit for bit) as w4a16_linear_out,
+ * but the split-K partials go to a static device array of 64 MiB per GPU
+ * (W4_NOALLOC_SCRATCH_BYTES) that the library holds from module load until
+ * the process ends, instead of the lazily allocated workspace: the call
+ * makes no hipMalloc, hipFree or other allocating call.  The first call on
+ * a device looks the array's address up (hipGetSymbolAddress) and keeps it.
+ * A forced `splits` whose partials (splits * M * ceil(N/64)*64 fp32) would
+ * not fit the array returns W4_ERR_UNSUPPORTED; splits = 0 always fits.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one device (different streams) race and may return wrong results.  The
+ * array needs no clearing (every partial a call reads, it first writes). */
+#define W4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int w4a16_linear_out_noalloc(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                             const uint16_t* zeros_t, int M, int N, int K, int group, void* y, int out_dtype,
+                             int kernel, int splits, void* stream);
+
 /* w4a16_linear_out with the work decomposition of the M <= 16 kernels
  * forced as well, for tests and tuning sweeps.  kwaves: 0 = automatic (at
  * M = 15, 16 with N >= 4096 the LDS-ring kernel of M > 16, one chunk per

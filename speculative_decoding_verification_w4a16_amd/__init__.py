@@ -62,6 +62,8 @@ _c = {
     "w4a16_linear": _sig("w4a16_linear", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "w4a16_linear_cfg": _sig("w4a16_linear_cfg", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _vp]),
     "w4a16_linear_out": _sig("w4a16_linear_out", [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp]),
+    "w4a16_linear_out_noalloc": _sig("w4a16_linear_out_noalloc",
+                                     [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _vp]),
     "w4a16_linear_tune": _sig("w4a16_linear_tune",
                               [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _vp]),
     "w4a16_plan": _sig("w4a16_plan", [_i, _i, _i, _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 6),
@@ -161,6 +163,13 @@ def w4a16_linear_out(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dty
     st = _stream(stream, x, y)
     _check(_c["w4a16_linear_out"](_ptr(x), _ptr(qweight_t), _ptr(scales_t), _ptr(zeros_t), M, N, K, group, _ptr(y),
                                   out_dtype, kernel, splits, st), "w4a16_linear_out")
+
+
+def w4a16_linear_out_noalloc(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype=W4_OUT_F32,
+                             kernel=W4_KERNEL_AUTO, splits=0, stream=None):
+    st = _stream(stream, x, y)
+    _check(_c["w4a16_linear_out_noalloc"](_ptr(x), _ptr(qweight_t), _ptr(scales_t), _ptr(zeros_t), M, N, K, group,
+                                          _ptr(y), out_dtype, kernel, splits, st), "w4a16_linear_out_noalloc")
 
 
 def w4a16_linear_tune(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype=W4_OUT_F32,

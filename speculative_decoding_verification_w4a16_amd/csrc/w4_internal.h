@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/w4a16.h"
+
 namespace w4 {
 
 constexpr int kChunkN = 64;   // output columns per chunk (4 MFMA n-tiles of 16)
@@ -48,6 +50,15 @@ constexpr int kLdsLimit = 160 * 1024 - 256;  // room for the small static LDS
 
 // Split-K workspace size (per device).
 constexpr size_t kWorkspaceBytes = size_t(64) << 20;
+
+// The allocation-free entry point's static split-K scratch (per device, the
+// same size as the workspace, so both plan every call alike).
+constexpr size_t kNoAllocScratchBytes = kWorkspaceBytes;
+static_assert(kNoAllocScratchBytes == W4_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+
+// Device address of the current device's static scratch (looked up once per
+// device with hipGetSymbolAddress; no allocation).
+hipError_t noalloc_scratch(Workspace* ws);
 
 // kwaves: 0 = the planner's choice, else 1, 2, 4 or 8 (M <= 16 only; the
 // M > 16 kernel always uses 1).  Returns non-zero for an impossible request.

@@ -132,6 +132,11 @@ int check_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, cons
     return W4_OK;
 }
 
+// The split-K partials' bytes of a plan.
+size_t partial_bytes(const w4::Plan& plan, int M, int N) {
+    return plan.splits > 1 ? (size_t)plan.splits * M * chunks(N) * w4::kChunkN * sizeof(float) : 0;
+}
+
 int run_linear(const uint16_t* x, const uint32_t* qt, const uint16_t* st, const uint16_t* zt, int M, int N, int K,
                void* y, int out_dtype, const w4::Plan& plan, hipStream_t stream) {
     if (M == 0 || N == 0) return W4_OK;
@@ -218,6 +223,33 @@ int w4a16_linear_out(const uint16_t* x, const uint32_t* qweight_t, const uint16_
                      int splits, void* stream) {
     return w4a16_linear_tune(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype, kernel, splits, 0,
                              stream);
+}
+
+int w4a16_linear_out_noalloc(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                             const uint16_t* zeros_t, int M, int N, int K, int group, void* y, int out_dtype,
+                             int kernel, int splits, void* stream) {
+    w4::Plan plan{};
+    int rc = check_linear(x, qweight_t, scales_t, zeros_t, M, N, K, group, y, out_dtype, kernel, splits, 0, &plan);
+    if (rc != W4_OK) return rc;
+    if (M == 0 || N == 0) return W4_OK;
+    // a forced split count whose partials would not fit the scratch is
+    // refused (the planner would otherwise lower it): the caller asked for a
+    // decomposition this entry point cannot hold
+    if (splits > 0 && plan.splits < std::min(splits, K / w4::kGroup) &&
+        (size_t)std::min(splits, K / w4::kGroup) * M * chunks(N) * w4::kChunkN * sizeof(float) >
+            w4::kNoAllocScratchBytes)
+        return W4_ERR_UNSUPPORTED;
+    if (partial_bytes(plan, M, N) > w4::kNoAllocScratchBytes) return W4_ERR_UNSUPPORTED;
+    if (K == 0) {
+        const size_t n = (size_t)M * N / (out_dtype == W4_OUT_BF16 ? 2 : 1);
+        return hip_status("zero_kernel launch", w4::launch_zero((float*)y, n, (hipStream_t)stream));
+    }
+    w4::Workspace ws{};
+    hipError_t e = w4::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+    return hip_status("verify-linear launch", w4::launch_linear(plan, x, qweight_t, scales_t, zeros_t, M, N, K, y,
+                                                                out_dtype == W4_OUT_BF16, ws,
+                                                                (hipStream_t)stream));
 }
 
 int w4a16_linear_cfg(const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,

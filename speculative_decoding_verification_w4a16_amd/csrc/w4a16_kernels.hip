@@ -30,6 +30,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -928,6 +929,38 @@ __global__ __launch_bounds__(256) void bench_copy_kernel(u32x4* __restrict__ dst
                                                          size_t n16) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// the allocation-free entry point's split-K scratch
+// ---------------------------------------------------------------------------
+//
+// A file-scope device array that every GPU running the library holds from
+// module load until the process ends.  In host code its name is only a
+// stand-in for the symbol: the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current
+// and kept per device; kernels receive that address, never the name.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(Workspace* ws) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDev] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    ws->partial = (float*)addr[dev];
+    ws->partial_bytes = kNoAllocScratchBytes;
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

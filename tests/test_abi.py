@@ -259,3 +259,18 @@ def test_size_limits():
             w4.w4a16_plan(1, N, K)
         rc = w4._c["w4a16_linear"](None, None, None, None, 1, N, K, 128, None, None)
         assert rc == w4.W4_ERR_UNSUPPORTED
+
+
+def test_noalloc_refuses_a_split_past_its_scratch_before_any_launch():
+    # 16 K splits of 64 x 128256 fp32 partials exceed the 64 MiB static
+    # scratch: refused on the host (no GPU needed); the same call without a
+    # forced split is accepted by validation (it would plan one split)
+    with pytest.raises(w4.W4Error) as err:
+        w4.w4a16_linear_out_noalloc(0x10000, 0x20000, 0x30000, 0x40000, 64, 128256, 8192, 128, 0x7000000000, 0, 0,
+                                    16, stream=0)
+    assert err.value.status == w4.W4_ERR_UNSUPPORTED
+    with pytest.raises(w4.W4Error) as err:  # misaligned y: rejected like w4a16_linear_out
+        w4.w4a16_linear_out_noalloc(0x10000, 0x20000, 0x30000, 0x40000, 4, 256, 512, 128, 0x7000000004, 0, 0, 0,
+                                    stream=0)
+    assert err.value.status == w4.W4_ERR_INVALID
+    assert w4.W4_OK == 0
