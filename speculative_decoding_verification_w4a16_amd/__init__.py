@@ -18,7 +18,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
-W4_OK, W4_ERR_INVALID, W4_ERR_UNSUPPORTED, W4_ERR_HIP = 0, 1, 2, 3
+W4_OK, W4_ERR_INVALID, W4_ERR_UNSUPPORTED, W4_ERR_HIP, W4_ERR_TIMEOUT = 0, 1, 2, 3, 4
+W4_PASS_MAX_DEPS = 4
 W4_KERNEL_AUTO, W4_KERNEL_GEMV, W4_KERNEL_MFMA = 0, 1, 2
 W4_OUT_F32, W4_OUT_BF16 = 0, 1
 GROUP = 128
@@ -45,6 +46,11 @@ class W4LinearDesc(ctypes.Structure):
                 ("K", _i)]
 
 
+class W4PassLinear(ctypes.Structure):
+    _fields_ = [("x", _vp), ("qweight_t", _vp), ("scales_t", _vp), ("zeros_t", _vp), ("y", _vp), ("y_bf16", _vp),
+                ("alpha", ctypes.c_float), ("N", _i), ("K", _i), ("ndeps", _i), ("deps", _i * 4)]
+
+
 def _sig(name, args, res=_i):
     f = getattr(_lib, name)
     f.argtypes = args
@@ -69,6 +75,12 @@ _c = {
     "w4a16_plan": _sig("w4a16_plan", [_i, _i, _i, _i, _i, _i, _i] + [ctypes.POINTER(_i)] * 6),
     "w4a16_verify_pass": _sig("w4a16_verify_pass", [ctypes.POINTER(W4LinearDesc), _i, _i, _i, _vp]),
     "w4_unpack": _sig("w4_unpack", [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "w4_pass_create": _sig("w4_pass_create", [ctypes.POINTER(W4PassLinear), _i, _i, _i, ctypes.POINTER(_vp)]),
+    "w4_pass_run": _sig("w4_pass_run", [_vp, _vp]),
+    "w4_pass_check": _sig("w4_pass_check", [_vp, _vp]),
+    "w4_pass_info": _sig("w4_pass_info", [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "w4_pass_set_spin_limit": _sig("w4_pass_set_spin_limit", [_vp, ctypes.c_uint32]),
+    "w4_pass_destroy": _sig("w4_pass_destroy", [_vp]),
     "w4_bench_read": _sig("w4_bench_read", [_vp, _sz, _vp, _vp]),
     "w4_bench_read_blocks": _sig("w4_bench_read_blocks", []),
     "w4_bench_copy": _sig("w4_bench_copy", [_vp, _vp, _sz, _vp]),
@@ -195,6 +207,58 @@ def w4a16_verify_pass(linears, M, group=GROUP, stream=None):
     first = linears[0]["y"] if linears else None
     st = _stream(stream, first)
     _check(_c["w4a16_verify_pass"](arr, len(linears), M, group, st), "w4a16_verify_pass")
+
+
+def w4_pass_create(linears, M, group=GROUP):
+    """`linears`: sequence of dicts with x, qweight_t, scales_t, zeros_t, y
+    (or None), y_bf16 (or None), N, K, and optionally alpha (1.0) and deps
+    (indices of earlier entries).  Returns the pass handle (an int)."""
+    n = len(linears)
+    arr = (W4PassLinear * max(1, n))()
+    for i, d in enumerate(linears):
+        deps = list(d.get("deps", ()))
+        arr[i] = W4PassLinear(_ptr(d["x"]), _ptr(d["qweight_t"]), _ptr(d["scales_t"]), _ptr(d["zeros_t"]),
+                              _ptr(d.get("y")), _ptr(d.get("y_bf16")), float(d.get("alpha", 1.0)), d["N"], d["K"],
+                              len(deps), (_i * 4)(*(deps + [0] * (4 - len(deps)))[:4]))
+    out = _vp()
+    _check(_c["w4_pass_create"](arr, n, M, group, ctypes.byref(out)), "w4_pass_create")
+    return out.value
+
+
+def w4_pass_run(handle, stream=None):
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(_c["w4_pass_run"](handle, stream), "w4_pass_run")
+
+
+def w4_pass_check(handle, stream=None):
+    """Synchronize `stream`; raise W4Error (W4_ERR_TIMEOUT) if a dependency
+    wait of the runs since the last check gave up."""
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(_c["w4_pass_check"](handle, stream), "w4_pass_check")
+
+
+def w4_pass_info(handle) -> dict:
+    outs = [_i() for _ in range(3)]
+    _check(_c["w4_pass_info"](handle, *[ctypes.byref(o) for o in outs]), "w4_pass_info")
+    return dict(zip(("persistent", "grid", "units"), (o.value for o in outs)))
+
+
+def w4_pass_set_spin_limit(handle, polls):
+    _check(_c["w4_pass_set_spin_limit"](handle, polls), "w4_pass_set_spin_limit")
+
+
+def w4_pass_destroy(handle):
+    _check(_c["w4_pass_destroy"](handle), "w4_pass_destroy")
 
 
 def w4_unpack(qweight_t, zeros_t, N, K, group, q_out, z_out, stream=None):

@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("w4a16_kernels.hip", "w4_accept.hip", "w4_tree_attn.hip", "w4a16_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("w4a16_kernels.hip", "w4_pass.hip", "w4_accept.hip", "w4_tree_attn.hip",
+                                          "w4a16_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

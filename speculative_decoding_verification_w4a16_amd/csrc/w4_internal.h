@@ -77,7 +77,44 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
                          const uint16_t* zeros_t, int M, int N, int K, void* y, int out_bf16, const Workspace& ws,
                          hipStream_t stream);
 
+// The same with both outputs optional (fp32 y and/or bf16 yb, at least one)
+// and the result scaled by alpha.
+hipError_t launch_linear_io(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                            const uint16_t* zeros_t, int M, int N, int K, float* y, uint16_t* yb, float alpha,
+                            const Workspace& ws, hipStream_t stream);
+
 hipError_t launch_zero(float* y, size_t n, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// the verify pass in one launch (w4_pass.hip), M <= kPassMaxM
+// ---------------------------------------------------------------------------
+constexpr int kPassMaxM = 16;
+constexpr int kPassWaves = 8;  // waves per workgroup
+constexpr int kPassRing = 4;   // groups of loads in flight per streaming wave
+constexpr int kPassMaxDeps = 4;
+
+// One linear of a pass, as the kernel reads it (device table).
+struct PassLinear {
+    const uint16_t* x;   // [M][K] bf16
+    const uint32_t* qt;  // tile layout (w4_repack)
+    const uint16_t* st;
+    const uint16_t* zt;
+    float* y;            // [M][N] fp32, or null
+    uint16_t* yb;        // [M][N] bf16, or null
+    float alpha;         // output scale
+    int N, K, NC, G;     // NC chunks of 64 columns, G groups of 128
+    int unit0;           // the pass's unit number of chunk 0
+    int kw;              // streaming waves with groups: min(kPassWaves, G)
+    int ndep;
+    int dep[kPassMaxDeps];        // producer linears
+    int dep_units[kPassMaxDeps];  // their unit (chunk) counts
+};
+
+hipError_t launch_pass(const PassLinear* tab, int n, int U, int M, uint32_t* done, uint32_t* state,
+                       uint32_t spin_limit, int grid, hipStream_t stream);
+
+// Workgroups of the pass kernel for M rows that fit one CU at once.
+hipError_t pass_occupancy(int M, int* per_cu);
 
 hipError_t launch_bench_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
 hipError_t launch_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

@@ -11,8 +11,11 @@
 #include <cmath>
 #include <cstdio>
 #include <mutex>
+#include <new>
+#include <vector>
 
 #include "../../include/w4_accept.h"
+#include "../../include/w4_pass.h"
 #include "../../include/w4_tree_attn.h"
 #include "../../include/w4a16.h"
 #include "../../include/w4a16_bench.h"
@@ -167,6 +170,7 @@ const char* w4_status_str(int status) {
         case W4_ERR_INVALID: return "W4_ERR_INVALID: invalid argument (null, negative, misaligned or overlapping)";
         case W4_ERR_UNSUPPORTED: return "W4_ERR_UNSUPPORTED: unsupported shape or group size";
         case W4_ERR_HIP: return "W4_ERR_HIP: a HIP runtime call failed";
+        case W4_ERR_TIMEOUT: return "W4_ERR_TIMEOUT: a verify pass waited too long for a producer (results invalid)";
         default: return "W4_ERR_UNKNOWN: unknown status code";
     }
 }
@@ -401,3 +405,257 @@ extern "C" int w4_tree_attention(const uint16_t* q, const uint16_t* k_cache, con
                       w4::launch_tree_attn(q, k_cache, v_cache, k_draft, v_draft, masks, M, L, num_heads,
                                            num_kv_heads, sc, out, ws, (hipStream_t)stream));
 }
+
+// ---------------------------------------------------------------------------
+// the verify pass as one launch (include/w4_pass.h)
+// ---------------------------------------------------------------------------
+
+struct w4_pass {
+    int device = 0;
+    int n = 0, M = 0, U = 0, grid = 0;
+    bool persistent = false;
+    w4::PassLinear* tab = nullptr;  // device table of the linears
+    uint32_t* counters = nullptr;   // device: [n] units done per linear, then exited workgroups, error flag
+    std::vector<w4_pass_linear> lin;
+    std::vector<w4::Plan> plans;    // per-linear launches (M > kPassMaxM)
+    w4::Workspace ws{};
+    uint32_t spin_limit = 1u << 24; // polls (each about 50 ns apart) before a wait gives up
+};
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+Range lines_of(Range r) { return Range{r.lo & ~(uintptr_t)127, (r.hi + 127) & ~(uintptr_t)127}; }
+bool meets(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+// Per-linear argument checks of a pass entry.
+int check_pass_linear(const w4_pass_linear& d, int i, int M, int group) {
+    if (d.N < 0 || d.K < 0 || d.ndeps < 0) return W4_ERR_INVALID;
+    int rc = check_shape(d.N, d.K, group);
+    if (rc != W4_OK) return rc;
+    if (d.N < 8 || d.K < w4::kGroup || d.ndeps > W4_PASS_MAX_DEPS) return W4_ERR_UNSUPPORTED;
+    if (!d.y && !d.y_bf16) return W4_ERR_INVALID;
+    if (!std::isfinite(d.alpha)) return W4_ERR_INVALID;
+    if ((d.y && !aligned(d.y, 128)) || (d.y_bf16 && !aligned(d.y_bf16, 128))) return W4_ERR_INVALID;
+    if (!aligned(d.zeros_t, 4)) return W4_ERR_INVALID;  // the pass kernel reads zero records in aligned pairs
+    for (int j = 0; j < d.ndeps; ++j) {
+        if (d.deps[j] < 0 || d.deps[j] >= i) return W4_ERR_INVALID;
+        for (int k = 0; k < j; ++k)
+            if (d.deps[k] == d.deps[j]) return W4_ERR_INVALID;
+    }
+    if (M == 0) return W4_OK;
+    if (d.y) {
+        rc = check_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, group, d.y, W4_OUT_F32,
+                          W4_KERNEL_AUTO, 0, 0, nullptr);
+        if (rc != W4_OK) return rc;
+    }
+    if (d.y_bf16) {
+        rc = check_linear(d.x, d.qweight_t, d.scales_t, d.zeros_t, M, d.N, d.K, group, d.y_bf16, W4_OUT_BF16,
+                          W4_KERNEL_AUTO, 0, 0, nullptr);
+        if (rc != W4_OK) return rc;
+    }
+    return W4_OK;
+}
+
+// Hazards between the linears of a pass (see w4_pass_create).
+int check_pass_hazards(const w4_pass_linear* L, int n, int M) {
+    std::vector<Range> xs(n), ws;
+    struct Out {
+        Range r;
+        int owner;
+    };
+    std::vector<Out> outs;
+    for (int i = 0; i < n; ++i) {
+        const w4_pass_linear& d = L[i];
+        size_t qb, sb, zb;
+        tile_sizes(d.N, d.K, &qb, &sb, &zb);
+        xs[i] = range_of(d.x, (size_t)M * d.K * 2);
+        ws.push_back(range_of(d.qweight_t, qb));
+        ws.push_back(range_of(d.scales_t, sb));
+        ws.push_back(range_of(d.zeros_t, zb));
+        if (d.y) outs.push_back(Out{range_of(d.y, (size_t)M * d.N * 4), i});
+        if (d.y_bf16) outs.push_back(Out{range_of(d.y_bf16, (size_t)M * d.N * 2), i});
+    }
+    for (size_t a = 0; a < outs.size(); ++a) {
+        const Range oa = outs[a].r, la = lines_of(oa);
+        const int j = outs[a].owner;
+        for (size_t b = a + 1; b < outs.size(); ++b)
+            if (meets(la, lines_of(outs[b].r))) return W4_ERR_INVALID;
+        for (const Range& w : ws)
+            if (meets(la, lines_of(w))) return W4_ERR_INVALID;
+        for (int i = 0; i < n; ++i) {
+            if (meets(oa, xs[i])) {
+                // linear i reads linear j's output: j must be earlier and a listed producer
+                if (i <= j) return W4_ERR_INVALID;
+                bool listed = false;
+                for (int k = 0; k < L[i].ndeps; ++k) listed = listed || L[i].deps[k] == j;
+                if (!listed) return W4_ERR_INVALID;
+            } else if (meets(la, lines_of(xs[i]))) {
+                return W4_ERR_INVALID;  // an unrelated input shares a cache line with the output
+            }
+        }
+    }
+    return W4_OK;
+}
+
+void pass_free(w4_pass* p) {
+    if (!p) return;
+    if (p->tab) (void)hipFree(p->tab);
+    if (p->counters) (void)hipFree(p->counters);
+    delete p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pass** out) {
+    if (!out) return W4_ERR_INVALID;
+    *out = nullptr;
+    if (n < 0 || M < 0 || (n > 0 && !linears)) return W4_ERR_INVALID;
+    if (group != w4::kGroup || M > W4_MAX_M || n > W4_PASS_MAX_LINEARS) return W4_ERR_UNSUPPORTED;
+    for (int i = 0; i < n; ++i) {
+        int rc = check_pass_linear(linears[i], i, M, group);
+        if (rc != W4_OK) return rc;
+    }
+    if (M > 0) {
+        int rc = check_pass_hazards(linears, n, M);
+        if (rc != W4_OK) return rc;
+    }
+    w4_pass* p = new (std::nothrow) w4_pass();
+    if (!p) return W4_ERR_HIP;
+    p->n = n;
+    p->M = M;
+    p->lin.assign(linears, linears + n);
+    p->persistent = M >= 1 && M <= w4::kPassMaxM;
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+        pass_free(p);
+        return hip_fail("hipGetDevice", e);
+    }
+    std::vector<w4::PassLinear> tab(n);
+    int U = 0;
+    for (int i = 0; i < n; ++i) {
+        const w4_pass_linear& d = linears[i];
+        w4::PassLinear& t = tab[i];
+        t.x = d.x;
+        t.qt = d.qweight_t;
+        t.st = d.scales_t;
+        t.zt = d.zeros_t;
+        t.y = d.y;
+        t.yb = d.y_bf16;
+        t.alpha = d.alpha;
+        t.N = d.N;
+        t.K = d.K;
+        t.NC = (int)chunks(d.N);
+        t.G = d.K / w4::kGroup;
+        t.unit0 = U;
+        t.kw = std::min(w4::kPassWaves, t.G);
+        t.ndep = d.ndeps;
+        for (int j = 0; j < w4::kPassMaxDeps; ++j) {
+            t.dep[j] = j < d.ndeps ? d.deps[j] : 0;
+            t.dep_units[j] = j < d.ndeps ? (int)chunks(linears[d.deps[j]].N) : 0;
+        }
+        U += t.NC;
+    }
+    p->U = U;
+    if (p->persistent && n > 0) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
+        if (e != hipSuccess) {
+            pass_free(p);
+            return hip_fail("hipDeviceGetAttribute", e);
+        }
+        int per_cu = 0;
+        e = w4::pass_occupancy(M, &per_cu);
+        if (e != hipSuccess || per_cu < 1) {
+            pass_free(p);
+            return hip_fail("pass occupancy", e != hipSuccess ? e : hipErrorInvalidConfiguration);
+        }
+        p->grid = std::max(1, std::min(U, cus));
+        e = hipMalloc((void**)&p->tab, sizeof(w4::PassLinear) * n);
+        if (e == hipSuccess) e = hipMalloc((void**)&p->counters, sizeof(uint32_t) * (n + 2));
+        if (e == hipSuccess) e = hipMemcpy(p->tab, tab.data(), sizeof(w4::PassLinear) * n, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemset(p->counters, 0, sizeof(uint32_t) * (n + 2));
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            pass_free(p);
+            return hip_fail("pass set-up", e);
+        }
+    } else if (M > 0) {
+        // per-linear launches: their plans, and the split-K workspace now
+        p->plans.resize(n);
+        for (int i = 0; i < n; ++i)
+            if (w4::plan_linear(M, linears[i].N, linears[i].K, W4_KERNEL_AUTO, 0, 0, w4::kWorkspaceBytes,
+                                &p->plans[i]) != 0) {
+                pass_free(p);
+                return W4_ERR_UNSUPPORTED;
+            }
+        int rc = device_state(&p->ws);
+        if (rc != W4_OK) {
+            pass_free(p);
+            return rc;
+        }
+    }
+    *out = p;
+    return W4_OK;
+}
+
+int w4_pass_run(w4_pass* p, void* stream) {
+    if (!p) return W4_ERR_INVALID;
+    if (p->M == 0 || p->n == 0) return W4_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    if (dev != p->device) return W4_ERR_INVALID;
+    if (p->persistent)
+        return hip_status("pass launch", w4::launch_pass(p->tab, p->n, p->U, p->M, p->counters, p->counters + p->n,
+                                                          p->spin_limit, p->grid, (hipStream_t)stream));
+    for (int i = 0; i < p->n; ++i) {
+        const w4_pass_linear& d = p->lin[i];
+        e = w4::launch_linear_io(p->plans[i], d.x, d.qweight_t, d.scales_t, d.zeros_t, p->M, d.N, d.K, d.y,
+                                 d.y_bf16, d.alpha, p->ws, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail("pass linear launch", e);
+    }
+    return W4_OK;
+}
+
+int w4_pass_check(w4_pass* p, void* stream) {
+    if (!p) return W4_ERR_INVALID;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("hipStreamSynchronize", e);
+    if (!p->persistent || !p->counters) return W4_OK;
+    uint32_t flag = 0;
+    e = hipMemcpy(&flag, p->counters + p->n + 1, sizeof(flag), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail("hipMemcpy(pass flag)", e);
+    if (flag == 0) return W4_OK;
+    e = hipMemset(p->counters + p->n + 1, 0, sizeof(uint32_t));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail("hipMemset(pass flag)", e);
+    return W4_ERR_TIMEOUT;
+}
+
+int w4_pass_info(const w4_pass* p, int* persistent, int* grid, int* units) {
+    if (!p) return W4_ERR_INVALID;
+    if (persistent) *persistent = p->persistent ? 1 : 0;
+    if (grid) *grid = p->grid;
+    if (units) *units = p->U;
+    return W4_OK;
+}
+
+int w4_pass_set_spin_limit(w4_pass* p, uint32_t polls) {
+    if (!p) return W4_ERR_INVALID;
+    p->spin_limit = polls;
+    return W4_OK;
+}
+
+int w4_pass_destroy(w4_pass* p) {
+    pass_free(p);
+    return W4_OK;
+}
+
+}  // extern "C"

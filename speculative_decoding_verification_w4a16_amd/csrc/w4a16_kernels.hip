@@ -27,69 +27,13 @@
 // 7-bit bf16 mantissa allows) is what the subtraction cancels: the fp32
 // partial sums carry about (16 + q) * sum|x| instead of |x . (q - z)|.
 #include "w4_internal.h"
+#include "w4_device.h"
 
 #include <algorithm>
 #include <cmath>
 #include <mutex>
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 namespace w4 {
-
-// ---------------------------------------------------------------------------
-// small device helpers
-// ---------------------------------------------------------------------------
-
-// A wave-uniform value copied into a VGPR (once, at kernel start).  With the
-// unpack mask in an SGPR and the magic value in a VGPR the compiler forms one
-// v_and_or_b32 per bf16 pair; with both in SGPRs it needs an AND and an OR
-// (a VALU op may read only one SGPR), and with literals it cannot fuse at all.
-__device__ __forceinline__ uint32_t to_vgpr(uint32_t s) {
-    uint32_t v;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
-    return v;
-}
-
-// 8 packed codes -> 4 bf16 pairs (16 + q): dword d holds k offsets 2d, 2d+1.
-// One v_alignbit_b32 (a rotate) and one v_and_or_b32 per pair, 7 VALU ops
-// per word.  `mask` (0x00780078) and `magic` (0x41804180) arrive as kernel
-// arguments so that the compiler keeps them in registers and forms one
-// v_and_or_b32 per pair (with literal constants it emits a separate AND and
-// OR).  Plain C, not inline asm, so the compiler's MFMA operand hazard checks
-// see every write.
-__device__ __forceinline__ u32x4 unpack_biased(uint32_t w, uint32_t mask, uint32_t magic) {
-    u32x4 r;
-    r[0] = (w & mask) | magic;
-    r[1] = (__builtin_amdgcn_alignbit(w, w, 4) & mask) | magic;
-    r[2] = (__builtin_amdgcn_alignbit(w, w, 8) & mask) | magic;
-    r[3] = (__builtin_amdgcn_alignbit(w, w, 12) & mask) | magic;
-    return r;
-}
-
-__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-// The bias of the unpacked operands (bf16 16 + q).
-constexpr float kCodeBias = 16.0f;
-
-// 16 + z for nibble j of a packed zero word, exact in fp32.
-__device__ __forceinline__ float biased_zero(uint32_t zw, int j) {
-    return (float)(16u + ((zw >> (4 * j)) & 15u));
-}
-
-// a . b + acc over one bf16 pair each, fp32 accumulation (v_dot2_f32_bf16).
-// Arguments are plain dwords: hipcc miscompiles __builtin_bit_cast applied
-// directly to an element of an ext_vector (it reads element 0), so vector
-// elements are always copied into a scalar first.
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
-}
 
 // ---------------------------------------------------------------------------
 // repack: canonical -> tile layout (offline, not timed)
@@ -212,8 +156,9 @@ struct LinearArgs {
     const u32x4* qt;
     const uint2* st;
     const uint16_t* zt;
-    float* y;        // fp32 output, or
+    float* y;        // fp32 output when not null, and/or
     uint16_t* yb;    // bf16 output (round to nearest even) when not null
+    float alpha;     // output scale (1 for the plain linear)
     float* ws;
     int M, N, K;
     int NC, KB, G;
@@ -224,52 +169,13 @@ struct LinearArgs {
     uint32_t magic;  // 0x41804180: bf16 16.0 in both halves
 };
 
-// fp32 -> bf16, round to nearest, ties to even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-// Final value of y[i] (unsplit K): fp32, or bf16 for the bf16 epilogue.
+// Final value of y[i] (unsplit K), scaled by alpha: fp32 and/or bf16 (the
+// bf16 epilogue).  alpha = 1 leaves every value's bits unchanged.
 __device__ __forceinline__ void store_y(const LinearArgs& a, size_t i, float v) {
-    if (a.yb)
-        a.yb[i] = f32_to_bf16_rne(v);
-    else
-        a.y[i] = v;
+    v *= a.alpha;
+    if (a.y) a.y[i] = v;
+    if (a.yb) a.yb[i] = f32_to_bf16_rne(v);
 }
-
-// Workgroup barrier for an LDS producer/consumer hand-off.  It waits for this
-// wave's LDS operations only: __syncthreads() also waits for every
-// outstanding global load, which would drain the weight ring at each stage.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Split-K partial sums travel through device memory with agent-scope (sc1)
-// stores and loads, which are made visible at, and read from, the device
-// coherence point directly.  No L2 write-back or invalidate is needed; those
-// (what __threadfence() emits) serialise per XCD and cost far more than the
-// kernel itself when every workgroup issues them.
-__device__ __forceinline__ void store_partial(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Non-temporal loads for the streaming kernels (M <= 16).  Every packed
-// weight, scale and zero byte is read once per call, while the activation
-// rows are re-read by every wave from L2; marking the one-pass stream
-// non-temporal keeps it from evicting them.  Measured on MI355X: 5-12 % off
-// the M = 1 and M = 5 linears (lm_head at M = 1: 101 -> 89 us).  The LDS-ring
-// kernel keeps ordinary loads (no gain there: its activations sit in LDS, and
-// its row slices re-read a tile's weights from L2).
-__device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ uint2 load_stream(const uint2* p) {
-    const uint64_t v = __builtin_nontemporal_load((const uint64_t*)p);
-    return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
-}
-__device__ __forceinline__ uint32_t load_stream(const uint16_t* p) { return __builtin_nontemporal_load(p); }
 
 // Weight ring.  A wave keeps kRing groups of weights (4 x 16 bytes per lane
 // each, plus the group's scales and zeros) in flight ahead of the group it
@@ -332,13 +238,6 @@ __device__ __forceinline__ WaveWork wave_work(const LinearArgs& a, int wave) {
     return w;
 }
 
-__device__ __forceinline__ void decode_scales(uint2 sv, float (&sj)[4]) {
-    sj[0] = f16_bits_to_f32(sv.x & 0xFFFFu);
-    sj[1] = f16_bits_to_f32(sv.x >> 16);
-    sj[2] = f16_bits_to_f32(sv.y & 0xFFFFu);
-    sj[3] = f16_bits_to_f32(sv.y >> 16);
-}
-
 // ---------------------------------------------------------------------------
 // M = 1: VALU GEMV (bf16 dot2, fp32 accumulation, cross-lane shuffles)
 // ---------------------------------------------------------------------------
@@ -350,7 +249,7 @@ __device__ __forceinline__ void decode_scales(uint2 sv, float (&sj)[4]) {
 // per-group sum of those octets (the zero-point term) is the lane's own.  The
 // four octet lanes of a column are summed with two xor-shuffles at the end.
 
-constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 (1.0, 1.0)
+
 
 // Groups of loads each wave keeps in flight (a slot is 4 weight words, the
 // activation pieces, one scale word and one zero word per lane; the total
@@ -850,8 +749,8 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // bits for every KB).
 template <int KB>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, float* __restrict__ y,
-                                                          uint16_t* __restrict__ yb, int M, int N, int npad,
-                                                          int splits) {
+                                                          uint16_t* __restrict__ yb, float alpha, int M, int N,
+                                                          int npad, int splits) {
     const int nq = N / 4;
     const size_t total = (size_t)M * nq;
     const size_t plane = (size_t)M * npad;
@@ -870,14 +769,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                 if (s0 + i < splits) acc += v[i];
         }
         const size_t o = (size_t)m * N + n;
+        acc *= alpha;
         if (yb) {
             const float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
             const uint32_t lo = f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
             const uint32_t hi = f32_to_bf16_rne(a2) | ((uint32_t)f32_to_bf16_rne(a3) << 16);
             *(uint2*)(yb + o) = uint2{lo, hi};
-        } else {
-            *(f32x4*)(y + o) = acc;
         }
+        if (y) *(f32x4*)(y + o) = acc;
     }
 }
 
@@ -1117,8 +1016,6 @@ hipError_t set_kernel_attributes() {
     return hipSuccess;
 }
 
-static constexpr uint32_t kNibbleMask = 0x00780078u;
-static constexpr uint32_t kBiasMagic = 0x41804180u;
 
 static int grid_for(size_t total, int block) {
     size_t g = (total + block - 1) / block;
@@ -1161,13 +1058,21 @@ hipError_t launch_unpack(const uint32_t* qweight_t, const uint16_t* zeros_t, int
 hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
                          const uint16_t* zeros_t, int M, int N, int K, void* y, int out_bf16, const Workspace& ws,
                          hipStream_t stream) {
+    return launch_linear_io(p, x, qweight_t, scales_t, zeros_t, M, N, K, out_bf16 ? nullptr : (float*)y,
+                            out_bf16 ? (uint16_t*)y : nullptr, 1.0f, ws, stream);
+}
+
+hipError_t launch_linear_io(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
+                            const uint16_t* zeros_t, int M, int N, int K, float* y, uint16_t* yb, float alpha,
+                            const Workspace& ws, hipStream_t stream) {
     LinearArgs a;
     a.x = x;
     a.qt = (const u32x4*)qweight_t;
     a.st = (const uint2*)scales_t;
     a.zt = zeros_t;
-    a.y = out_bf16 ? nullptr : (float*)y;
-    a.yb = out_bf16 ? (uint16_t*)y : nullptr;
+    a.y = y;
+    a.yb = yb;
+    a.alpha = alpha;
     a.ws = ws.partial;
     a.M = M;
     a.N = N;
@@ -1212,11 +1117,11 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
     const dim3 rgrid(grid_for(total, 256)), rblock(256);
     const float* part = ws.partial;
     const int npad = a.NC * kChunkN;
-    if (p.splits <= 2) return launch(splitk_reduce_kernel<2>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
-    if (p.splits <= 4) return launch(splitk_reduce_kernel<4>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
-    if (p.splits <= 8) return launch(splitk_reduce_kernel<8>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
-    if (p.splits <= 16) return launch(splitk_reduce_kernel<16>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
-    return launch(splitk_reduce_kernel<32>, rgrid, rblock, 0, stream, part, a.y, a.yb, M, N, npad, p.splits);
+    if (p.splits <= 2) return launch(splitk_reduce_kernel<2>, rgrid, rblock, 0, stream, part, a.y, a.yb, a.alpha, M, N, npad, p.splits);
+    if (p.splits <= 4) return launch(splitk_reduce_kernel<4>, rgrid, rblock, 0, stream, part, a.y, a.yb, a.alpha, M, N, npad, p.splits);
+    if (p.splits <= 8) return launch(splitk_reduce_kernel<8>, rgrid, rblock, 0, stream, part, a.y, a.yb, a.alpha, M, N, npad, p.splits);
+    if (p.splits <= 16) return launch(splitk_reduce_kernel<16>, rgrid, rblock, 0, stream, part, a.y, a.yb, a.alpha, M, N, npad, p.splits);
+    return launch(splitk_reduce_kernel<32>, rgrid, rblock, 0, stream, part, a.y, a.yb, a.alpha, M, N, npad, p.splits);
 }
 
 hipError_t launch_zero(float* y, size_t n, hipStream_t stream) {

@@ -9,7 +9,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("w4a16.h", "w4a16_bench.h", "w4_accept.h", "w4_tree_attn.h")]
+HEADERS = [os.path.join(ROOT, "include", h)
+           for h in ("w4a16.h", "w4a16_bench.h", "w4_accept.h", "w4_tree_attn.h", "w4_pass.h")]
 
 w4 = pytest.importorskip("speculative_decoding_verification_w4a16_amd")
 
@@ -274,3 +275,54 @@ def test_noalloc_refuses_a_split_past_its_scratch_before_any_launch():
                                     stream=0)
     assert err.value.status == w4.W4_ERR_INVALID
     assert w4.W4_OK == 0
+
+
+def _pl(x, y, yb=0, N=256, K=512, deps=(), qt=0x100000, st=0x200000, zt=0x300000, alpha=1.0):
+    d = list(deps)
+    return w4.W4PassLinear(x, qt, st, zt, y, yb, alpha, N, K, len(d), (ctypes.c_int * 4)(*(d + [0] * 4)[:4]))
+
+
+def _create(entries, M=4):
+    arr = (w4.W4PassLinear * len(entries))(*entries)
+    out = ctypes.c_void_p()
+    return w4._c["w4_pass_create"](arr, len(entries), M, 128, ctypes.byref(out))
+
+
+def test_pass_validation_before_any_hip_call():
+    # M = 4, K = 512, N = 256: x is 4 KB, y (fp32) 4 KB; distinct weights per entry
+    X0, Y0, Y1 = 0x1000000, 0x2000000, 0x3000000
+    wt = lambda i: dict(qt=0x10000000 + i * 0x1000000, st=0x20000000 + i * 0x1000000, zt=0x30000000 + i * 0x1000000)
+    ok_chain = [_pl(X0, Y0, **wt(0)), _pl(Y0, Y1, K=256, deps=[0], **wt(1))]
+    # a valid chain passes validation and only then needs the device (none here: W4_ERR_HIP)
+    rc = _create(ok_chain)
+    assert rc in (w4.W4_OK, w4.W4_ERR_HIP), rc
+    bad = {
+        "reads an earlier output without listing it": [_pl(X0, Y0, **wt(0)), _pl(Y0, Y1, K=256, **wt(1))],
+        "depends on a later linear": [_pl(X0, Y0, deps=[1], **wt(0)), _pl(X0 + 0x100000, Y1, **wt(1))],
+        "depends on itself": [_pl(X0, Y0, deps=[0], **wt(0))],
+        "reads the output of a later linear": [_pl(Y1, Y0, **wt(0)), _pl(X0, Y1, **wt(1))],
+        "writes its own input": [_pl(X0, X0, **wt(0))],
+        "two outputs overlap": [_pl(X0, Y0, **wt(0)), _pl(X0, Y0 + 3968, **wt(1))],
+        # a 64-byte bf16 output (4 rows x 8 columns) and an unrelated input in the rest of its line
+        "an input shares an output's cache line": [_pl(X0, 0, yb=Y0, N=8, **wt(0)), _pl(Y0 + 64, Y1, **wt(1))],
+        "output not 128-byte aligned": [_pl(X0, Y0 + 64, **wt(0))],
+        "no output": [_pl(X0, 0, **wt(0))],
+        "output over the weights": [_pl(X0, 0x10000000, **wt(0))],
+        "zeros not 4-byte aligned": [_pl(X0, Y0, qt=0x10000000, st=0x20000000, zt=0x30000002)],
+        "alpha not finite": [_pl(X0, Y0, alpha=float("inf"), **wt(0))],
+        "duplicate producer": [_pl(X0, Y0, **wt(0)), _pl(Y0, Y1, K=256, deps=[0, 0], **wt(1))],
+    }
+    for name, entries in bad.items():
+        assert _create(entries) == w4.W4_ERR_INVALID, name
+    # more producers than the limit, group, M, shapes: unsupported
+    many = [_pl(X0 + i * 0x10000, Y0 + i * 0x10000, **wt(i)) for i in range(5)]
+    many.append(_pl(X0 + 0x900000, Y1, deps=[0, 1, 2, 3, 4], **wt(5)))
+    assert _create(many) == w4.W4_ERR_UNSUPPORTED
+    assert _create([_pl(X0, Y0, N=4, **wt(0))]) == w4.W4_ERR_UNSUPPORTED
+    assert _create([_pl(X0, Y0, **wt(0))], M=65) == w4.W4_ERR_UNSUPPORTED
+    out = ctypes.c_void_p()
+    arr = (w4.W4PassLinear * 1)(_pl(X0, Y0, **wt(0)))
+    assert w4._c["w4_pass_create"](arr, 1, 4, 64, ctypes.byref(out)) == w4.W4_ERR_UNSUPPORTED
+    assert w4._c["w4_pass_create"](arr, 1, 4, 128, None) == w4.W4_ERR_INVALID
+    assert w4._c["w4_pass_run"](None, None) == w4.W4_ERR_INVALID
+    assert w4._c["w4_pass_destroy"](None) == w4.W4_OK

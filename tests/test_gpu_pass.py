@@ -1,0 +1,198 @@
+"""GPU parity of the verify pass as one launch (include/w4_pass.h).
+
+The pass is a chain with real data flow, shaped like Llama-3 decoder layers:
+q, k and v read the layer input; o reads q's output (standing in for the
+attention output, which has q's shape) and waits for q, k and v; gate and up
+read o's output; down reads gate's output and waits for gate and up; the next
+layer's q, k and v read down's output; the lm_head reads the last down's.
+Every linear writes its bf16 output (the next activation) and some also fp32,
+scaled by a power-of-two alpha that keeps magnitudes near 1.
+
+Each output is checked against the oracle applied to the input the linear
+actually read (its producer's output buffer after the run), so a consumer
+that read its input before the producer finished would not match.  Between
+runs the external input changes and every output is filled with NaN first:
+a stale or early read shows up as a mismatch or a NaN.  Cases: the
+persistent kernel at M = 1 (GEMV) and 2, 5, 8, 16 (MFMA), the per-linear
+launches at M = 17 and 64, a HIP graph replayed with eager changes between
+replays, a forced dependency-wait timeout (spin limit 0) and recovery, and
+one full-size Llama-3-70B layer at M = 1 and 5.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import bf16_bits_to_f64, linear64_gemm
+
+from gpu_util import DEV, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+w4 = pytest.importorskip("speculative_decoding_verification_w4a16_amd")
+
+
+def _alpha(K):
+    # a power of two near 1 / (0.02 sqrt(K)): outputs stay near unit scale
+    return 2.0 ** -round(math.log2(0.02 * math.sqrt(K)))
+
+
+class Chain:
+    """Weights, buffers and the pass descriptors of a layered chain."""
+
+    def __init__(self, M, H, KV, F, layers, vocab, seed=7000, fp32_leaves=True):
+        self.M = M
+        self.lins, self.descs, self.names = [], [], []
+        self.x0 = torch.empty((M, H), dtype=torch.int16, device=DEV)
+        self.bufs = []
+        idx = {}
+
+        def add(name, N, K, x, deps, fp32):
+            lin = synth.gen_linear(seed + len(self.lins), N, K)
+            pk = w4.repack(to_dev(lin["qweight"]), to_dev(lin["scales"]), to_dev(lin["zeros"]), N, K)
+            yb = torch.empty((M, N), dtype=torch.int16, device=DEV)
+            y = torch.empty((M, N), dtype=torch.float32, device=DEV) if fp32 else None
+            self.bufs += [t for t in (yb, y) if t is not None]
+            idx[name] = len(self.lins)
+            self.lins.append((lin, pk))
+            self.names.append(name)
+            self.descs.append(dict(x=x, qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t, y=y,
+                                   y_bf16=yb, N=N, K=K, alpha=_alpha(K), deps=[idx[d] for d in deps]))
+            return yb
+
+        h, hdeps = self.x0, []
+        for L in range(layers):
+            q = add(f"q{L}", H, H, h, hdeps, False)
+            add(f"k{L}", KV, H, h, hdeps, fp32_leaves)
+            add(f"v{L}", KV, H, h, hdeps, fp32_leaves)
+            o = add(f"o{L}", H, H, q, [f"q{L}", f"k{L}", f"v{L}"], False)
+            g = add(f"gate{L}", F, H, o, [f"o{L}"], False)
+            add(f"up{L}", F, H, o, [f"o{L}"], fp32_leaves)
+            h = add(f"down{L}", H, F, g, [f"gate{L}", f"up{L}"], True)
+            hdeps = [f"down{L}"]
+        if vocab:
+            add("lm_head", vocab, H, h, hdeps, True)
+        self.handle = w4.w4_pass_create(self.descs, M)
+
+    def close(self):
+        w4.w4_pass_destroy(self.handle)
+
+    def set_input(self, seed):
+        x = synth.gen_x(self.M, self.x0.shape[1], seed_base=seed)
+        self.x0.copy_(to_dev(x))
+
+    def poison(self):
+        for t in self.bufs:
+            if t.dtype == torch.float32:
+                t.fill_(float("nan"))
+            else:
+                t.fill_(0x7FC0)  # bf16 NaN
+
+    def check(self, what):
+        """Every output against the oracle on the input the linear read."""
+        torch.cuda.synchronize()
+        worst = 0.0
+        for (lin, pk), d, name in zip(self.lins, self.descs, self.names):
+            x = d["x"].cpu().numpy().view(np.uint16)
+            assert np.all(np.isfinite(bf16_bits_to_f64(x))), (what, name, "input not finite")
+            Y, A = linear64_gemm(x, lin["qweight"], lin["scales"], lin["zeros"], 128, 0, d["N"])
+            al = d["alpha"]
+            Y, A = Y * al, A * al
+            yb = bf16_bits_to_f64(d["y_bf16"].cpu().numpy().view(np.uint16))
+            err = np.abs(yb - Y)
+            bound = 4e-3 * A * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(Y)
+            assert np.all(err <= bound), (what, name, float(np.nanmax(err / bound)))
+            if d["y"] is not None:
+                y = d["y"].cpu().numpy().astype(np.float64)
+                assert np.all(np.abs(y - Y) <= 4e-3 * A), (what, name)
+                worst = max(worst, float(np.max(np.abs(y - Y) / np.maximum(4e-3 * A, 1e-300))))
+        return worst
+
+
+SMALL = dict(H=1024, KV=128, F=2816, layers=2, vocab=4096)
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 16, 17, 64])
+def test_chain_against_the_oracle_with_changing_inputs(M):
+    ch = Chain(M, **SMALL)
+    info = w4.w4_pass_info(ch.handle)
+    assert info["persistent"] == (1 if M <= 16 else 0), info
+    assert info["units"] == 2 * (16 + 2 + 2 + 16 + 44 + 44 + 16) + 64
+    try:
+        for run, seed in enumerate((8100, 8200, 8300)):
+            ch.set_input(seed)
+            ch.poison()
+            w4.w4_pass_run(ch.handle)
+            w4.w4_pass_check(ch.handle)
+            worst = ch.check((M, run))
+        print(f"M={M}: {info}, worst err/bound of the fp32 outputs {worst:.2e}")
+    finally:
+        ch.close()
+
+
+@pytest.mark.parametrize("M", [1, 5])
+def test_graph_replays_with_eager_changes_between(M):
+    ch = Chain(M, **SMALL)
+    try:
+        ch.set_input(8400)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):  # warm-up outside the capture
+            w4.w4_pass_run(ch.handle, s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            w4.w4_pass_run(ch.handle)
+        for rep, seed in enumerate((8500, 8600, 8700)):
+            ch.set_input(seed)
+            ch.poison()
+            g.replay()
+            w4.w4_pass_check(ch.handle)
+            ch.check(("graph", M, rep))
+    finally:
+        torch.cuda.synchronize()
+        ch.close()
+
+
+def test_forced_wait_timeout_is_reported_and_recovered():
+    # spin limit 0: every dependency wait not already satisfied gives up at
+    # once (the launch still runs to its end); the check reports it, and the
+    # next run with the default limit is correct again
+    ch = Chain(1, **SMALL)
+    try:
+        ch.set_input(8800)
+        w4.w4_pass_set_spin_limit(ch.handle, 0)
+        w4.w4_pass_run(ch.handle)
+        with pytest.raises(w4.W4Error) as err:
+            w4.w4_pass_check(ch.handle)
+        assert err.value.status == w4.W4_ERR_TIMEOUT
+        w4.w4_pass_check(ch.handle)  # the flag was cleared
+        w4.w4_pass_set_spin_limit(ch.handle, 1 << 24)
+        ch.poison()
+        w4.w4_pass_run(ch.handle)
+        w4.w4_pass_check(ch.handle)
+        ch.check("after the timeout")
+    finally:
+        ch.close()
+
+
+@pytest.mark.parametrize("M", [1, 5])
+def test_full_size_llama_layer(M):
+    # one Llama-3-70B decoder layer (hidden 8192, kv 1024, MLP 28672) with the
+    # layer's data flow, every column of every output against the oracle
+    ch = Chain(M, H=8192, KV=1024, F=28672, layers=1, vocab=0, seed=1000, fp32_leaves=True)
+    try:
+        ch.set_input(2000)
+        ch.poison()
+        w4.w4_pass_run(ch.handle)
+        w4.w4_pass_check(ch.handle)
+        worst = ch.check(("llama layer", M))
+        print(f"Llama-3-70B layer M={M}: worst err/bound {worst:.2e}")
+    finally:
+        ch.close()
