@@ -8,13 +8,29 @@ o 8192->8192, gate/up 8192->28672, down 28672->8192) and an int4 lm_head
 W ~ N(0, 0.02) quantised round-to-nearest; layer L's linear idx uses seed
 10000 + 7L + idx and the lm_head seed 20000.  ~36.1 GB of packed weights stay
 resident in HBM.  One *step* is three verify passes, at M = 1 (plain decode),
-M = 5 (a sequence draft) and M = 64 (a flattened tree draft): 561 linear
-launches each, captured once per M in a HIP graph and replayed.
+M = 5 (a sequence draft) and M = 64 (a flattened tree draft).
+
+A pass keeps the model's data dependencies: layer L's q, k and v read the
+layer input (layer L-1's down output; layer 0: a seeded input), o reads q's
+output (standing in for the attention output, which has q's shape) and waits
+for q, k and v, gate and up read o's output, down reads gate's output and
+waits for gate and up, and the lm_head reads the last down output.  Every
+linear writes its result as bf16 (the next layer's activation type), scaled
+by a power of two (1/2 for K = 8192, 1/4 for K = 28672) that keeps the
+activations near unit scale over 80 layers.  A pass is one pass object
+(include/w4_pass.h): at M = 1 and 5 one persistent launch, at M = 64 the 561
+linears as their own launches; each captured once in a HIP graph and
+replayed.  Algorithmic bytes per linear: 0.51953125 N K (codes, scales,
+zeros) + 2 M K (x) + 2 M N (the bf16 output).
 
 Printed JSON line: `value` is the step's effective HBM throughput (algorithmic
 bytes of the three passes / step time, TB/s); per-M microseconds per pass,
-t(M)/t(1), roofline fractions, the measured HBM read ceiling, the oracle's
-host throughput on a bounded sample and the oracle spot checks ride along.
+t(M)/t(1), roofline fractions, the same passes as 561 independent launches
+(no dependencies, fp32 outputs) for comparison, the measured HBM read
+ceiling, the oracle's host throughput on a bounded sample and the oracle
+checks (every output column of three seeded-random layers and a 512-column
+slice of the lm_head, against the oracle on the inputs each linear read)
+ride along.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3]
 """
@@ -44,11 +60,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(M: int, N: int, K: int) -> int:
+def alg_bytes(M: int, N: int, K: int, out_bytes: int = 4) -> int:
     """Algorithmic HBM bytes of one linear: packed codes (N K / 2), fp16 scales
     and uint4 zeros per group of 128 (N K / 64 + N K / 256), x once (2 M K)
-    and y once (4 M N)."""
-    return N * K // 2 + N * K // 64 + N * K // 256 + 2 * M * K + 4 * M * N
+    and y once (out_bytes M N: 4 for fp32, 2 for bf16)."""
+    return N * K // 2 + N * K // 64 + N * K // 256 + 2 * M * K + out_bytes * M * N
 
 
 def alg_flops(M: int, N: int, K: int) -> int:
@@ -165,7 +181,8 @@ def build_model(torch, w4, keep_layers, keep_linears=()):
         dq.copy_(hq, non_blocking=True)
         ds.copy_(hs, non_blocking=True)
         dz.copy_(hz, non_blocking=True)
-        pk = w4.repack(dq, ds, dz, N, K)
+        G = K // 128
+        pk = w4.repack(dq.view(K // 8, N), ds.view(G, N), dz.view(G, N // 8), N, K)
         ev = torch.cuda.Event()
         ev.record(stream)
         ev.synchronize()  # the slot's host data has been consumed
@@ -200,20 +217,6 @@ def hbm_read_ceiling(torch, w4, nbytes=8 << 30, reps=5):
         best = max(best, nbytes / (s.elapsed_time(e) * 1e-3) / 1e9)
     del buf
     return best
-
-
-def per_launch_durations(torch, w4, descs, M, reps=2):
-    """Eager pass with events around every launch (ms per launch, mean over reps)."""
-    dur = np.zeros(len(descs))
-    for _ in range(reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in descs]
-        for d, (s, e) in zip(descs, evs):
-            s.record()
-            w4.w4a16_verify_pass([d], M)
-            e.record()
-        torch.cuda.synchronize()
-        dur += np.array([s.elapsed_time(e) for s, e in evs])
-    return dur / reps
 
 
 def source_digest():
@@ -279,38 +282,81 @@ def cpu_baseline(host, budget_s=20.0):
                       f"{nbytes / 1e9:.3f} GB of algorithmic traffic in {secs:.2f} s"}
 
 
-def parity_checks(torch, w4, packed, host, xs, check_layers, n0):
-    """Oracle spot checks (3 layers x 7 linears on sampled column slices, and
-    the lm_head on a 512-column slice) at every pass M, using the same launch
-    plan as the sweep."""
-    import synth
-    from oracle import check_contract, linear64_columns
+# ---------------------------------------------------------------------------
+# the verify pass with the model's data dependencies (one pass object per M)
+# ---------------------------------------------------------------------------
 
+def layer_alpha(K: int) -> float:
+    """Power-of-two output scale near 1 / (0.02 sqrt(K)): 1/2 at K = 8192, 1/4
+    at K = 28672, so activations stay near unit scale through 80 layers."""
+    import math
+
+    return 2.0 ** -round(math.log2(0.02 * math.sqrt(K)))
+
+
+def dependent_pass(torch, w4, packed, M, input_seed=2000):
+    """The pass object of the sweep at M: every linear reads the bf16 output
+    of its producer (see the module docstring) and writes its own bf16
+    output to a buffer of its own.  Returns (handle, outputs by (layer,
+    name), layer-0 input tensor, the descriptors)."""
+    import synth
+
+    dev = "cuda:0"
+    H = synth.LAYER_LINEARS[0][2]
+    h0 = torch.from_numpy(synth.gen_x(M, H, seed_base=input_seed).view(np.int16)).to(dev)
+    outs, descs, index = {}, [], {}
+    h, hdeps = h0, []
+
+    def add(L, name, x, deps):
+        pk = packed[(L, name)]
+        y = torch.empty((M, pk.N), dtype=torch.int16, device=dev)
+        outs[(L, name)] = y
+        index[(L, name)] = len(descs)
+        descs.append(dict(x=x, qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t, y=None,
+                          y_bf16=y, N=pk.N, K=pk.K, alpha=layer_alpha(pk.K), deps=[index[d] for d in deps],
+                          key=(L, name)))
+        return y
+
+    for L in range(synth.N_LAYERS):
+        q = add(L, "q", h, hdeps)
+        add(L, "k", h, hdeps)
+        add(L, "v", h, hdeps)
+        o = add(L, "o", q, [(L, "q"), (L, "k"), (L, "v")])
+        g = add(L, "gate", o, [(L, "o")])
+        add(L, "up", o, [(L, "o")])
+        h = add(L, "down", g, [(L, "gate"), (L, "up")])
+        hdeps = [(L, "down")]
+    add(None, "lm_head", h, hdeps)
+    handle = w4.w4_pass_create(descs, M)
+    return handle, outs, h0, descs
+
+
+def dependent_pass_parity(torch, w4, host, descs, check_layers, n0, M):
+    """Every output column of the checked layers' linears, and columns
+    [n0, n0 + 512) of the lm_head, against the oracle applied to the input
+    buffer each linear read (its producer's bf16 output after the pass):
+    |y - alpha Y64| <= 4e-3 alpha A64 (1 + 2^-8) + 2^-8 |alpha Y64| (the
+    contract plus the bf16 rounding of the output).  Returns the worst ratio."""
+    from oracle import bf16_bits_to_f64, linear64_gemm
+
+    torch.cuda.synchronize()
     worst = 0.0
-    rng = np.random.default_rng(1)
-    for M in PASS_M:
-        for L in check_layers:
-            for name, N, K in synth.LAYER_LINEARS:
-                lin = host[(L, name)]
-                y = w4.linear(xs[K][:M], packed[(L, name)])
-                torch.cuda.synchronize()
-                yh = y.cpu().numpy()
-                mid = int(rng.integers(1, N // 64 - 1)) * 64
-                for a, b in ((0, 64), (mid, mid + 64), (N - 64, N)):
-                    Y, A = linear64_columns(synth.gen_x(M, K), lin["qweight"], lin["scales"], lin["zeros"], 128, a, b)
-                    ok, r = check_contract(yh[:, a:b], Y, A)
-                    worst = max(worst, r)
-                    if not ok:
-                        raise AssertionError(f"parity failure layer {L} {name} M={M} cols {a}:{b} ratio {r}")
-        lin = host[(None, "lm_head")]
-        name, N, K = synth.LM_HEAD
-        y = w4.linear(xs[K][:M], packed[(None, "lm_head")])
-        torch.cuda.synchronize()
-        Y, A = linear64_columns(synth.gen_x(M, K), lin["qweight"], lin["scales"], lin["zeros"], 128, n0, n0 + 512)
-        ok, r = check_contract(y.cpu().numpy()[:, n0:n0 + 512], Y, A)
-        worst = max(worst, r)
-        if not ok:
-            raise AssertionError(f"parity failure lm_head M={M} ratio {r}")
+    for d in descs:
+        L, name = d["key"]
+        if L not in check_layers and name != "lm_head":
+            continue
+        lin = host[(L, name)]
+        x = d["x"].cpu().numpy().view(np.uint16)
+        y = bf16_bits_to_f64(d["y_bf16"].cpu().numpy().view(np.uint16))
+        cols = [(n0, n0 + 512)] if name == "lm_head" else [(a, min(d["N"], a + 4096)) for a in range(0, d["N"], 4096)]
+        for a, b in cols:
+            Y, A = linear64_gemm(x, lin["qweight"], lin["scales"], lin["zeros"], 128, a, b)
+            Y, A = Y * d["alpha"], A * d["alpha"]
+            bound = 4e-3 * A * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(Y)
+            r = float(np.max(np.abs(y[:, a:b] - Y) / bound))
+            if not r <= 1.0:
+                raise AssertionError(f"parity failure: layer {L} {name} M={M} cols {a}:{b} ratio {r}")
+            worst = max(worst, r)
     return worst
 
 
@@ -781,32 +827,23 @@ def main():
     dev = "cuda:0"
     if args.copy_calib:
         copy_calibration(torch, w4, args.copy_calib)
-    xs = {K: torch.from_numpy(synth.gen_x(64, K).view(np.int16)).to(dev) for K in (8192, 28672)}
-    ys = {N: torch.empty((64, N), dtype=torch.float32, device=dev) for N in (1024, 8192, 28672, 128256)}
     specs = model_specs()
+    nlin = len(specs)
 
-    def descs_for(M):
-        out = []
-        for s in specs:
-            pk = packed[(s["layer"], s["name"])]
-            out.append(dict(x=xs[s["K"]][:M], qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t,
-                            y=ys[s["N"]][:M], N=s["N"], K=s["K"]))
-        return out
-
-    descs = {M: descs_for(M) for M in PASS_M}
-    pass_bytes = {M: sum(alg_bytes(M, s["N"], s["K"]) for s in specs) for M in PASS_M}
+    # the dependent passes (the measured workload)
+    passes = {M: dependent_pass(torch, w4, packed, M) for M in PASS_M}
+    pass_bytes = {M: sum(alg_bytes(M, s["N"], s["K"], 2) for s in specs) for M in PASS_M}
     pass_flops = {M: sum(alg_flops(M, s["N"], s["K"]) for s in specs) for M in PASS_M}
-
-    # eager pass once per M (also the graph's warm-up), then capture
-    for M in PASS_M:
-        w4.w4a16_verify_pass(descs[M], M)
-    torch.cuda.synchronize()
+    info = {M: w4.w4_pass_info(passes[M][0]) for M in PASS_M}
+    for M in PASS_M:  # eager run once per M (also the graph's warm-up)
+        w4.w4_pass_run(passes[M][0])
+        w4.w4_pass_check(passes[M][0])
     graphs = {}
     cap = torch.cuda.Stream()
     for M in PASS_M:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            w4.w4a16_verify_pass(descs[M], M)
+            w4.w4_pass_run(passes[M][0])
         graphs[M] = g
     torch.cuda.synchronize()
 
@@ -824,64 +861,89 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
+    for M in PASS_M:
+        w4.w4_pass_check(passes[M][0])  # no dependency wait gave up in any replay
     step_bytes = sum(pass_bytes.values())
     value_tbs = step_bytes / (ms_per_step * 1e-3) / 1e12
 
     # per-M pass times (graph replays)
-    us_per_pass = {}
-    for M in PASS_M:
-        reps = max(3, args.steps)
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
+    def replay_us(g, reps):
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
         for _ in range(reps):
-            graphs[M].replay()
-        e.record()
+            g.replay()
+        s1.record()
         torch.cuda.synchronize()
-        us_per_pass[M] = s.elapsed_time(e) * 1e3 / reps
-    # eager (no graph) pass times, for the launch-overhead comparison
+        return s0.elapsed_time(s1) * 1e3 / reps
+
+    us_per_pass = {M: replay_us(graphs[M], max(3, args.steps)) for M in PASS_M}
     us_eager = {}
     for M in PASS_M:
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        w4.w4a16_verify_pass(descs[M], M)
-        e.record()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        w4.w4_pass_run(passes[M][0])
+        s1.record()
         torch.cuda.synchronize()
-        us_eager[M] = s.elapsed_time(e) * 1e3
+        us_eager[M] = s0.elapsed_time(s1) * 1e3
 
-    # per-kernel roofline: every linear of a pass runs one kernel
-    # (M=1 -> the GEMV, M=5 -> the direct MFMA kernel with one m-block,
-    # M=64 -> the LDS-ring MFMA kernel with four m-blocks, on k and v four row
-    # slices of one m-block each), followed, when its
-    # K is split, by splitk_reduce_kernel; the unit of the figures below is
-    # the linear, i.e. that kernel plus its reduction.
-    kernel_of = {1: "w4a16_gemv_kernel<4>", 5: "w4a16_mfma_direct_kernel<1, 4>",
-                 64: "w4a16_mfma_lds_kernel<4 (k, v: 1), 4 or 8>"}
-    # The graph of a pass holds nothing but those launches (the gaps between
-    # them measure ~0 in the kernel trace), so the pass time per linear is the
-    # mean duration of a linear; events around single eager linears are
-    # reported beside it (they add a few microseconds each).
+    # the same linears as 561 independent launches (no dependencies, one input
+    # per K, fp32 outputs): the structure of a launch per linear, for comparison
+    xs = {K: torch.from_numpy(synth.gen_x(64, K).view(np.int16)).to(dev) for K in (8192, 28672)}
+    ys = {N: torch.empty((64, N), dtype=torch.float32, device=dev) for N in (1024, 8192, 28672, 128256)}
+
+    def descs_for(M):
+        out = []
+        for sp in specs:
+            pk = packed[(sp["layer"], sp["name"])]
+            out.append(dict(x=xs[sp["K"]][:M], qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t,
+                            y=ys[sp["N"]][:M], N=sp["N"], K=sp["K"]))
+        return out
+
+    sep_descs = {M: descs_for(M) for M in PASS_M}
+    us_separate = {}
+    for M in PASS_M:
+        w4.w4a16_verify_pass(sep_descs[M], M)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            w4.w4a16_verify_pass(sep_descs[M], M)
+        g.replay()
+        torch.cuda.synchronize()
+        us_separate[M] = replay_us(g, max(3, args.steps))
+        del g
+    sep_bytes = {M: sum(alg_bytes(M, sp["N"], sp["K"]) for sp in specs) for M in PASS_M}
+
+    # per-kernel roofline.  M = 1 and 5: the whole pass is one launch of the
+    # persistent pass kernel (GEMV and MFMA form); M = 64: 561 launches of the
+    # LDS-ring MFMA kernel (k, v: four row slices of one row block), each with
+    # its split-K reduction when K is split -- there the unit is the linear.
+    # Durations come from the graph replays (events on the replay stream).
     kernels = {}
     for M in PASS_M:
-        dur_ms = per_launch_durations(torch, w4, descs[M], M)
-        mean_us = us_per_pass[M] / len(specs)
-        bytes_per_launch = pass_bytes[M] / len(specs)
-        flops_per_launch = pass_flops[M] / len(specs)
-        achieved = bytes_per_launch / (mean_us * 1e-6) / 1e9
-        kernels[kernel_of[M]] = {
-            "M": M, "launches_per_pass": len(specs), "mean_launch_us": round(mean_us, 3),
-            "mean_launch_us_events": round(float(dur_ms.mean() * 1e3), 3),
-            "alg_bytes_per_launch": int(bytes_per_launch), "achieved_GBps": round(achieved, 1),
+        if info[M]["persistent"]:
+            name = "w4_pass_kernel<GEMV>" if M == 1 else "w4_pass_kernel<MFMA 16 rows>"
+            launches = 1
+        else:
+            name = "w4a16_mfma_lds_kernel<4 (k, v: 1), 4 or 8>"
+            launches = nlin
+        mean_us = us_per_pass[M] / launches
+        bpl = pass_bytes[M] / launches
+        achieved = bpl / (mean_us * 1e-6) / 1e9
+        kernels[name] = {
+            "M": M, "launches_per_pass": launches, "mean_launch_us": round(mean_us, 3),
+            "alg_bytes_per_launch": int(bpl), "achieved_GBps": round(achieved, 1),
             "frac_hbm": round(achieved / HBM_PEAK_GBS, 4),
-            "mfma_util": round(flops_per_launch / (mean_us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+            "mfma_util": round(pass_flops[M] / launches / (mean_us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
             "time_share_us": round(us_per_pass[M], 1)}
     dom = max(kernels, key=lambda k: kernels[k]["time_share_us"])
     dk = kernels[dom]
     traffic = traffic_from_profiles(dk["M"])
     roofline = {"bound": "hbm", "achieved": dk["achieved_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dk["achieved_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
-                "per_launch": "alg_bytes_per_launch = 0.51953125 N K + 2 M K + 4 M N averaged over the 561 "
-                              "linears of the pass; achieved = that / (graph pass time / 561); a linear is the "
-                              "kernel plus splitk_reduce_kernel when its K is split"}
+                "per_launch": ("alg_bytes_per_launch = 0.51953125 N K + 2 M K + 2 M N (bf16 output) summed over "
+                               "the launch's linears: the 561 linears of the pass for the persistent pass kernel, "
+                               "one linear (averaged over the pass) for per-linear launches; achieved = that / "
+                               "the launch's mean duration from the graph replays")}
 
     fused = acceptance = tree = None
     if not args.no_extras:
@@ -892,8 +954,17 @@ def main():
     ceiling = hbm_read_ceiling(torch, w4)
     parity = None
     if not args.no_parity:
-        parity = {"layers": check_layers, "lm_head_cols": [n0, n0 + 512],
-                  "worst_err_over_bound": parity_checks(torch, w4, packed, host, xs, check_layers, n0)}
+        worst = {}
+        for M in PASS_M:
+            handle, outs, h0, pdescs = passes[M]
+            h0.copy_(torch.from_numpy(synth.gen_x(M, h0.shape[1], seed_base=2500).view(np.int16)))
+            for t in outs.values():
+                t.fill_(0x7FC0)  # bf16 NaN: an output left unwritten, or read early, shows up
+            graphs[M].replay()  # the captured pass, on a changed input
+            w4.w4_pass_check(handle)
+            worst[str(M)] = dependent_pass_parity(torch, w4, host, pdescs, check_layers, n0, M)
+        parity = {"layers": check_layers, "lm_head_cols": [n0, n0 + 512], "columns": "all (lm_head: the slice)",
+                  "worst_err_over_bound": worst}
     cpu = None if args.no_cpu_baseline else cpu_baseline(host)
 
     t_roof = {M: max(pass_bytes[M] / (HBM_PEAK_GBS * 1e9), pass_flops[M] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
@@ -913,9 +984,16 @@ def main():
         "data": "synthetic (seeded Gaussian weights quantised to uint4 g=128, Gaussian bf16 activations)",
         "config": {"workload": "llama3-70b-w4a16-verify-sweep", "layers": 80, "linears_per_pass": len(specs),
                    "passes_per_step": list(PASS_M), "group": 128, "weight_bytes": int(sum(
-                       s["N"] * s["K"] * 0.51953125 for s in specs)), "graph": True},
+                       s["N"] * s["K"] * 0.51953125 for s in specs)), "graph": True,
+                   "dependencies": "each linear reads its producer's bf16 output", "output": "bf16",
+                   "launches_per_pass": {str(M): (1 if info[M]["persistent"] else nlin) for M in PASS_M}},
         "us_per_pass": {str(M): round(us_per_pass[M], 1) for M in PASS_M},
         "us_per_pass_eager": {str(M): round(us_eager[M], 1) for M in PASS_M},
+        "separate_launches": {"us_per_pass": {str(M): round(us_separate[M], 1) for M in PASS_M},
+                              "roofline_frac_per_pass": {str(M): round(max(
+                                  sep_bytes[M] / (HBM_PEAK_GBS * 1e9),
+                                  pass_flops[M] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6 / us_separate[M], 4)
+                                  for M in PASS_M}},
         "tbps_per_pass": {str(M): round(pass_bytes[M] / (us_per_pass[M] * 1e-6) / 1e12, 4) for M in PASS_M},
         "roofline_frac_per_pass": {str(M): round(t_roof[M] / us_per_pass[M], 4) for M in PASS_M},
         "t_over_t1": {str(M): round(us_per_pass[M] / us_per_pass[1], 4) for M in PASS_M},

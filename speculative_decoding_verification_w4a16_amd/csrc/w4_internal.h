@@ -92,6 +92,15 @@ constexpr int kPassMaxM = 16;
 constexpr int kPassWaves = 8;  // waves per workgroup
 constexpr int kPassRing = 4;   // groups of loads in flight per streaming wave
 constexpr int kPassMaxDeps = 4;
+// Completion counters: each linear has kPassSub sub-counters, one 64-byte
+// line apart; chunk c counts on sub-counter c % kPassSub.  (Atomics on one
+// address are performed one at a time: a single counter per linear would
+// queue every unit's increment behind the others.)
+constexpr int kPassSub = 64;
+constexpr int kPassSubStride = 16;  // dwords between sub-counters
+// dwords of the counter block of n linears: the sub-counters, then the
+// exited-workgroup count and the error flag
+constexpr size_t pass_counter_words(int n) { return (size_t)n * kPassSub * kPassSubStride + 2; }
 
 // One linear of a pass, as the kernel reads it (device table).
 struct PassLinear {
@@ -108,6 +117,7 @@ struct PassLinear {
     int ndep;
     int dep[kPassMaxDeps];        // producer linears
     int dep_units[kPassMaxDeps];  // their unit (chunk) counts
+    int dep_class;       // the first linear with the same set of producers (-1: none)
 };
 
 hipError_t launch_pass(const PassLinear* tab, int n, int U, int M, uint32_t* done, uint32_t* state,

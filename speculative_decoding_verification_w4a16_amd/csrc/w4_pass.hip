@@ -28,23 +28,31 @@
 // at one depth: loads retire in issue order, so waiting for a later load
 // also waits for every older one).  The last round of R steps of a unit
 // reloads the ring with the wave's first R groups of weights of its next
-// unit; that unit's activations are loaded once its producers are seen
-// complete.  At the end of a unit each wave leaves its partial [rows x 64]
-// sums in LDS and the waves meet at a barrier; one wave (rotating) then sums
-// the partials in wave order, scales by the linear's alpha and stores the
-// tile (fp32 and/or bf16) with agent-scope stores, which reach the device
-// coherence point directly.
+// unit; that unit's activations follow once its producers are complete.  At
+// the end of a unit each wave leaves its partial [rows x 64] sums in LDS and
+// the waves meet at a barrier; one wave (rotating) then sums the partials in
+// wave order, scales by the linear's alpha and stores the tile (fp32 and/or
+// bf16) with agent-scope stores, which reach the device coherence point
+// directly.
 //
-// Ordering without stalls: a wave polls the producer counters of its next
-// unit at the start of the current unit's last round, before that round's
-// reloads, so the answer is back by the unit's end without draining the
-// ring.  The writing wave stores the tile before it loads the next unit's
-// activations; as loads and stores retire in issue order, the wait for the
-// first of those activations also covers the stores, and right after it the
-// wave counts the unit done.  Where the next unit's producers are not yet
-// done, the writing wave first drains its stores and counts its unit done,
-// then every wave polls until they are -- a wave never waits with a unit of
-// its own still uncounted.
+// Completion counting: unit c of a linear counts on one of 64 sub-counters
+// (c mod 64), each on its own 64-byte line -- atomics on one address are
+// performed one at a time, and a single counter per linear would queue
+// every unit's increment behind all the others.  A consumer's lane j reads
+// sub-counter j; the producer is complete when every lane has seen its
+// count.
+//
+// Ordering without stalls: within a linear, and across linears with the
+// same producers, the producers are already known complete, so the last
+// round loads the next unit's activations right away and the ring never
+// drains.  The writing wave then counts its unit done at step 0 of the next
+// unit's second round, once the loads issued after its tile stores have
+// retired (in-order retirement covers the stores).  At a linear whose
+// producers are not known complete, the writing wave retires its stores and
+// counts its unit done at once (no wave waits with a unit of its own
+// uncounted), wave 0 polls the producers' sub-counters, the workgroup meets
+// at a barrier, and every wave loads the activations of its next unit (its
+// weights are in the ring already).
 //
 // Units are numbered in pass order and a linear's producers come before it,
 // so the lowest unit not yet done has all its producers done: with every
@@ -89,7 +97,7 @@ struct PassArgs {
     int n;                // linears
     int U;                // units (sum of the linears' chunk counts)
     int M;                // rows (verified tokens)
-    uint32_t* done;       // [n] units done per linear (zero between launches)
+    uint32_t* done;       // units done per linear: kPassSub sub-counters each (zero between launches)
     uint32_t* state;      // [0] workgroups exited, [1] error flag (sticky)
     uint32_t spin_limit;  // polls before a wait gives up
     uint32_t mask, magic; // the unpack's constants (see unpack_biased)
@@ -164,38 +172,33 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
         const bool xvalid = MB == 0 || t < a.M;
         const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2});
 
-        // producer counters of linear l, and the blocking wait for them; past
-        // the limit the error flag is raised and the wait abandoned (the
-        // results are then invalid, but every wave still exits)
-        // (always kPassMaxDeps loads -- unused entries read counter 0 -- so
-        // that the compiler counts the loads in flight exactly)
-        auto poll = [&](int l, uint32_t (&pv)[kPassMaxDeps]) {
-            const PassLinear& L = tab[l];
-#pragma unroll
-            for (int j = 0; j < kPassMaxDeps; ++j) pv[j] = load_agent(a.done + (j < L.ndep ? L.dep[j] : 0));
-        };
-        auto deps_ok = [&](int l, const uint32_t (&pv)[kPassMaxDeps]) {
-            const PassLinear& L = tab[l];
-            bool ok = true;
-#pragma unroll
-            for (int j = 0; j < kPassMaxDeps; ++j) ok = ok && (j >= L.ndep || pv[j] >= (uint32_t)L.dep_units[j]);
-            return ok;
-        };
+        // Completion of a producer: its chunk c counts on sub-counter c % 64,
+        // so lane j reads sub-counter j and compares it with the number of
+        // chunks that count there; the producer is complete when every lane
+        // agrees.  One wave of the workgroup polls (wave 0); past the limit
+        // it raises the error flag and gives up (the results are then
+        // invalid, but every wave still exits).
+        auto sub = [&](int l) { return a.done + ((size_t)l * kPassSub + lane) * kPassSubStride; };
+        auto expected = [&](int nc) { return (uint32_t)(nc / kPassSub + (lane < nc % kPassSub ? 1 : 0)); };
         auto wait_deps = [&](int l) {
             const PassLinear& L = tab[l];
             for (int j = 0; j < L.ndep; ++j) {
-                const uint32_t* cnt = a.done + L.dep[j];
-                const uint32_t target = (uint32_t)L.dep_units[j];
+                const uint32_t* cnt = sub(L.dep[j]);
+                const uint32_t target = expected(L.dep_units[j]);
                 for (uint32_t it = 0;; ++it) {
-                    if (load_agent(cnt) >= target) break;
+                    if (__ballot(load_agent(cnt) < target) == 0ull) break;
                     if (it >= a.spin_limit || ((it & 63) == 63 && load_agent(a.state + 1) != 0u)) {
-                        store_agent(a.state + 1, 1u);
+                        if (lane == 0) store_agent(a.state + 1, 1u);
                         break;
                     }
-                    __builtin_amdgcn_s_sleep(2);
+                    __builtin_amdgcn_s_sleep(1);
                 }
             }
         };
+        // The producers of every linear with the dependency class `ok` (the
+        // same set of producers) are known complete: its units need no wait.
+        int ok = -1;
+        auto known_ready = [&](int l) { return tab[l].ndep == 0 || tab[l].dep_class == ok; };
 
         int l = find_linear(tab, a, 0, u);
         WaveUnit cur = wave_unit<R>(tab, a, l, u, wave, lane, W);
@@ -205,7 +208,6 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
             ln = find_linear(tab, a, l, un);
             nxt = wave_unit<R>(tab, a, ln, un, wave, lane, W);
         }
-        uint32_t pv[kPassMaxDeps] = {0u, 0u, 0u, 0u};
 
         u32x4 rw[R][4];
         uint2 rs[R];
@@ -286,70 +288,85 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
         };
 
         // the unit this wave stored and has not counted yet (-1: none)
-        int pend_l = -1;
+        int pend_l = -1, pend_c = 0;
         auto count_done = [&]() {
             if (pend_l >= 0 && lane == 0)
-                __hip_atomic_fetch_add(a.done + pend_l, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(a.done + ((size_t)pend_l * kPassSub + pend_c % kPassSub) * kPassSubStride, 1u,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             pend_l = -1;
         };
-
-        // Rounds of R steps of the current share.  round_mid reloads each slot
-        // with the share's own step R ahead (weights, then activations);
-        // round_last polls the next unit's producers, then reloads each slot
-        // with the next unit's first R groups of weights only.  The first
-        // round of a unit (which also counts the previous unit done once its
-        // stores have retired), the middle rounds (a loop) and the last are
-        // separate code, so every loop header sees one pattern of loads in
-        // flight and the compiler's wait counts stay exact (a separate copy
-        // for one-round units doubled the live registers: units have two
-        // rounds at least).
-        auto round_first = [&]() {
-#pragma unroll
-            for (int d = 0; d < R; ++d) {
-                if (d < cur.ng) step(d);
-                if (d == 0) count_done();  // step 0 waited for loads issued after the stores
-                load_w(d, cur, d + R);
-                load_x(d, cur, d + R);
-            }
+        // Loads a step issues: 4 of weights, 1 of scales, 1 of zeros, 4 of
+        // activations.  At step 0 of the second round the whole first round's
+        // loads were issued after the tile stores; waiting until no more than
+        // that many are outstanding retires the stores (the step itself
+        // usually waits longer already -- not when the step is padding).
+        constexpr int kLoadsPerStep = 10;
+        auto count_done_stored = [&]() {
+            if (pend_l >= 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(R * kLoadsPerStep) : "memory");
+            count_done();
         };
-        auto round_mid = [&](int r0) {
+        // One round of R steps; each step reloads its slot R steps ahead
+        // within the unit.
+        auto round = [&](int r) {
 #pragma unroll
             for (int d = 0; d < R; ++d) {
-                const int i = r0 * R + d;
+                const int i = r * R + d;
                 if (i < cur.ng) step(d);
+                if (r == 1 && d == 0) count_done_stored();
                 load_w(d, cur, i + R);
                 load_x(d, cur, i + R);
             }
         };
-        auto round_last = [&](int r0) {
-            poll(ln, pv);
+        // The last round reloads the ring with the next unit's weights; its
+        // activations follow, for all R slots, once its producers are
+        // complete: at once when they are known complete, else after the
+        // wait.  Both ways the ring is loaded in the same order (weights of
+        // slots 0..R-1, then activations of slots 0..R-1), so the compiler's
+        // wait counts hold for either.
+        auto last_round = [&](int r) {
 #pragma unroll
             for (int d = 0; d < R; ++d) {
-                const int i = r0 * R + d;
+                const int i = r * R + d;
                 if (i < cur.ng) step(d);
+                if (r == 1 && d == 0) count_done_stored();
                 load_w(d, nxt, d);
             }
         };
+        auto load_next_x = [&]() {
+#pragma unroll
+            for (int d = 0; d < R; ++d) {
+                __builtin_amdgcn_sched_barrier(0);  // in slot order
+                load_x(d, nxt, d);
+            }
+        };
 
-        // the first unit: its weights now, its activations once its producers are done
+        // the first unit: its producers, then its first R groups
+        if (wave == 0) wait_deps(l);
+        __syncthreads();
+        ok = tab[l].dep_class;
 #pragma unroll
         for (int d = 0; d < R; ++d) load_w(d, cur, d);
-        wait_deps(l);
-        for (int cnt = 0;; ++cnt) {
 #pragma unroll
-            for (int d = 0; d < R; ++d) load_x(d, cur, d);
-            // issue all four in slot order here: the compiler would otherwise
-            // sink slot 0's loads into the step that uses them, behind the
-            // others, and the first wait would then drain the whole ring
-            asm volatile("" ::: "memory");
+        for (int d = 0; d < R; ++d) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_x(d, cur, d);
+        }
+        for (int cnt = 0;; ++cnt) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 yg[j] = 0.0f;
                 ym[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
-            round_first();
-            for (int r0 = 1; r0 < cur.nr - 1; ++r0) round_mid(r0);
-            round_last(cur.nr - 1);
+            // round 0 apart: it starts from the ring as a unit start leaves it
+            // (weights, then activations), the later rounds from a round's
+            // order (slot by slot) -- each gets its own exact wait counts
+            round(0);
+            for (int r = 1; r < cur.nr - 1; ++r) round(r);
+            const bool more = un < a.U;
+            const bool fast = more && known_ready(ln);
+            const bool writer = wave == cnt % W;  // the wave that stores this unit's tile
+            last_round(cur.nr - 1);
+            if (fast) load_next_x();
             // this wave's partial sums of the unit, into LDS
             float* dst = part[cnt & 1][wave];
             if (MB == 0) {
@@ -368,7 +385,7 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
                     for (int rr = 0; rr < 4; ++rr) dst[(4 * o + rr) * kChunkN + 16 * j + t] = ym[j][rr];
             }
             lds_barrier();  // the W partials of the unit are complete
-            if (wave == cnt % W) {
+            if (writer) {
                 // this wave writes the tile: W partials summed in wave order
                 const PassLinear& L = tab[l];
                 const int c = u - L.unit0;
@@ -386,51 +403,50 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
                         if ((lane & 1) == 0 && n < L.N) store_agent((uint32_t*)(L.yb + n), b | (b1 << 16));
                     }
                 } else {
-                    const int r = lane >> 2, cb = (lane & 3) * 16;  // row r, 16 columns from cb
-                    float v[16];
+                    // lane: row r, 16 columns from cb, one quad at a time (the
+                    // next unit's ring is in flight: few registers to spare)
+                    const int r = lane >> 2, cb = (lane & 3) * 16;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-                    for (int w = 0; w < W; ++w)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const f32x4 p4 = *(const f32x4*)&part[buf][w][r * kChunkN + cb + 4 * q];
-                            v[4 * q + 0] += p4[0];
-                            v[4 * q + 1] += p4[1];
-                            v[4 * q + 2] += p4[2];
-                            v[4 * q + 3] += p4[3];
+                    for (int q = 0; q < 4; ++q) {
+                        f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        for (int w = 0; w < W; ++w) v += *(const f32x4*)&part[buf][w][r * kChunkN + cb + 4 * q];
+                        const int n = c * kChunkN + cb + 4 * q;
+                        // N % 8 == 0: a quad is all in or all out
+                        if (r >= a.M || n >= L.N) continue;
+                        const float y0 = v[0] * alpha, y1 = v[1] * alpha;
+                        const float y2 = v[2] * alpha, y3 = v[3] * alpha;
+                        const size_t off = (size_t)r * L.N + n;
+                        if (L.y) {
+                            store_agent((uint64_t*)(L.y + off),
+                                        (uint64_t)__float_as_uint(y0) | ((uint64_t)__float_as_uint(y1) << 32));
+                            store_agent((uint64_t*)(L.y + off + 2),
+                                        (uint64_t)__float_as_uint(y2) | ((uint64_t)__float_as_uint(y3) << 32));
                         }
-                    if (r < a.M) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int n = c * kChunkN + cb + 4 * q;
-                            if (n >= L.N) continue;  // N % 8 == 0: a quad is all in or all out
-                            const float y0 = v[4 * q] * alpha, y1 = v[4 * q + 1] * alpha;
-                            const float y2 = v[4 * q + 2] * alpha, y3 = v[4 * q + 3] * alpha;
-                            const size_t off = (size_t)r * L.N + n;
-                            if (L.y) {
-                                store_agent((uint64_t*)(L.y + off),
-                                            (uint64_t)__float_as_uint(y0) | ((uint64_t)__float_as_uint(y1) << 32));
-                                store_agent((uint64_t*)(L.y + off + 2),
-                                            (uint64_t)__float_as_uint(y2) | ((uint64_t)__float_as_uint(y3) << 32));
-                            }
-                            if (L.yb) {
-                                const uint64_t lo = f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
-                                const uint64_t hi = f32_to_bf16_rne(y2) | ((uint32_t)f32_to_bf16_rne(y3) << 16);
-                                store_agent((uint64_t*)(L.yb + off), lo | (hi << 32));
-                            }
+                        if (L.yb) {
+                            const uint64_t lo = f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+                            const uint64_t hi = f32_to_bf16_rne(y2) | ((uint32_t)f32_to_bf16_rne(y3) << 16);
+                            store_agent((uint64_t*)(L.yb + off), lo | (hi << 32));
                         }
                     }
                 }
                 pend_l = l;
+                pend_c = c;
             }
-            if (un >= a.U) break;
-            if (!deps_ok(ln, pv)) {
-                // producers still running: count this wave's own unit first
-                if (pend_l >= 0) {
+            if (!more) break;
+            if (!fast) {
+                // The next unit's producers are not known complete.  The
+                // writer retires its stores and counts its unit done (no
+                // wave waits with a unit of its own uncounted); wave 0 waits
+                // for the producers; then every wave loads the next unit's
+                // activations (its weights are in the ring already).
+                if (writer) {
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     count_done();
                 }
-                wait_deps(ln);
+                if (wave == 0) wait_deps(ln);
+                __syncthreads();
+                ok = tab[ln].dep_class;
+                load_next_x();
             }
             u = un;
             l = ln;
@@ -449,16 +465,16 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
     }
 
     // exit: the last workgroup out resets the counters for the next launch
+    __shared__ uint32_t last;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (wave == 0) {
-        uint32_t old = 0;
-        if (lane == 0) old = __hip_atomic_fetch_add(a.state, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old = (uint32_t)__shfl((int)old, 0);
-        if (old == (uint32_t)G - 1) {
-            for (int i = lane; i < a.n; i += 64) store_agent(a.done + i, 0u);
-            if (lane == 0) store_agent(a.state, 0u);
-        }
+    if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(a.state, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)G - 1;
+    __syncthreads();
+    if (last) {
+        const size_t subs = (size_t)a.n * kPassSub;
+        for (size_t i = threadIdx.x; i < subs; i += blockDim.x) store_agent(a.done + i * kPassSubStride, 0u);
+        if (threadIdx.x == 0) store_agent(a.state, 0u);
     }
 }
 

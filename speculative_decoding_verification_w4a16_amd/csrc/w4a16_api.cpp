@@ -415,7 +415,7 @@ struct w4_pass {
     int n = 0, M = 0, U = 0, grid = 0;
     bool persistent = false;
     w4::PassLinear* tab = nullptr;  // device table of the linears
-    uint32_t* counters = nullptr;   // device: [n] units done per linear, then exited workgroups, error flag
+    uint32_t* counters = nullptr;   // device: units done per linear (sub-counters), exited workgroups, error flag
     std::vector<w4_pass_linear> lin;
     std::vector<w4::Plan> plans;    // per-linear launches (M > kPassMaxM)
     w4::Workspace ws{};
@@ -427,6 +427,12 @@ namespace {
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
 };
+
+std::vector<int> sorted_deps(const w4_pass_linear& d) {
+    std::vector<int> v(d.deps, d.deps + d.ndeps);
+    std::sort(v.begin(), v.end());
+    return v;
+}
 
 Range range_of(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
 Range lines_of(Range r) { return Range{r.lo & ~(uintptr_t)127, (r.hi + 127) & ~(uintptr_t)127}; }
@@ -560,6 +566,14 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
             t.dep[j] = j < d.ndeps ? d.deps[j] : 0;
             t.dep_units[j] = j < d.ndeps ? (int)chunks(linears[d.deps[j]].N) : 0;
         }
+        // linears with the same set of producers share a class: once one
+        // has seen its producers complete, the others need not wait
+        t.dep_class = -1;
+        if (d.ndeps > 0) {
+            const std::vector<int> mine = sorted_deps(d);
+            for (int j = 0; j <= i && t.dep_class < 0; ++j)
+                if (linears[j].ndeps == d.ndeps && sorted_deps(linears[j]) == mine) t.dep_class = j;
+        }
         U += t.NC;
     }
     p->U = U;
@@ -578,9 +592,10 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
         }
         p->grid = std::max(1, std::min(U, cus));
         e = hipMalloc((void**)&p->tab, sizeof(w4::PassLinear) * n);
-        if (e == hipSuccess) e = hipMalloc((void**)&p->counters, sizeof(uint32_t) * (n + 2));
+        const size_t words = w4::pass_counter_words(n);
+        if (e == hipSuccess) e = hipMalloc((void**)&p->counters, sizeof(uint32_t) * words);
         if (e == hipSuccess) e = hipMemcpy(p->tab, tab.data(), sizeof(w4::PassLinear) * n, hipMemcpyHostToDevice);
-        if (e == hipSuccess) e = hipMemset(p->counters, 0, sizeof(uint32_t) * (n + 2));
+        if (e == hipSuccess) e = hipMemset(p->counters, 0, sizeof(uint32_t) * words);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) {
             pass_free(p);
@@ -613,8 +628,10 @@ int w4_pass_run(w4_pass* p, void* stream) {
     if (e != hipSuccess) return hip_fail("hipGetDevice", e);
     if (dev != p->device) return W4_ERR_INVALID;
     if (p->persistent)
-        return hip_status("pass launch", w4::launch_pass(p->tab, p->n, p->U, p->M, p->counters, p->counters + p->n,
-                                                          p->spin_limit, p->grid, (hipStream_t)stream));
+        return hip_status("pass launch",
+                          w4::launch_pass(p->tab, p->n, p->U, p->M, p->counters,
+                                          p->counters + w4::pass_counter_words(p->n) - 2, p->spin_limit, p->grid,
+                                          (hipStream_t)stream));
     for (int i = 0; i < p->n; ++i) {
         const w4_pass_linear& d = p->lin[i];
         e = w4::launch_linear_io(p->plans[i], d.x, d.qweight_t, d.scales_t, d.zeros_t, p->M, d.N, d.K, d.y,
@@ -630,10 +647,11 @@ int w4_pass_check(w4_pass* p, void* stream) {
     if (e != hipSuccess) return hip_fail("hipStreamSynchronize", e);
     if (!p->persistent || !p->counters) return W4_OK;
     uint32_t flag = 0;
-    e = hipMemcpy(&flag, p->counters + p->n + 1, sizeof(flag), hipMemcpyDeviceToHost);
+    uint32_t* const err = p->counters + w4::pass_counter_words(p->n) - 1;
+    e = hipMemcpy(&flag, err, sizeof(flag), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail("hipMemcpy(pass flag)", e);
     if (flag == 0) return W4_OK;
-    e = hipMemset(p->counters + p->n + 1, 0, sizeof(uint32_t));
+    e = hipMemset(err, 0, sizeof(uint32_t));
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail("hipMemset(pass flag)", e);
     return W4_ERR_TIMEOUT;
