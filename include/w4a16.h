@@ -26,12 +26,17 @@
  *    stream has drained.
  *  - Arguments are validated before any HIP call; a failed check returns a
  *    status and launches nothing.  The library never prints or aborts.
- *  - Hidden state: one 64 MiB split-K workspace per device, allocated on
- *    the first call that needs it (or by w4_init) and kept until the
- *    process ends.  A linear with a K split runs as two launches on the
- *    caller's stream (the streaming kernel, then the reduction of its
- *    partials).  Calls that overlap in time on one device (different
- *    streams) share the workspace and must not run concurrently.
+ *  - Hidden state: per device, three workspaces allocated together on the
+ *    first call that needs one (or by w4_init) and kept until the process
+ *    ends -- 64 MiB of split-K partials, 1 MiB for the acceptance step, 48
+ *    MiB for tree attention (113 MiB).  A linear with a K split runs as two
+ *    launches on the caller's stream (the streaming kernel, then the
+ *    reduction of its partials).  Calls that overlap in time on one device
+ *    (different streams, or threads) share these workspaces and must not
+ *    run concurrently; calls on one stream are ordered by it.
+ *    w4a16_linear_out_noalloc uses a static array of its own instead (its
+ *    calls must not overlap each other either), and a persistent verify
+ *    pass (w4_pass.h, M <= 16) only its own counters.
  */
 #ifndef W4A16_H
 #define W4A16_H

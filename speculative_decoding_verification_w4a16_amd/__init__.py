@@ -16,7 +16,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libw4a16.so")
+# W4A16_LIB selects another build of the same library (the tests use it to
+# load the host-sanitizer build); by default the in-tree libw4a16.so.
+LIB_PATH = os.environ.get("W4A16_LIB") or os.path.join(HERE, "libw4a16.so")
 
 W4_OK, W4_ERR_INVALID, W4_ERR_UNSUPPORTED, W4_ERR_HIP, W4_ERR_TIMEOUT = 0, 1, 2, 3, 4
 W4_PASS_MAX_DEPS = 4

@@ -56,19 +56,30 @@ int device_state(w4::Workspace* out, void** accept = nullptr, float** tree = nul
     if (!st.ready) {
         e = w4::set_kernel_attributes();
         if (e != hipSuccess) return hip_fail("hipFuncSetAttribute", e);
-        void* p = nullptr;
-        e = hipMalloc(&p, w4::kWorkspaceBytes);
-        if (e != hipSuccess) return hip_fail("hipMalloc(workspace)", e);
-        st.ws.partial = (float*)p;
+        // all three workspaces or none (a failed call leaves nothing behind
+        // and the next call tries again)
+        void* part = nullptr;
+        void* acc = nullptr;
+        void* tree = nullptr;
+        const char* what = "hipMalloc(workspace)";
+        e = hipMalloc(&part, w4::kWorkspaceBytes);
+        if (e == hipSuccess) {
+            what = "hipMalloc(acceptance workspace)";
+            e = hipMalloc(&acc, w4::kAcceptWorkspaceBytes);
+        }
+        if (e == hipSuccess) {
+            what = "hipMalloc(tree attention workspace)";
+            e = hipMalloc(&tree, w4::kTreeWorkspaceBytes);
+        }
+        if (e != hipSuccess) {
+            if (part) (void)hipFree(part);
+            if (acc) (void)hipFree(acc);
+            return hip_fail(what, e);
+        }
+        st.ws.partial = (float*)part;
         st.ws.partial_bytes = w4::kWorkspaceBytes;
-        p = nullptr;
-        e = hipMalloc(&p, w4::kAcceptWorkspaceBytes);
-        if (e != hipSuccess) return hip_fail("hipMalloc(acceptance workspace)", e);
-        st.accept = p;
-        p = nullptr;
-        e = hipMalloc(&p, w4::kTreeWorkspaceBytes);
-        if (e != hipSuccess) return hip_fail("hipMalloc(tree attention workspace)", e);
-        st.tree = (float*)p;
+        st.accept = acc;
+        st.tree = (float*)tree;
         st.ready = true;
     }
     if (out) *out = st.ws;
