@@ -224,15 +224,17 @@ def source_digest():
     HBM byte counters in profiles/traffic.json were taken on)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_verification_w4a16_amd", "csrc")
-    for f in ("w4_internal.h", "w4a16_kernels.hip"):
+    for f in ("w4_internal.h", "w4_device.h", "w4a16_kernels.hip", "w4_pass.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(M: int):
-    """HBM bytes per linear of the pass at M from the committed PMC summary,
-    if it was taken on the current kernel sources; else None."""
+    """HBM bytes per launch of the pass at M (the whole pass for the
+    persistent pass kernel, one linear for per-linear launches) from the
+    committed PMC summary, if it was taken on the current kernel sources;
+    else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -244,22 +246,31 @@ def traffic_from_profiles(M: int):
     if data.get("source_digest") != source_digest():
         return None
     ent = data.get("passes", {}).get(str(M))
-    return None if ent is None else ent.get("hbm_bytes_per_linear")
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(host, budget_s=20.0):
     """The oracle, as it stands, on a bounded sample of the workload: the
     sweep's linears held in host memory (layer 0, then the parity layers), each
     at the pass M = 1, 5 and 64, one (layer, M, linear) unit at a time until
-    about budget_s seconds of CPU work."""
+    about budget_s seconds of CPU work.  Besides the rate: the host's core
+    count, the BLAS numpy calls and the threads it used, the oracle's two
+    steps timed apart per (linear, M) -- dequantisation (unpack, (q - z) * s
+    in float64) and the float64 products -- and one unit on a single thread."""
     import synth
     from oracle import linear64
+    from oracle.w4a16_ref import _rows as rows64, _weights64 as weights64
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         cores = os.cpu_count() or 1
+    blas = [dict(api=i.get("user_api"), lib=i.get("internal_api"), version=i.get("version"),
+                 threads=i.get("num_threads")) for i in threadpool_info() if i.get("user_api") == "blas"]
+    blas_threads = max([b["threads"] or 0 for b in blas] or [cores])
     units, secs, nbytes = 0, 0.0, 0
+    steps = {}  # "linear M" -> [dequant s, product s, units]
     layers = sorted({L for (L, _) in host if L is not None})
     xs = {}
     for L in layers:
@@ -271,15 +282,42 @@ def cpu_baseline(host, budget_s=20.0):
                 lin = host[key]
                 if K not in xs:
                     xs[K] = synth.gen_x(64, K)
-                t = time.perf_counter()
-                linear64(xs[K][:M], lin["qweight"], lin["scales"], lin["zeros"])
-                secs += time.perf_counter() - t
+                # linear64 is its two steps in turn: the float64 weights
+                # (unpack, dequantise), then the products row by row
+                t0 = time.perf_counter()
+                W64 = weights64(lin["qweight"], lin["scales"], lin["zeros"], 128)
+                t1 = time.perf_counter()
+                rows64(xs[K][:M], W64)
+                t2 = time.perf_counter()
+                del W64
+                secs += t2 - t0
                 nbytes += alg_bytes(M, N, K)
                 units += 1
-    return {"value": round(nbytes / secs / 1e12, 6), "unit": "TB/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 oracle (numpy, BLAS threads={cores}) on {units} (layer, M, linear) units of the "
-                      f"sweep (layers {layers}, M in {list(PASS_M)}, in that order until ~{budget_s:.0f} s): "
-                      f"{nbytes / 1e9:.3f} GB of algorithmic traffic in {secs:.2f} s"}
+                st = steps.setdefault(f"{name} M={M}", [0.0, 0.0, 0])
+                st[0] += t1 - t0
+                st[1] += t2 - t1
+                st[2] += 1
+    # one unit on one thread: layer 0's q at M = 1
+    single = None
+    key = (layers[0], "q") if layers else None
+    if key in host:
+        lin = host[key]
+        N, K = next((n, k) for (nm, n, k) in synth.LAYER_LINEARS if nm == "q")
+        with threadpool_limits(limits=1, user_api="blas"):
+            t = time.perf_counter()
+            linear64(synth.gen_x(1, K), lin["qweight"], lin["scales"], lin["zeros"])
+            dt = time.perf_counter() - t
+        single = {"linear": f"q {N}x{K}", "M": 1, "seconds": round(dt, 3),
+                  "value": round(alg_bytes(1, N, K) / dt / 1e12, 6), "unit": "TB/s", "threads": 1}
+    return {"value": round(nbytes / secs / 1e12, 6), "unit": "TB/s", "cores": blas_threads, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "affinity_cores": cores, "blas": blas,
+            "steps_seconds": {k: {"dequant": round(v[0], 3), "product": round(v[1], 3), "units": v[2]}
+                              for k, v in steps.items()},
+            "single_thread": single,
+            "sample": f"float64 oracle (numpy, BLAS threads={blas_threads}) on {units} (layer, M, linear) units of "
+                      f"the sweep (layers {layers}, M in {list(PASS_M)}, in that order until ~{budget_s:.0f} s): "
+                      f"{nbytes / 1e9:.3f} GB of algorithmic traffic in {secs:.2f} s; steps_seconds: the "
+                      f"oracle's two steps (float64 weights, then products) timed apart"}
 
 
 # ---------------------------------------------------------------------------
@@ -618,13 +656,14 @@ def copy_calibration(torch, w4, mib):
 
 
 def traffic_from_pmc(fetch_dir, write_dir, copy_mib, out_path):
-    """HBM bytes per linear of each sweep pass from two rocprofv3 --pmc runs of
-    the sweep (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by
-    what the counter reads for w4_bench_copy of copy_mib MiB.  A linear is its
-    streaming kernel plus the split-K reductions dispatched right after it;
-    the streaming kernel names the pass (GEMV: M=1, direct MFMA: M=5, LDS
-    MFMA: M=64).  Writes profiles/traffic.json (tagged with the kernel-source
-    digest) and returns it."""
+    """HBM bytes per launch of each sweep pass from two rocprofv3 --pmc runs
+    of the sweep (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
+    by what the counter reads for w4_bench_copy of copy_mib MiB.  M = 1 and 5:
+    a launch is one dispatch of the persistent pass kernel (GEMV form: M = 1,
+    MFMA form: M = 5), the whole pass.  M = 64: a launch is one linear, the
+    LDS-ring MFMA kernel plus the split-K reduction dispatched right after it
+    when K is split.  Writes profiles/traffic.json (tagged with the
+    kernel-source digest) and returns it."""
     import csv
     import glob
 
@@ -639,30 +678,39 @@ def traffic_from_pmc(fetch_dir, write_dir, copy_mib, out_path):
                 names[i] = r["Kernel_Name"]
         return vals, names
 
-    out = {"source_digest": source_digest(), "copy_calibration_mib": copy_mib, "passes": {}}
+    def pass_of(name):
+        if "w4_pass_kernel<0" in name:
+            return "1"
+        if "w4_pass_kernel<1" in name:
+            return "5"
+        if "w4a16_mfma_lds_kernel" in name:
+            return "64"
+        return None
+
+    out = {"source_digest": source_digest(), "copy_calibration_mib": copy_mib,
+           "launch": {"1": "pass", "5": "pass", "64": "linear"}, "passes": {}}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals, names = per_dispatch(d, counter)
         copies = [vals[i] for i in vals if "bench_copy" in names[i]]
         factor = (copy_mib * 1024.0) / (sum(copies) / len(copies))  # true KiB per counted KiB
         out[counter + "_factor"] = round(factor, 4)
-        pass_of = {"gemv": "1", "direct": "5", "lds": "64"}
         sums, counts, cur = {}, {}, None
         for i in sorted(vals):
             n = names[i]
             if "splitk_reduce" in n:
-                if cur is not None:
+                if cur == "64":
                     sums[cur] += vals[i] * factor * 1024
                 continue
-            cur = next((m for k, m in pass_of.items() if f"w4a16_{'mfma_' if k != 'gemv' else ''}{k}" in n), None)
+            cur = pass_of(n)
             if cur is not None:
                 sums[cur] = sums.get(cur, 0.0) + vals[i] * factor * 1024
                 counts[cur] = counts.get(cur, 0) + 1
         for m in sums:
-            ent = out["passes"].setdefault(m, {"linears_counted": counts[m]})
-            ent[counter.lower() + "_bytes_per_linear"] = int(sums[m] / counts[m])
+            ent = out["passes"].setdefault(m, {"launches_counted": counts[m]})
+            ent[counter.lower() + "_bytes_per_launch"] = int(sums[m] / counts[m])
     for m, ent in out["passes"].items():
-        ent["hbm_bytes_per_linear"] = ent.get("fetch_size_bytes_per_linear", 0) + \
-            ent.get("write_size_bytes_per_linear", 0)
+        ent["hbm_bytes_per_launch"] = ent.get("fetch_size_bytes_per_launch", 0) + \
+            ent.get("write_size_bytes_per_launch", 0)
     with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
     return out
@@ -706,19 +754,26 @@ def shapes_report(args):
                     w4.linear(x[:M], pk, y=y[:M], splits=args.splits, kwaves=args.kwaves)
             g.replay()
             torch.cuda.synchronize()
-            best = float("inf")
-            for _ in range(max(3, args.steps)):
+            # 20 repeats of at least 200 calls each; the figure is the median
+            # of the repeats' per-call means
+            replays = -(-200 // R)
+            per_call = []
+            for _ in range(20):
                 s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 s0.record()
-                g.replay()
+                for _ in range(replays):
+                    g.replay()
                 s1.record()
                 s1.synchronize()
-                best = min(best, s0.elapsed_time(s1) * 1e3 / R)
+                per_call.append(s0.elapsed_time(s1) * 1e3 / (R * replays))
+            med = float(np.median(per_call))
             B, F = alg_bytes(M, N, K), alg_flops(M, N, K)
             t_roof = max(B / (HBM_PEAK_GBS * 1e9), F / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
-            print(json.dumps({"linear": name, "N": N, "K": K, "M": M, "us": round(best, 3),
-                              "tbps": round(B / (best * 1e-6) / 1e12, 4), "roofline_frac": round(t_roof / best, 4),
-                              "mfma_util": round(F / (best * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+            print(json.dumps({"linear": name, "N": N, "K": K, "M": M, "us": round(med, 3),
+                              "us_min": round(min(per_call), 3), "us_max": round(max(per_call), 3),
+                              "protocol": f"median of 20 repeats x {R * replays} calls",
+                              "tbps": round(B / (med * 1e-6) / 1e12, 4), "roofline_frac": round(t_roof / med, 4),
+                              "mfma_util": round(F / (med * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
                               "plan": plan, "rotation_copies": R}), flush=True)
             del g
         del copies, base
