@@ -98,9 +98,14 @@ constexpr int kPassMaxDeps = 4;
 // queue every unit's increment behind the others.)
 constexpr int kPassSub = 64;
 constexpr int kPassSubStride = 16;  // dwords between sub-counters
-// dwords of the counter block of n linears: the sub-counters, then the
-// exited-workgroup count and the error flag
-constexpr size_t pass_counter_words(int n) { return (size_t)n * kPassSub * kPassSubStride + 2; }
+// dwords of the counter block of n linears with `arrivals` split chunks: the
+// sub-counters, the split chunks' arrival counts, then the exited-workgroup
+// count and the error flag
+constexpr size_t pass_counter_words(int n, int arrivals) {
+    return (size_t)n * kPassSub * kPassSubStride + (size_t)arrivals + 2;
+}
+// fp32 values of one partial tile of a K-split unit: its rows x 64 columns
+constexpr int pass_tile_floats(int M) { return (M == 1 ? 1 : 16) * 64; }
 
 // One linear of a pass, as the kernel reads it (device table).
 struct PassLinear {
@@ -112,16 +117,29 @@ struct PassLinear {
     uint16_t* yb;        // [M][N] bf16, or null
     float alpha;         // output scale
     int N, K, NC, G;     // NC chunks of 64 columns, G groups of 128
-    int unit0;           // the pass's unit number of chunk 0
-    int kw;              // streaming waves with groups: min(kPassWaves, G)
+    int unit0;           // the pass's unit number of the linear's first unit (chunk 0, slice 0)
+    int kw;              // streaming waves with groups: min(kPassWaves, groups of the smallest slice)
     int ndep;
     int dep[kPassMaxDeps];        // producer linears
-    int dep_units[kPassMaxDeps];  // their unit (chunk) counts
+    int dep_units[kPassMaxDeps];  // their chunk counts
     int dep_class;       // the first linear with the same set of producers (-1: none)
+    int S, gps;          // K slices per chunk (units per chunk) and groups per slice
+    int part0, arr0;     // S > 1: first partial tile and first arrival counter of the linear
 };
 
-hipError_t launch_pass(const PassLinear* tab, int n, int U, int M, uint32_t* done, uint32_t* state,
-                       uint32_t spin_limit, int grid, hipStream_t stream);
+// One launch of the pass kernel.
+struct PassLaunch {
+    const PassLinear* tab;  // device table
+    int n, U, M;            // linears, units, rows
+    uint32_t* done;         // sub-counters, then `arrivals` arrival counts
+    int arrivals;
+    uint32_t* state;        // [0] exited workgroups, [1] error flag
+    float* part;            // partial tiles of the K-split units (or null)
+    uint32_t spin_limit;
+    int grid;
+};
+
+hipError_t launch_pass(const PassLaunch& l, hipStream_t stream);
 
 // Workgroups of the pass kernel for M rows that fit one CU at once.
 hipError_t pass_occupancy(int M, int* per_cu);

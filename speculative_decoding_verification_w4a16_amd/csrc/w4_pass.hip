@@ -89,16 +89,23 @@ __device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t load_agent64(const uint64_t* p) {
+    return __hip_atomic_load((const __attribute__((address_space(1))) uint64_t*)p, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // The table of linears is a separate `const __restrict__` kernel argument:
 // read-only for the whole launch, so the compiler reads it with scalar loads,
 // which wait on their own counter and never on the weight ring.
 struct PassArgs {
     int n;                // linears
-    int U;                // units (sum of the linears' chunk counts)
+    int U;                // units (sum over the linears of chunks x K slices)
     int M;                // rows (verified tokens)
-    uint32_t* done;       // units done per linear: kPassSub sub-counters each (zero between launches)
+    uint32_t* done;       // chunks done per linear: kPassSub sub-counters each (zero between launches)
+    uint32_t* arr;        // slices arrived per split chunk (zero between launches)
+    int narr;
     uint32_t* state;      // [0] workgroups exited, [1] error flag (sticky)
+    float* part;          // partial tiles of the K-split units
     uint32_t spin_limit;  // polls before a wait gives up
     uint32_t mask, magic; // the unpack's constants (see unpack_biased)
 };
@@ -119,10 +126,12 @@ __device__ __forceinline__ const W4_GLOBAL T* as_global(const T* p) {
     return (const W4_GLOBAL T*)p;
 }
 
-// One wave's share of a unit: groups [g0, g0 + ng) of chunk c of linear l,
-// in at least two rounds of R steps (steps past ng are padding: their loads
-// are clamped to the share's last group, their results unused).  Two rounds
-// at least, so that every unit runs one first round and one last round.
+// A unit is slice s of chunk c of linear l (the linear's units in chunk
+// order, its S slices of K adjacent): groups [s gps, min(G, (s + 1) gps)).
+// One wave's share of it is groups [g0, g0 + ng), in at least two rounds of R
+// steps (steps past ng are padding: their loads are clamped to the share's
+// last group, their results unused).  Two rounds at least, so that every
+// unit runs one first round and one last round.
 struct WaveUnit {
     int ng, nr;
     const W4_GLOBAL u32x4* wp;     // weights of group g0, this lane's 16 bytes
@@ -135,12 +144,15 @@ template <int R>
 __device__ __forceinline__ WaveUnit wave_unit(const PassLinear* __restrict__ tab, const PassArgs& a, int l, int u,
                                               int wave, int lane, int W) {
     const PassLinear& L = tab[l];
-    const int c = u - L.unit0;
+    const int cs = u - L.unit0;
+    const int c = cs / L.S;
     const int G = L.G, kw = L.kw;
-    int g0 = 0, ng = 0;
+    const int sg0 = (cs - c * L.S) * L.gps;
+    const int sng = min(G, sg0 + L.gps) - sg0;
+    int g0 = sg0, ng = 0;
     if (wave < kw) {
-        g0 = G * wave / kw;
-        ng = G * (wave + 1) / kw - g0;
+        g0 = sg0 + sng * wave / kw;
+        ng = sg0 + sng * (wave + 1) / kw - g0;
     }
     WaveUnit w;
     w.ng = ng;
@@ -323,13 +335,18 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
         // wait.  Both ways the ring is loaded in the same order (weights of
         // slots 0..R-1, then activations of slots 0..R-1), so the compiler's
         // wait counts hold for either.
-        auto last_round = [&](int r) {
+        // `hold`: this wave writes the tile and then waits for producers --
+        // it reloads this unit's first group instead (recently read, so a
+        // cache hit), leaving little in flight behind its tile stores, which
+        // it retires before counting; it loads the next unit's weights after
+        // the wait.
+        auto last_round = [&](int r, bool hold) {
 #pragma unroll
             for (int d = 0; d < R; ++d) {
                 const int i = r * R + d;
                 if (i < cur.ng) step(d);
                 if (r == 1 && d == 0) count_done_stored();
-                load_w(d, nxt, d);
+                load_w(d, hold ? cur : nxt, hold ? 0 : d);
             }
         };
         auto load_next_x = [&]() {
@@ -365,7 +382,7 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
             const bool more = un < a.U;
             const bool fast = more && known_ready(ln);
             const bool writer = wave == cnt % W;  // the wave that stores this unit's tile
-            last_round(cur.nr - 1);
+            last_round(cur.nr - 1, writer && !fast);
             if (fast) load_next_x();
             // this wave's partial sums of the unit, into LDS
             float* dst = part[cnt & 1][wave];
@@ -386,33 +403,50 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
             }
             lds_barrier();  // the W partials of the unit are complete
             if (writer) {
-                // this wave writes the tile: W partials summed in wave order
+                // This wave writes the tile: the W partials summed in wave
+                // order, scaled by alpha, stored as fp32 and/or bf16.  A K
+                // slice of a split chunk stores its unscaled partial tile
+                // instead; the chunk's last slice to arrive sums the S
+                // partial tiles in slice order and stores the chunk's tile.
                 const PassLinear& L = tab[l];
-                const int c = u - L.unit0;
-                const float alpha = L.alpha;
+                const int cs = u - L.unit0;
+                const int c = cs / L.S;
                 const int buf = cnt & 1;
-                if (MB == 0) {
-                    float v = 0.0f;
-                    for (int w = 0; w < W; ++w) v += part[buf][w][lane];
-                    const int n = c * kChunkN + lane;
-                    const float y0 = v * alpha;
-                    if (L.y && n < L.N) store_agent((uint32_t*)(L.y + n), __float_as_uint(y0));
-                    if (L.yb) {
-                        const uint32_t b = f32_to_bf16_rne(y0);
-                        const uint32_t b1 = (uint32_t)__shfl_down((int)b, 1);
-                        if ((lane & 1) == 0 && n < L.N) store_agent((uint32_t*)(L.yb + n), b | (b1 << 16));
+                constexpr int kTile = kRows * kChunkN;
+                // the lane's element(s) of the tile: GEMV column `lane`;
+                // MFMA row r, columns cb + 4q .. + 3
+                const int r = lane >> 2, cb = (lane & 3) * 16;
+                auto wave_sum = [&](int q) {
+                    if (MB == 0) {
+                        float v = 0.0f;
+                        for (int w = 0; w < W; ++w) v += part[buf][w][lane];
+                        return f32x4{v, 0.0f, 0.0f, 0.0f};
                     }
-                } else {
-                    // lane: row r, 16 columns from cb, one quad at a time (the
-                    // next unit's ring is in flight: few registers to spare)
-                    const int r = lane >> 2, cb = (lane & 3) * 16;
+                    f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    for (int w = 0; w < W; ++w) v += *(const f32x4*)&part[buf][w][r * kChunkN + cb + 4 * q];
+                    return v;
+                };
+                auto store_tile = [&](auto&& value) {
+                    const float alpha = L.alpha;
+                    if (MB == 0) {
+                        const float y0 = value(0)[0] * alpha;
+                        const int n = c * kChunkN + lane;
+                        if (L.y && n < L.N) store_agent((uint32_t*)(L.y + n), __float_as_uint(y0));
+                        if (L.yb) {
+                            const uint32_t b = f32_to_bf16_rne(y0);
+                            const uint32_t b1 = (uint32_t)__shfl_down((int)b, 1);
+                            if ((lane & 1) == 0 && n < L.N) store_agent((uint32_t*)(L.yb + n), b | (b1 << 16));
+                        }
+                        return;
+                    }
+                    // one quad at a time (the next unit's ring is in flight:
+                    // few registers to spare)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                        for (int w = 0; w < W; ++w) v += *(const f32x4*)&part[buf][w][r * kChunkN + cb + 4 * q];
                         const int n = c * kChunkN + cb + 4 * q;
                         // N % 8 == 0: a quad is all in or all out
                         if (r >= a.M || n >= L.N) continue;
+                        const f32x4 v = value(q);
                         const float y0 = v[0] * alpha, y1 = v[1] * alpha;
                         const float y2 = v[2] * alpha, y3 = v[3] * alpha;
                         const size_t off = (size_t)r * L.N + n;
@@ -428,9 +462,61 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
                             store_agent((uint64_t*)(L.yb + off), lo | (hi << 32));
                         }
                     }
+                };
+                if (L.S == 1) {
+                    store_tile(wave_sum);
+                    pend_l = l;
+                    pend_c = c;
+                } else {
+                    float* tile = a.part + (size_t)(L.part0 + cs) * kTile;
+                    if (MB == 0) {
+                        store_agent((uint32_t*)(tile + lane), __float_as_uint(wave_sum(0)[0]));
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            if (r >= a.M) continue;
+                            const f32x4 v = wave_sum(q);
+                            float* p4 = tile + r * kChunkN + cb + 4 * q;
+                            store_agent((uint64_t*)p4, (uint64_t)__float_as_uint(v[0]) |
+                                                           ((uint64_t)__float_as_uint(v[1]) << 32));
+                            store_agent((uint64_t*)(p4 + 2), (uint64_t)__float_as_uint(v[2]) |
+                                                                 ((uint64_t)__float_as_uint(v[3]) << 32));
+                        }
+                    }
+                    // the partial tile retires before the slice arrives
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    uint32_t old = 0;
+                    if (lane == 0)
+                        old = __hip_atomic_fetch_add(a.arr + L.arr0 + c, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                    old = (uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl((int)old, 0));
+                    if (old == (uint32_t)L.S - 1) {
+                        // every other slice stored its tile before arriving
+                        const float* t0 = a.part + (size_t)(L.part0 + c * L.S) * kTile;
+                        store_tile([&](int q) {
+                            f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                            for (int s2 = 0; s2 < L.S; ++s2) {
+                                const float* p4 = t0 + (size_t)s2 * kTile;
+                                if (MB == 0) {
+                                    v[0] += __uint_as_float(load_agent((const uint32_t*)(p4 + lane)));
+                                } else {
+                                    const uint64_t lo = load_agent64((const uint64_t*)(p4 + r * kChunkN + cb + 4 * q));
+                                    const uint64_t hi =
+                                        load_agent64((const uint64_t*)(p4 + r * kChunkN + cb + 4 * q + 2));
+                                    v[0] += __uint_as_float((uint32_t)lo);
+                                    v[1] += __uint_as_float((uint32_t)(lo >> 32));
+                                    v[2] += __uint_as_float((uint32_t)hi);
+                                    v[3] += __uint_as_float((uint32_t)(hi >> 32));
+                                }
+                            }
+                            return v;
+                        });
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        pend_l = l;
+                        pend_c = c;
+                        count_done();
+                    }
                 }
-                pend_l = l;
-                pend_c = c;
             }
             if (!more) break;
             if (!fast) {
@@ -438,7 +524,8 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
                 // writer retires its stores and counts its unit done (no
                 // wave waits with a unit of its own uncounted); wave 0 waits
                 // for the producers; then every wave loads the next unit's
-                // activations (its weights are in the ring already).
+                // activations (their weights are in the ring already, except
+                // the writer's).
                 if (writer) {
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     count_done();
@@ -446,6 +533,9 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
                 if (wave == 0) wait_deps(ln);
                 __syncthreads();
                 ok = tab[ln].dep_class;
+                if (writer)
+#pragma unroll
+                    for (int d = 0; d < R; ++d) load_w(d, nxt, d);
                 load_next_x();
             }
             u = un;
@@ -474,29 +564,33 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
     if (last) {
         const size_t subs = (size_t)a.n * kPassSub;
         for (size_t i = threadIdx.x; i < subs; i += blockDim.x) store_agent(a.done + i * kPassSubStride, 0u);
+        for (int i = threadIdx.x; i < a.narr; i += blockDim.x) store_agent(a.arr + i, 0u);
         if (threadIdx.x == 0) store_agent(a.state, 0u);
     }
 }
 
 }  // namespace
 
-hipError_t launch_pass(const PassLinear* tab, int n, int U, int M, uint32_t* done, uint32_t* state,
-                       uint32_t spin_limit, int grid, hipStream_t stream) {
+hipError_t launch_pass(const PassLaunch& l, hipStream_t stream) {
     PassArgs a;
-    a.n = n;
-    a.U = U;
-    a.M = M;
-    a.done = done;
-    a.state = state;
-    a.spin_limit = spin_limit;
+    a.n = l.n;
+    a.U = l.U;
+    a.M = l.M;
+    a.done = l.done;
+    a.arr = l.done + (size_t)l.n * kPassSub * kPassSubStride;
+    a.narr = l.arrivals;
+    a.state = l.state;
+    a.part = l.part;
+    a.spin_limit = l.spin_limit;
     a.mask = kNibbleMask;
     a.magic = kBiasMagic;
+    const PassLinear* tab = l.tab;
     void* argv[] = {(void*)&tab, (void*)&a};
     const dim3 block(64 * kPassWaves);
-    if (M == 1)
-        return hipLaunchKernel((const void*)w4_pass_kernel<0, kPassWaves, kPassRing>, dim3(grid), block, argv, 0,
+    if (l.M == 1)
+        return hipLaunchKernel((const void*)w4_pass_kernel<0, kPassWaves, kPassRing>, dim3(l.grid), block, argv, 0,
                                stream);
-    return hipLaunchKernel((const void*)w4_pass_kernel<1, kPassWaves, kPassRing>, dim3(grid), block, argv, 0,
+    return hipLaunchKernel((const void*)w4_pass_kernel<1, kPassWaves, kPassRing>, dim3(l.grid), block, argv, 0,
                            stream);
 }
 

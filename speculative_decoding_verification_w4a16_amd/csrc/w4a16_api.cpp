@@ -426,7 +426,10 @@ struct w4_pass {
     int n = 0, M = 0, U = 0, grid = 0;
     bool persistent = false;
     w4::PassLinear* tab = nullptr;  // device table of the linears
-    uint32_t* counters = nullptr;   // device: units done per linear (sub-counters), exited workgroups, error flag
+    uint32_t* counters = nullptr;   // device: chunks done per linear (sub-counters), split chunks' arrivals,
+                                    // exited workgroups, error flag
+    int arrivals = 0;               // split chunks (K-split units' arrival counters)
+    float* part = nullptr;          // device: partial tiles of the K-split units
     std::vector<w4_pass_linear> lin;
     std::vector<w4::Plan> plans;    // per-linear launches (M > kPassMaxM)
     w4::Workspace ws{};
@@ -523,6 +526,7 @@ void pass_free(w4_pass* p) {
     if (!p) return;
     if (p->tab) (void)hipFree(p->tab);
     if (p->counters) (void)hipFree(p->counters);
+    if (p->part) (void)hipFree(p->part);
     delete p;
 }
 
@@ -554,8 +558,17 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
         pass_free(p);
         return hip_fail("hipGetDevice", e);
     }
+    int cus = 0;
+    if (p->persistent && n > 0) {
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
+        if (e != hipSuccess) {
+            pass_free(p);
+            return hip_fail("hipDeviceGetAttribute", e);
+        }
+    }
     std::vector<w4::PassLinear> tab(n);
-    int U = 0;
+    int U = 0, arrivals = 0;
+    size_t tiles = 0;
     for (int i = 0; i < n; ++i) {
         const w4_pass_linear& d = linears[i];
         w4::PassLinear& t = tab[i];
@@ -571,7 +584,25 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
         t.NC = (int)chunks(d.N);
         t.G = d.K / w4::kGroup;
         t.unit0 = U;
-        t.kw = std::min(w4::kPassWaves, t.G);
+        // K slices: a linear with fewer chunks than half the CUs would leave
+        // the other CUs idle while it runs (its consumers wait for all of
+        // it); its chunks are split into S slices of K, S units each, as long
+        // as every wave keeps at least two rounds of groups.  The last slice
+        // of a chunk to finish adds the slices' partial tiles in slice order.
+        t.S = 1;
+        if (p->persistent && cus >= 2 * t.NC) {
+            const int per_wave = 2 * w4::kPassRing;
+            t.S = std::max(1, std::min(cus / t.NC, t.G / (per_wave * w4::kPassWaves)));
+        }
+        t.gps = (t.G + t.S - 1) / t.S;
+        t.S = (t.G + t.gps - 1) / t.gps;
+        t.kw = std::min(w4::kPassWaves, t.G - (t.S - 1) * t.gps);
+        t.part0 = t.S > 1 ? (int)tiles : 0;
+        t.arr0 = t.S > 1 ? arrivals : 0;
+        if (t.S > 1) {
+            tiles += (size_t)t.NC * t.S;
+            arrivals += t.NC;
+        }
         t.ndep = d.ndeps;
         for (int j = 0; j < w4::kPassMaxDeps; ++j) {
             t.dep[j] = j < d.ndeps ? d.deps[j] : 0;
@@ -585,16 +616,11 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
             for (int j = 0; j <= i && t.dep_class < 0; ++j)
                 if (linears[j].ndeps == d.ndeps && sorted_deps(linears[j]) == mine) t.dep_class = j;
         }
-        U += t.NC;
+        U += t.NC * t.S;
     }
     p->U = U;
+    p->arrivals = arrivals;
     if (p->persistent && n > 0) {
-        int cus = 0;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device);
-        if (e != hipSuccess) {
-            pass_free(p);
-            return hip_fail("hipDeviceGetAttribute", e);
-        }
         int per_cu = 0;
         e = w4::pass_occupancy(M, &per_cu);
         if (e != hipSuccess || per_cu < 1) {
@@ -603,8 +629,10 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
         }
         p->grid = std::max(1, std::min(U, cus));
         e = hipMalloc((void**)&p->tab, sizeof(w4::PassLinear) * n);
-        const size_t words = w4::pass_counter_words(n);
+        const size_t words = w4::pass_counter_words(n, arrivals);
         if (e == hipSuccess) e = hipMalloc((void**)&p->counters, sizeof(uint32_t) * words);
+        if (e == hipSuccess && tiles > 0)
+            e = hipMalloc((void**)&p->part, sizeof(float) * tiles * w4::pass_tile_floats(M));
         if (e == hipSuccess) e = hipMemcpy(p->tab, tab.data(), sizeof(w4::PassLinear) * n, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemset(p->counters, 0, sizeof(uint32_t) * words);
         if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -638,11 +666,20 @@ int w4_pass_run(w4_pass* p, void* stream) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail("hipGetDevice", e);
     if (dev != p->device) return W4_ERR_INVALID;
-    if (p->persistent)
-        return hip_status("pass launch",
-                          w4::launch_pass(p->tab, p->n, p->U, p->M, p->counters,
-                                          p->counters + w4::pass_counter_words(p->n) - 2, p->spin_limit, p->grid,
-                                          (hipStream_t)stream));
+    if (p->persistent) {
+        w4::PassLaunch l;
+        l.tab = p->tab;
+        l.n = p->n;
+        l.U = p->U;
+        l.M = p->M;
+        l.done = p->counters;
+        l.arrivals = p->arrivals;
+        l.state = p->counters + w4::pass_counter_words(p->n, p->arrivals) - 2;
+        l.part = p->part;
+        l.spin_limit = p->spin_limit;
+        l.grid = p->grid;
+        return hip_status("pass launch", w4::launch_pass(l, (hipStream_t)stream));
+    }
     for (int i = 0; i < p->n; ++i) {
         const w4_pass_linear& d = p->lin[i];
         e = w4::launch_linear_io(p->plans[i], d.x, d.qweight_t, d.scales_t, d.zeros_t, p->M, d.N, d.K, d.y,
@@ -658,7 +695,7 @@ int w4_pass_check(w4_pass* p, void* stream) {
     if (e != hipSuccess) return hip_fail("hipStreamSynchronize", e);
     if (!p->persistent || !p->counters) return W4_OK;
     uint32_t flag = 0;
-    uint32_t* const err = p->counters + w4::pass_counter_words(p->n) - 1;
+    uint32_t* const err = p->counters + w4::pass_counter_words(p->n, p->arrivals) - 1;
     e = hipMemcpy(&flag, err, sizeof(flag), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail("hipMemcpy(pass flag)", e);
     if (flag == 0) return W4_OK;

@@ -15,8 +15,10 @@ runs the external input changes and every output is filled with NaN first:
 a stale or early read shows up as a mismatch or a NaN.  Cases: the
 persistent kernel at M = 1 (GEMV) and 2, 5, 8, 16 (MFMA), the per-linear
 launches at M = 17 and 64, a HIP graph replayed with eager changes between
-replays, a forced dependency-wait timeout (spin limit 0) and recovery, and
-one full-size Llama-3-70B layer at M = 1 and 5.
+replays, a forced dependency-wait timeout (spin limit 0) and recovery, a
+producer split into K slices across workgroups (the last slice of a chunk
+adds the partial tiles) read by its consumer, and one full-size
+Llama-3-70B layer at M = 1 and 5 (its down projection is K-split).
 """
 import math
 
@@ -24,7 +26,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import bf16_bits_to_f64, linear64_gemm
+from oracle import bf16_bits_to_f64, linear64_gemm, round_to_bf16
 
 from gpu_util import DEV, to_dev
 
@@ -180,6 +182,49 @@ def test_forced_wait_timeout_is_reported_and_recovered():
         ch.check("after the timeout")
     finally:
         ch.close()
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_k_split_producer_against_the_oracle(M):
+    # a producer with few chunks and a long K (8 chunks, 512 groups) is split
+    # into K slices across workgroups; the last slice of each chunk adds the
+    # partial tiles.  Its consumer reads the summed bf16 output.
+    N1, K1, N2 = 512, 65536, 1024
+    lin1, lin2 = synth.gen_linear(9100, N1, K1), synth.gen_linear(9101, N2, N1)
+    pk1 = w4.repack(to_dev(lin1["qweight"]), to_dev(lin1["scales"]), to_dev(lin1["zeros"]), N1, K1)
+    pk2 = w4.repack(to_dev(lin2["qweight"]), to_dev(lin2["scales"]), to_dev(lin2["zeros"]), N2, N1)
+    x0 = torch.empty((M, K1), dtype=torch.int16, device=DEV)
+    h = torch.empty((M, N1), dtype=torch.int16, device=DEV)
+    yf = torch.empty((M, N1), dtype=torch.float32, device=DEV)
+    y2 = torch.empty((M, N2), dtype=torch.float32, device=DEV)
+    a1 = _alpha(K1)
+    descs = [dict(x=x0, qweight_t=pk1.qweight_t, scales_t=pk1.scales_t, zeros_t=pk1.zeros_t, y=yf, y_bf16=h,
+                  N=N1, K=K1, alpha=a1, deps=[]),
+             dict(x=h, qweight_t=pk2.qweight_t, scales_t=pk2.scales_t, zeros_t=pk2.zeros_t, y=y2, y_bf16=None,
+                  N=N2, K=N1, alpha=1.0, deps=[0])]
+    hd = w4.w4_pass_create(descs, M)
+    try:
+        info = w4.w4_pass_info(hd)
+        assert info["persistent"] == 1 and info["units"] > (N1 // 64) + (N2 // 64), info  # the producer is split
+        for seed in (9200, 9300):
+            x = synth.gen_x(M, K1, seed_base=seed)
+            x0.copy_(to_dev(x))
+            for t in (h, yf, y2):
+                t.fill_(0x7FC0) if t.dtype == torch.int16 else t.fill_(float("nan"))
+            w4.w4_pass_run(hd)
+            w4.w4_pass_check(hd)
+            torch.cuda.synchronize()
+            Y1, A1 = linear64_gemm(x, lin1["qweight"], lin1["scales"], lin1["zeros"], 128, 0, N1)
+            y1 = yf.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(y1 - a1 * Y1) <= 4e-3 * a1 * A1), (M, seed, "producer")
+            hb = h.cpu().numpy().view(np.uint16)
+            assert np.array_equal(hb, round_to_bf16(yf.cpu().numpy()).astype(np.uint16)), (M, seed, "bf16 output")
+            Y2, A2 = linear64_gemm(hb, lin2["qweight"], lin2["scales"], lin2["zeros"], 128, 0, N2)
+            y2h = y2.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(y2h - Y2) <= 4e-3 * A2), (M, seed, "consumer")
+    finally:
+        torch.cuda.synchronize()
+        w4.w4_pass_destroy(hd)
 
 
 @pytest.mark.parametrize("M", [1, 5])
