@@ -194,17 +194,21 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
         auto expected = [&](int nc) { return (uint32_t)(nc / kPassSub + (lane < nc % kPassSub ? 1 : 0)); };
         auto wait_deps = [&](int l) {
             const PassLinear& L = tab[l];
-            for (int j = 0; j < L.ndep; ++j) {
-                const uint32_t* cnt = sub(L.dep[j]);
-                const uint32_t target = expected(L.dep_units[j]);
-                for (uint32_t it = 0;; ++it) {
-                    if (__ballot(load_agent(cnt) < target) == 0ull) break;
-                    if (it >= a.spin_limit || ((it & 63) == 63 && load_agent(a.state + 1) != 0u)) {
-                        if (lane == 0) store_agent(a.state + 1, 1u);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
+            if (L.ndep == 0) return;
+            for (uint32_t it = 0;; ++it) {
+                // every producer in one round trip
+                uint32_t v[kPassMaxDeps];
+#pragma unroll
+                for (int j = 0; j < kPassMaxDeps; ++j) v[j] = j < L.ndep ? load_agent(sub(L.dep[j])) : 0u;
+                bool ok = true;
+#pragma unroll
+                for (int j = 0; j < kPassMaxDeps; ++j) ok = ok && (j >= L.ndep || v[j] >= expected(L.dep_units[j]));
+                if (__ballot(!ok) == 0ull) break;
+                if (it >= a.spin_limit || ((it & 63) == 63 && load_agent(a.state + 1) != 0u)) {
+                    if (lane == 0) store_agent(a.state + 1, 1u);
+                    break;
                 }
+                __builtin_amdgcn_s_sleep(1);
             }
         };
         // The producers of every linear with the dependency class `ok` (the

@@ -583,26 +583,9 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
         t.K = d.K;
         t.NC = (int)chunks(d.N);
         t.G = d.K / w4::kGroup;
-        t.unit0 = U;
-        // K slices: a linear with fewer chunks than half the CUs would leave
-        // the other CUs idle while it runs (its consumers wait for all of
-        // it); its chunks are split into S slices of K, S units each, as long
-        // as every wave keeps at least two rounds of groups.  The last slice
-        // of a chunk to finish adds the slices' partial tiles in slice order.
         t.S = 1;
-        if (p->persistent && cus >= 2 * t.NC) {
-            const int per_wave = 2 * w4::kPassRing;
-            t.S = std::max(1, std::min(cus / t.NC, t.G / (per_wave * w4::kPassWaves)));
-        }
-        t.gps = (t.G + t.S - 1) / t.S;
-        t.S = (t.G + t.gps - 1) / t.gps;
-        t.kw = std::min(w4::kPassWaves, t.G - (t.S - 1) * t.gps);
-        t.part0 = t.S > 1 ? (int)tiles : 0;
-        t.arr0 = t.S > 1 ? arrivals : 0;
-        if (t.S > 1) {
-            tiles += (size_t)t.NC * t.S;
-            arrivals += t.NC;
-        }
+        t.gps = t.G;
+        t.kw = std::min(w4::kPassWaves, t.G);
         t.ndep = d.ndeps;
         for (int j = 0; j < w4::kPassMaxDeps; ++j) {
             t.dep[j] = j < d.ndeps ? d.deps[j] : 0;
@@ -615,6 +598,42 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
             const std::vector<int> mine = sorted_deps(d);
             for (int j = 0; j <= i && t.dep_class < 0; ++j)
                 if (linears[j].ndeps == d.ndeps && sorted_deps(linears[j]) == mine) t.dep_class = j;
+        }
+    }
+    // K slices.  The linears of one dependency class run side by side, and
+    // their consumers wait for all of them; when together they have fewer
+    // chunks than half the CUs, the other CUs would sit idle.  Their chunks
+    // are then split into S slices of K (S units each), as long as a slice
+    // keeps every wave of a workgroup busy for two rounds (measured: q and o
+    // in two slices of four waves each made the pass slower).  The last
+    // slice of a chunk to finish adds the slices' partial tiles in slice
+    // order.
+    if (p->persistent) {
+        // (the linears without producers form one class, index n)
+        std::vector<long> class_chunks(n + 1, 0);
+        for (int i = 0; i < n; ++i) class_chunks[tab[i].dep_class >= 0 ? tab[i].dep_class : n] += tab[i].NC;
+        const int per_wave = 2 * w4::kPassRing;  // groups of two rounds
+        for (int i = 0; i < n; ++i) {
+            w4::PassLinear& t = tab[i];
+            const long cc = class_chunks[t.dep_class >= 0 ? t.dep_class : n];
+            const int s_cus = (int)std::max<long>(1, cus / std::max<long>(cc, 1));
+            const int s_k = std::max(1, t.G / (w4::kPassWaves * per_wave));
+            int S = std::min(s_cus, s_k);
+            if (S > 1) {
+                t.gps = (t.G + S - 1) / S;
+                t.S = (t.G + t.gps - 1) / t.gps;
+                t.kw = std::max(1, std::min(w4::kPassWaves, (t.G - (t.S - 1) * t.gps) / per_wave));
+            }
+        }
+    }
+    for (int i = 0; i < n; ++i) {
+        w4::PassLinear& t = tab[i];
+        t.unit0 = U;
+        t.part0 = t.S > 1 ? (int)tiles : 0;
+        t.arr0 = t.S > 1 ? arrivals : 0;
+        if (t.S > 1) {
+            tiles += (size_t)t.NC * t.S;
+            arrivals += t.NC;
         }
         U += t.NC * t.S;
     }
