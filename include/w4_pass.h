@@ -45,7 +45,7 @@ extern "C" {
 
 /* One linear of a pass (host struct; pointers are device pointers). */
 typedef struct {
-    const uint16_t* x;          /* [M][K] bf16 input, 16-byte aligned */
+    const uint16_t* x;          /* bf16 input: row m at x + m * ldx, its first K values read; 16-byte aligned */
     const uint32_t* qweight_t;  /* tile-layout weights (w4_repack) */
     const uint16_t* scales_t;
     const uint16_t* zeros_t;    /* 4-byte aligned (w4a16_linear needs 2) */
@@ -55,6 +55,9 @@ typedef struct {
     int N, K;                   /* N % 8 == 0, N >= 8; K % 128 == 0, K >= 128 */
     int ndeps;                  /* 0..W4_PASS_MAX_DEPS */
     int deps[W4_PASS_MAX_DEPS]; /* indices of earlier linears whose outputs must be complete before x is read */
+    int ldx;                    /* elements between rows of x: 0 means K; else >= K and a multiple of 8 (so a
+                                   linear can read the first K columns of a wider output, e.g. the q part of a
+                                   fused q|k|v output) */
 } w4_pass_linear;
 
 typedef struct w4_pass w4_pass;
@@ -64,7 +67,8 @@ typedef struct w4_pass w4_pass;
  * the current device, once, and keeps them until w4_pass_destroy).  `linears`
  * is a host array of n entries; they run in array order at M rows each.
  *
- * Data hazards are checked, never guessed: an x that overlaps the output of
+ * Data hazards are checked, never guessed (x counts as the whole span of its
+ * M rows, from x to the end of row M - 1's K values): an x that overlaps the output of
  * an earlier linear must list that linear in `deps`; an output may not
  * overlap any input of the same or an earlier linear, any weights, or any
  * other output.  Outputs must be 128-byte aligned and, rounded out to whole
@@ -73,7 +77,8 @@ typedef struct w4_pass w4_pass;
  * linear and read by its consumers only after it is complete).  The buffers
  * must stay allocated, and are not re-checked, until w4_pass_destroy.
  * Returns W4_OK and *out, or W4_ERR_INVALID (null, negative, misaligned,
- * overlapping, a dependency on a later linear), W4_ERR_UNSUPPORTED (group,
+ * overlapping, a dependency on a later linear, ldx below K or not a
+ * multiple of 8), W4_ERR_UNSUPPORTED (group,
  * shapes, M > 64, more than W4_PASS_MAX_DEPS producers) or W4_ERR_HIP. */
 int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pass** out);
 

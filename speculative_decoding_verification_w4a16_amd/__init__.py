@@ -50,7 +50,7 @@ class W4LinearDesc(ctypes.Structure):
 
 class W4PassLinear(ctypes.Structure):
     _fields_ = [("x", _vp), ("qweight_t", _vp), ("scales_t", _vp), ("zeros_t", _vp), ("y", _vp), ("y_bf16", _vp),
-                ("alpha", ctypes.c_float), ("N", _i), ("K", _i), ("ndeps", _i), ("deps", _i * 4)]
+                ("alpha", ctypes.c_float), ("N", _i), ("K", _i), ("ndeps", _i), ("deps", _i * 4), ("ldx", _i)]
 
 
 def _sig(name, args, res=_i):
@@ -213,15 +213,16 @@ def w4a16_verify_pass(linears, M, group=GROUP, stream=None):
 
 def w4_pass_create(linears, M, group=GROUP):
     """`linears`: sequence of dicts with x, qweight_t, scales_t, zeros_t, y
-    (or None), y_bf16 (or None), N, K, and optionally alpha (1.0) and deps
-    (indices of earlier entries).  Returns the pass handle (an int)."""
+    (or None), y_bf16 (or None), N, K, and optionally alpha (1.0), deps
+    (indices of earlier entries) and ldx (elements between rows of x; 0, the
+    default, means K).  Returns the pass handle (an int)."""
     n = len(linears)
     arr = (W4PassLinear * max(1, n))()
     for i, d in enumerate(linears):
         deps = list(d.get("deps", ()))
         arr[i] = W4PassLinear(_ptr(d["x"]), _ptr(d["qweight_t"]), _ptr(d["scales_t"]), _ptr(d["zeros_t"]),
                               _ptr(d.get("y")), _ptr(d.get("y_bf16")), float(d.get("alpha", 1.0)), d["N"], d["K"],
-                              len(deps), (_i * 4)(*(deps + [0] * (4 - len(deps)))[:4]))
+                              len(deps), (_i * 4)(*(deps + [0] * (4 - len(deps)))[:4]), int(d.get("ldx", 0)))
     out = _vp()
     _check(_c["w4_pass_create"](arr, n, M, group, ctypes.byref(out)), "w4_pass_create")
     return out.value

@@ -79,9 +79,9 @@ hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweig
 
 // The same with both outputs optional (fp32 y and/or bf16 yb, at least one)
 // and the result scaled by alpha.
-hipError_t launch_linear_io(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
-                            const uint16_t* zeros_t, int M, int N, int K, float* y, uint16_t* yb, float alpha,
-                            const Workspace& ws, hipStream_t stream);
+hipError_t launch_linear_io(const Plan& p, const uint16_t* x, int ldx, const uint32_t* qweight_t,
+                            const uint16_t* scales_t, const uint16_t* zeros_t, int M, int N, int K, float* y,
+                            uint16_t* yb, float alpha, const Workspace& ws, hipStream_t stream);
 
 hipError_t launch_zero(float* y, size_t n, hipStream_t stream);
 
@@ -109,7 +109,7 @@ constexpr int pass_tile_floats(int M) { return (M == 1 ? 1 : 16) * 64; }
 
 // One linear of a pass, as the kernel reads it (device table).
 struct PassLinear {
-    const uint16_t* x;   // [M][K] bf16
+    const uint16_t* x;   // [M][ldx] bf16, the first K of each row read
     const uint32_t* qt;  // tile layout (w4_repack)
     const uint16_t* st;
     const uint16_t* zt;
@@ -117,6 +117,7 @@ struct PassLinear {
     uint16_t* yb;        // [M][N] bf16, or null
     float alpha;         // output scale
     int N, K, NC, G;     // NC chunks of 64 columns, G groups of 128
+    int ldx;             // elements between rows of x
     int unit0;           // the pass's unit number of the linear's first unit (chunk 0, slice 0)
     int kw;              // streaming waves with groups: min(kPassWaves, groups of the smallest slice)
     int ndep;

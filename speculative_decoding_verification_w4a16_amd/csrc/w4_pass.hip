@@ -162,7 +162,7 @@ __device__ __forceinline__ WaveUnit wave_unit(const PassLinear* __restrict__ tab
     w.sp = as_global((const uint64_t*)L.st) + ((size_t)c * G + g0) * 16 + t;
     w.zp = as_global((const uint32_t*)L.zt) + ((size_t)c * G + g0) * 8 + (t >> 1);
     const int row = min(t, a.M - 1);  // the GEMV reads row 0 (M = 1)
-    w.xp = as_global((const u32x4*)(L.x + (size_t)row * L.K + (size_t)g0 * kGroup + 8 * o));
+    w.xp = as_global((const u32x4*)(L.x + (size_t)row * L.ldx + (size_t)g0 * kGroup + 8 * o));
     (void)W;
     return w;
 }

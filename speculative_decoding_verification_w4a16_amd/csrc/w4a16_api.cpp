@@ -453,8 +453,17 @@ Range lines_of(Range r) { return Range{r.lo & ~(uintptr_t)127, (r.hi + 127) & ~(
 bool meets(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
 
 // Per-linear argument checks of a pass entry.
+// Elements between rows of a pass linear's x (0 means K).
+int pass_ldx(const w4_pass_linear& d) { return d.ldx == 0 ? d.K : d.ldx; }
+
+// Bytes from x to the end of row M - 1's K values.
+size_t pass_x_bytes(const w4_pass_linear& d, int M) {
+    return M > 0 ? ((size_t)(M - 1) * pass_ldx(d) + d.K) * 2 : 0;
+}
+
 int check_pass_linear(const w4_pass_linear& d, int i, int M, int group) {
     if (d.N < 0 || d.K < 0 || d.ndeps < 0) return W4_ERR_INVALID;
+    if (d.ldx != 0 && (d.ldx < d.K || d.ldx % 8 != 0)) return W4_ERR_INVALID;
     int rc = check_shape(d.N, d.K, group);
     if (rc != W4_OK) return rc;
     if (d.N < 8 || d.K < w4::kGroup || d.ndeps > W4_PASS_MAX_DEPS) return W4_ERR_UNSUPPORTED;
@@ -478,6 +487,10 @@ int check_pass_linear(const w4_pass_linear& d, int i, int M, int group) {
                           W4_KERNEL_AUTO, 0, 0, nullptr);
         if (rc != W4_OK) return rc;
     }
+    // the outputs may not overlap the whole span of a strided x either
+    const size_t xb = pass_x_bytes(d, M);
+    if (overlap(d.y, (size_t)M * d.N * 4, d.x, xb) || overlap(d.y_bf16, (size_t)M * d.N * 2, d.x, xb))
+        return W4_ERR_INVALID;
     return W4_OK;
 }
 
@@ -493,7 +506,7 @@ int check_pass_hazards(const w4_pass_linear* L, int n, int M) {
         const w4_pass_linear& d = L[i];
         size_t qb, sb, zb;
         tile_sizes(d.N, d.K, &qb, &sb, &zb);
-        xs[i] = range_of(d.x, (size_t)M * d.K * 2);
+        xs[i] = range_of(d.x, pass_x_bytes(d, M));
         ws.push_back(range_of(d.qweight_t, qb));
         ws.push_back(range_of(d.scales_t, sb));
         ws.push_back(range_of(d.zeros_t, zb));
@@ -581,6 +594,7 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
         t.alpha = d.alpha;
         t.N = d.N;
         t.K = d.K;
+        t.ldx = pass_ldx(d);
         t.NC = (int)chunks(d.N);
         t.G = d.K / w4::kGroup;
         t.S = 1;
@@ -701,7 +715,7 @@ int w4_pass_run(w4_pass* p, void* stream) {
     }
     for (int i = 0; i < p->n; ++i) {
         const w4_pass_linear& d = p->lin[i];
-        e = w4::launch_linear_io(p->plans[i], d.x, d.qweight_t, d.scales_t, d.zeros_t, p->M, d.N, d.K, d.y,
+        e = w4::launch_linear_io(p->plans[i], d.x, pass_ldx(d), d.qweight_t, d.scales_t, d.zeros_t, p->M, d.N, d.K, d.y,
                                  d.y_bf16, d.alpha, p->ws, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail("pass linear launch", e);
     }

@@ -161,6 +161,7 @@ struct LinearArgs {
     float alpha;     // output scale (1 for the plain linear)
     float* ws;
     int M, N, K;
+    int ldx;         // elements between consecutive rows of x (>= K)
     int NC, KB, G;
     int gps, splits, ntiles;
     int kw;          // waves of a workgroup that split one chunk's K range (1: one chunk per wave)
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(kMaxThreads) void w4a16_mfma_direct_kernel(LinearAr
     for (int mb = 0; mb < MB; ++mb) {
         const int row = 16 * mb + t;
         xvalid[mb] = row < a.M;
-        xp[mb] = (const u32x4*)(a.x + (size_t)min(row, a.M - 1) * a.K + (size_t)g0 * kGroup + 8 * o);
+        xp[mb] = (const u32x4*)(a.x + (size_t)min(row, a.M - 1) * a.ldx + (size_t)g0 * kGroup + 8 * o);
     }
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2});
 
@@ -597,7 +598,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (line >= 4 * MB) line = 4 * MB >= WV ? line - WV : line % (4 * MB);
         xline[ii] = line;
         const int r = 4 * line + o;
-        xoff[ii] = (m0 + min(r, ml - 1)) * a.K + 8 * (t ^ (r & 15));
+        xoff[ii] = (m0 + min(r, ml - 1)) * a.ldx + 8 * (t ^ (r & 15));
     }
     const uint16_t* xg = a.x + (size_t)g0 * kGroup;
     auto issue_x = [&](int buf, int gl) {
@@ -1058,13 +1059,13 @@ hipError_t launch_unpack(const uint32_t* qweight_t, const uint16_t* zeros_t, int
 hipError_t launch_linear(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
                          const uint16_t* zeros_t, int M, int N, int K, void* y, int out_bf16, const Workspace& ws,
                          hipStream_t stream) {
-    return launch_linear_io(p, x, qweight_t, scales_t, zeros_t, M, N, K, out_bf16 ? nullptr : (float*)y,
+    return launch_linear_io(p, x, K, qweight_t, scales_t, zeros_t, M, N, K, out_bf16 ? nullptr : (float*)y,
                             out_bf16 ? (uint16_t*)y : nullptr, 1.0f, ws, stream);
 }
 
-hipError_t launch_linear_io(const Plan& p, const uint16_t* x, const uint32_t* qweight_t, const uint16_t* scales_t,
-                            const uint16_t* zeros_t, int M, int N, int K, float* y, uint16_t* yb, float alpha,
-                            const Workspace& ws, hipStream_t stream) {
+hipError_t launch_linear_io(const Plan& p, const uint16_t* x, int ldx, const uint32_t* qweight_t,
+                            const uint16_t* scales_t, const uint16_t* zeros_t, int M, int N, int K, float* y,
+                            uint16_t* yb, float alpha, const Workspace& ws, hipStream_t stream) {
     LinearArgs a;
     a.x = x;
     a.qt = (const u32x4*)qweight_t;
@@ -1077,6 +1078,7 @@ hipError_t launch_linear_io(const Plan& p, const uint16_t* x, const uint32_t* qw
     a.M = M;
     a.N = N;
     a.K = K;
+    a.ldx = ldx;
     a.NC = ceil_div(N, kChunkN);
     a.KB = K / kKBlock;
     a.G = K / kGroup;

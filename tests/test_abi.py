@@ -277,9 +277,9 @@ def test_noalloc_refuses_a_split_past_its_scratch_before_any_launch():
     assert w4.W4_OK == 0
 
 
-def _pl(x, y, yb=0, N=256, K=512, deps=(), qt=0x100000, st=0x200000, zt=0x300000, alpha=1.0):
+def _pl(x, y, yb=0, N=256, K=512, deps=(), qt=0x100000, st=0x200000, zt=0x300000, alpha=1.0, ldx=0):
     d = list(deps)
-    return w4.W4PassLinear(x, qt, st, zt, y, yb, alpha, N, K, len(d), (ctypes.c_int * 4)(*(d + [0] * 4)[:4]))
+    return w4.W4PassLinear(x, qt, st, zt, y, yb, alpha, N, K, len(d), (ctypes.c_int * 4)(*(d + [0] * 4)[:4]), ldx)
 
 
 def _create(entries, M=4):
@@ -296,6 +296,10 @@ def test_pass_validation_before_any_hip_call():
     # a valid chain passes validation and only then needs the device (none here: W4_ERR_HIP)
     rc = _create(ok_chain)
     assert rc in (w4.W4_OK, w4.W4_ERR_HIP), rc
+    # a consumer reading the first 512 columns of a 1024-column bf16 output (ldx = 1024)
+    strided = [_pl(X0, 0, yb=Y0, N=1024, **wt(0)), _pl(Y0, Y1, K=512, ldx=1024, deps=[0], **wt(1))]
+    rc = _create(strided)
+    assert rc in (w4.W4_OK, w4.W4_ERR_HIP), rc
     bad = {
         "reads an earlier output without listing it": [_pl(X0, Y0, **wt(0)), _pl(Y0, Y1, K=256, **wt(1))],
         "depends on a later linear": [_pl(X0, Y0, deps=[1], **wt(0)), _pl(X0 + 0x100000, Y1, **wt(1))],
@@ -311,6 +315,13 @@ def test_pass_validation_before_any_hip_call():
         "zeros not 4-byte aligned": [_pl(X0, Y0, qt=0x10000000, st=0x20000000, zt=0x30000002)],
         "alpha not finite": [_pl(X0, Y0, alpha=float("inf"), **wt(0))],
         "duplicate producer": [_pl(X0, Y0, **wt(0)), _pl(Y0, Y1, K=256, deps=[0, 0], **wt(1))],
+        "ldx below K": [_pl(X0, Y0, ldx=256, **wt(0))],
+        "ldx not a multiple of 8": [_pl(X0, Y0, ldx=516, **wt(0))],
+        # x rows 8 KB apart: the span of 4 rows reaches the later linear's output at X0 + 0x4000
+        "a strided input's span meets a later output": [_pl(X0, Y0, ldx=4096, **wt(0)),
+                                                        _pl(X0 + 0x200000, X0 + 0x4000, **wt(1))],
+        "a strided read of an output not listed": [_pl(X0, 0, yb=Y0, N=1024, **wt(0)),
+                                                   _pl(Y0, Y1, K=512, ldx=1024, **wt(1))],
     }
     for name, entries in bad.items():
         assert _create(entries) == w4.W4_ERR_INVALID, name

@@ -17,7 +17,8 @@ persistent kernel at M = 1 (GEMV) and 2, 5, 8, 16 (MFMA), the per-linear
 launches at M = 17 and 64, a HIP graph replayed with eager changes between
 replays, a forced dependency-wait timeout (spin limit 0) and recovery, a
 producer split into K slices across workgroups (the last slice of a chunk
-adds the partial tiles) read by its consumer, and one full-size
+adds the partial tiles) read by its consumer, a consumer reading a column
+slice of a fused output through a row stride, and one full-size
 Llama-3-70B layer at M = 1 and 5 (its down projection is K-split).
 """
 import math
@@ -222,6 +223,42 @@ def test_k_split_producer_against_the_oracle(M):
             Y2, A2 = linear64_gemm(hb, lin2["qweight"], lin2["scales"], lin2["zeros"], 128, 0, N2)
             y2h = y2.cpu().numpy().astype(np.float64)
             assert np.all(np.abs(y2h - Y2) <= 4e-3 * A2), (M, seed, "consumer")
+    finally:
+        torch.cuda.synchronize()
+        w4.w4_pass_destroy(hd)
+
+
+@pytest.mark.parametrize("M", [1, 5, 17, 64])
+def test_consumer_reads_a_column_slice_of_a_fused_output(M):
+    # a fused producer (q|k|v-like: N = 1024 + 256 + 256) writes [M, 1536];
+    # its consumer reads the first 1024 columns of each row (ldx = 1536), as
+    # o reads the q part of a fused q|k|v output -- the persistent kernel at
+    # M <= 16, the per-linear launches above
+    H, NF, N2 = 1024, 1536, 512
+    lin1, lin2 = synth.gen_linear(9400, NF, H), synth.gen_linear(9401, N2, H)
+    pk1 = w4.repack(to_dev(lin1["qweight"]), to_dev(lin1["scales"]), to_dev(lin1["zeros"]), NF, H)
+    pk2 = w4.repack(to_dev(lin2["qweight"]), to_dev(lin2["scales"]), to_dev(lin2["zeros"]), N2, H)
+    x0 = torch.empty((M, H), dtype=torch.int16, device=DEV)
+    f = torch.empty((M, NF), dtype=torch.int16, device=DEV)
+    y2 = torch.empty((M, N2), dtype=torch.float32, device=DEV)
+    descs = [dict(x=x0, qweight_t=pk1.qweight_t, scales_t=pk1.scales_t, zeros_t=pk1.zeros_t, y=None, y_bf16=f,
+                  N=NF, K=H, alpha=_alpha(H), deps=[]),
+             dict(x=f, qweight_t=pk2.qweight_t, scales_t=pk2.scales_t, zeros_t=pk2.zeros_t, y=y2, y_bf16=None,
+                  N=N2, K=H, ldx=NF, alpha=1.0, deps=[0])]
+    hd = w4.w4_pass_create(descs, M)
+    try:
+        for seed in (9500, 9600):
+            x0.copy_(to_dev(synth.gen_x(M, H, seed_base=seed)))
+            f.fill_(0x7FC0)
+            y2.fill_(float("nan"))
+            w4.w4_pass_run(hd)
+            w4.w4_pass_check(hd)
+            torch.cuda.synchronize()
+            xs = f.cpu().numpy().view(np.uint16)[:, :H].copy()  # the slice the consumer reads
+            assert np.all(np.isfinite(bf16_bits_to_f64(xs))), (M, seed)
+            Y, A = linear64_gemm(xs, lin2["qweight"], lin2["scales"], lin2["zeros"], 128, 0, N2)
+            y = y2.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(y - Y) <= 4e-3 * A), (M, seed)
     finally:
         torch.cuda.synchronize()
         w4.w4_pass_destroy(hd)

@@ -11,7 +11,7 @@ its edge; the Llama-3-70B grouping (64 query heads over 8 key/value heads)
 and other groupings; a token that sees nothing; one key split and the most
 splits (M = 1 over 4096 and 12288 keys); repeatability, also with calls of
 other shapes in between (the key splits' partial results share one
-workspace, merged by a second launch).
+workspace, merged by a second launch), and under HIP graph replays.
 """
 import numpy as np
 import pytest
@@ -108,3 +108,38 @@ def test_repeatable_across_shapes():
     b, args = _case(11, 1, 4096, 64, 8, [-1])
     assert np.array_equal(a, b)
     _check(b, args, "after other shapes")
+
+
+def test_graph_replays_merge_every_time():
+    # a captured call (the split kernel, then the merge launch) replays
+    # correctly, also with the query changed between replays
+    M, L, Hq, Hkv = 1, 4096, 64, 8
+    rng = np.random.default_rng(4242)
+    D = 128
+    kcb, kc = _bf16(rng, (L, Hkv, D))
+    vcb, vc = _bf16(rng, (L, Hkv, D))
+    kdb, kd = _bf16(rng, (M, Hkv, D))
+    vdb, vd = _bf16(rng, (M, Hkv, D))
+    masks = ancestor_masks([-1])
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).to(DEV)
+    qd = torch.empty((M, Hq, D), dtype=torch.int16, device=DEV)
+    out = torch.empty((M, Hq, D), dtype=torch.float32, device=DEV)
+    tens = [dev(kcb), dev(vcb), dev(kdb), dev(vdb), torch.from_numpy(masks.view(np.int64)).to(DEV)]
+    qb0, _ = _bf16(rng, (M, Hq, D))
+    qd.copy_(dev(qb0))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w4.tree_attention(qd, *tens, out=out, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w4.tree_attention(qd, *tens, out=out)
+    for rep in range(3):
+        qb, q = _bf16(rng, (M, Hq, D))
+        qd.copy_(dev(qb))
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        _check(out.cpu().numpy().astype(np.float64), (q, kc, vc, kd, vd, masks), ("graph replay", rep))
