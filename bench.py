@@ -369,6 +369,76 @@ def dependent_pass(torch, w4, packed, M, input_seed=2000):
     return handle, outs, h0, descs
 
 
+def fused_dependent_pass(torch, w4, fpk, M, input_seed=2000):
+    """The dependent pass over the fused projections: per layer qkv (N =
+    10240) reads the layer input; o reads the q part of qkv's output (its
+    first 8192 columns, ldx = 10240); gate_up (N = 57344) reads o's output;
+    down reads the gate part of gate_up's output (its first 28672 columns,
+    ldx = 57344); the lm_head reads the last down's output.  Returns (handle,
+    outputs by (layer, name), layer-0 input tensor, the descriptors)."""
+    import synth
+
+    dev = "cuda:0"
+    H = synth.LAYER_LINEARS[0][2]
+    h0 = torch.from_numpy(synth.gen_x(M, H, seed_base=input_seed).view(np.int16)).to(dev)
+    outs, descs, index = {}, [], {}
+    h, hdeps = h0, []
+
+    def add(L, name, x, deps, K, ldx=0):
+        pk = fpk[(L, name)]
+        y = torch.empty((M, pk.N), dtype=torch.int16, device=dev)
+        outs[(L, name)] = y
+        index[(L, name)] = len(descs)
+        descs.append(dict(x=x, qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t, y=None,
+                          y_bf16=y, N=pk.N, K=K, ldx=ldx, alpha=layer_alpha(K), deps=[index[d] for d in deps],
+                          key=(L, name)))
+        return y
+
+    F = synth.LAYER_LINEARS[4][1]
+    for L in range(synth.N_LAYERS):
+        qkv = add(L, "qkv", h, hdeps, H)
+        o = add(L, "o", qkv, [(L, "qkv")], H, ldx=qkv.shape[1])
+        gu = add(L, "gate_up", o, [(L, "o")], H)
+        h = add(L, "down", gu, [(L, "gate_up")], F, ldx=gu.shape[1])
+        hdeps = [(L, "down")]
+    add(None, "lm_head", h, hdeps, H)
+    handle = w4.w4_pass_create(descs, M)
+    return handle, outs, h0, descs
+
+
+def fused_dependent_parity(w4, host, descs, check_layers, n0):
+    """Every output column of the checked layers' fused linears (each part
+    against its own linear's oracle on the input the linear read) and the
+    lm_head slice; the same bound as dependent_pass_parity."""
+    import synth
+    from oracle import bf16_bits_to_f64, linear64_gemm
+
+    parts = {"qkv": ("q", "k", "v"), "o": ("o",), "gate_up": ("gate", "up"), "down": ("down",),
+             "lm_head": ("lm_head",)}
+    worst = 0.0
+    for d in descs:
+        L, name = d["key"]
+        if L not in check_layers and name != "lm_head":
+            continue
+        x = d["x"].cpu().numpy().view(np.uint16)[:, :d["K"]].copy()  # the columns the linear read
+        y = bf16_bits_to_f64(d["y_bf16"].cpu().numpy().view(np.uint16))
+        c0 = 0
+        for part in parts[name]:
+            lin = host[(None if part == "lm_head" else L, part)]
+            N = lin["scales"].shape[1]
+            cols = [(n0, n0 + 512)] if part == "lm_head" else [(a, min(N, a + 4096)) for a in range(0, N, 4096)]
+            for a, b in cols:
+                Y, A = linear64_gemm(x, lin["qweight"], lin["scales"], lin["zeros"], 128, a, b)
+                Y, A = Y * d["alpha"], A * d["alpha"]
+                bound = 4e-3 * A * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(Y)
+                r = float(np.max(np.abs(y[:, c0 + a:c0 + b] - Y) / bound))
+                if not r <= 1.0:
+                    raise AssertionError(f"fused parity failure: layer {L} {name}/{part} cols {a}:{b} ratio {r}")
+                worst = max(worst, r)
+            c0 += N
+    return worst
+
+
 def dependent_pass_parity(torch, w4, host, descs, check_layers, n0, M):
     """Every output column of the checked layers' linears, and columns
     [n0, n0 + 512) of the lm_head, against the oracle applied to the input
@@ -400,26 +470,42 @@ def dependent_pass_parity(torch, w4, host, descs, check_layers, n0, M):
 
 # ---------------------------------------------------------------------------
 
-def fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args):
+FUSED_GROUPS = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",))]
+
+
+def fuse_projections(w4, packed):
+    """The sweep's packed weights with the projections that share an input
+    concatenated on the device (the tile layout is chunk-major): per layer qkv
+    (N = 10240), o, gate_up (N = 57344), down; and the lm_head."""
+    import synth
+
+    fpk = {}
+    for L in range(synth.N_LAYERS):
+        for fname, names in FUSED_GROUPS:
+            fpk[(L, fname)] = (packed[(L, names[0])] if len(names) == 1
+                               else w4.concat_packed([packed[(L, n)] for n in names]))
+    fpk[(None, "lm_head")] = packed[(None, "lm_head")]
+    return fpk
+
+
+def fused_sweep(torch, w4, fpk, xs, host, check_layers, args):
     """The same pass with the projections that share an input fused: per
     layer qkv (N = 10240) | o | gate+up (N = 57344) | down, plus the lm_head
     (321 launches instead of 561), with fp32 output and with the bf16
-    epilogue.  Weights are the sweep's, concatenated on the device (the tile
-    layout is chunk-major).  Graph-replayed like the sweep; parity of the
-    fused linears on the checked layers' sampled columns (fp32 output against
-    the contract, bf16 output against the rounded fp32 output)."""
+    epilogue, as independent launches (no data flow between them).
+    Graph-replayed like the sweep; parity of the fused linears on the checked
+    layers' sampled columns (fp32 output against the contract, bf16 output
+    against the rounded fp32 output)."""
     import synth
     from oracle import check_contract, linear64_columns
 
     dev = "cuda:0"
-    groups = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",))]
-    fpk, fspec = {}, []
+    groups = FUSED_GROUPS
+    fspec = []
     for L in range(synth.N_LAYERS):
         for fname, names in groups:
-            pk = packed[(L, names[0])] if len(names) == 1 else w4.concat_packed([packed[(L, n)] for n in names])
-            fpk[(L, fname)] = pk
+            pk = fpk[(L, fname)]
             fspec.append((L, fname, pk.N, pk.K))
-    fpk[(None, "lm_head")] = packed[(None, "lm_head")]
     fspec.append((None, "lm_head", synth.LM_HEAD[1], synth.LM_HEAD[2]))
     yf = {N: torch.empty((64, N), dtype=torch.float32, device=dev) for N in {s[2] for s in fspec}}
     yb = {N: torch.empty((64, N), dtype=torch.int16, device=dev) for N in {s[2] for s in fspec}}
@@ -461,6 +547,7 @@ def fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args):
         out["us_per_pass_bf16_out"][str(M)] = round(us_b, 1)
         out["tbps_per_pass"][str(M)] = round(B / (us * 1e-6) / 1e12, 4)
         out["roofline_frac_per_pass"][str(M)] = round(t_roof / us, 4)
+
     if args.no_parity:
         out["worst_err_over_bound"] = None
     else:
@@ -490,7 +577,7 @@ def fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args):
                         worst = max(worst, w)
                         c0 += N
         out["worst_err_over_bound"] = worst
-    del fpk, yf, yb
+    del yf, yb
     torch.cuda.empty_cache()
     return out
 
@@ -883,12 +970,15 @@ def main():
     if args.copy_calib:
         copy_calibration(torch, w4, args.copy_calib)
     specs = model_specs()
-    nlin = len(specs)
 
-    # the dependent passes (the measured workload)
-    passes = {M: dependent_pass(torch, w4, packed, M) for M in PASS_M}
-    pass_bytes = {M: sum(alg_bytes(M, s["N"], s["K"], 2) for s in specs) for M in PASS_M}
-    pass_flops = {M: sum(alg_flops(M, s["N"], s["K"]) for s in specs) for M in PASS_M}
+    # the dependent passes (the measured workload): the layer's projections
+    # that share an input fused (q|k|v, gate|up), each linear reading its
+    # producer's output
+    fpk = fuse_projections(w4, packed)
+    passes = {M: fused_dependent_pass(torch, w4, fpk, M) for M in PASS_M}
+    pass_bytes = {M: sum(alg_bytes(M, d["N"], d["K"], 2) for d in passes[M][3]) for M in PASS_M}
+    pass_flops = {M: sum(alg_flops(M, d["N"], d["K"]) for d in passes[M][3]) for M in PASS_M}
+    nlaunch = len(passes[PASS_M[0]][3])
     info = {M: w4.w4_pass_info(passes[M][0]) for M in PASS_M}
     for M in PASS_M:  # eager run once per M (also the graph's warm-up)
         w4.w4_pass_run(passes[M][0])
@@ -941,6 +1031,38 @@ def main():
         torch.cuda.synchronize()
         us_eager[M] = s0.elapsed_time(s1) * 1e3
 
+    # the same dependent pass over the seven unfused linears of each layer
+    # (561 linears), for comparison
+    unfused = {}
+    for M in PASS_M:
+        handle, uouts, uh0, udescs = dependent_pass(torch, w4, packed, M)
+        w4.w4_pass_run(handle)
+        w4.w4_pass_check(handle)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            w4.w4_pass_run(handle)
+        g.replay()
+        torch.cuda.synchronize()
+        ub = sum(alg_bytes(M, d["N"], d["K"], 2) for d in udescs)
+        uf = sum(alg_flops(M, d["N"], d["K"]) for d in udescs)
+        uus = replay_us(g, max(3, args.steps))
+        w4.w4_pass_check(handle)
+        ent = {"us": round(uus, 1), "roofline_frac": round(max(ub / (HBM_PEAK_GBS * 1e9),
+                                                               uf / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6 / uus, 4),
+               "launches": 1 if w4.w4_pass_info(handle)["persistent"] else len(udescs)}
+        if not args.no_parity:
+            uh0.copy_(torch.from_numpy(synth.gen_x(M, uh0.shape[1], seed_base=2700).view(np.int16)))
+            for t in uouts.values():
+                t.fill_(0x7FC0)
+            g.replay()
+            w4.w4_pass_check(handle)
+            ent["worst_err_over_bound"] = dependent_pass_parity(torch, w4, host, udescs, check_layers, n0, M)
+        torch.cuda.synchronize()
+        del g
+        w4.w4_pass_destroy(handle)
+        del uouts, udescs, uh0
+        unfused[M] = ent
+
     # the same linears as 561 independent launches (no dependencies, one input
     # per K, fp32 outputs): the structure of a launch per linear, for comparison
     xs = {K: torch.from_numpy(synth.gen_x(64, K).view(np.int16)).to(dev) for K in (8192, 28672)}
@@ -969,18 +1091,18 @@ def main():
     sep_bytes = {M: sum(alg_bytes(M, sp["N"], sp["K"]) for sp in specs) for M in PASS_M}
 
     # per-kernel roofline.  M = 1 and 5: the whole pass is one launch of the
-    # persistent pass kernel (GEMV and MFMA form); M = 64: 561 launches of the
-    # LDS-ring MFMA kernel (k, v: four row slices of one row block), each with
-    # its split-K reduction when K is split -- there the unit is the linear.
-    # Durations come from the graph replays (events on the replay stream).
+    # persistent pass kernel (GEMV and MFMA form); M = 64: 321 launches of the
+    # LDS-ring MFMA kernel, each with its split-K reduction when K is split --
+    # there the unit is the (fused) linear.  Durations come from the graph
+    # replays (events on the replay stream).
     kernels = {}
     for M in PASS_M:
         if info[M]["persistent"]:
             name = "w4_pass_kernel<GEMV>" if M == 1 else "w4_pass_kernel<MFMA 16 rows>"
             launches = 1
         else:
-            name = "w4a16_mfma_lds_kernel<4 (k, v: 1), 4 or 8>"
-            launches = nlin
+            name = "w4a16_mfma_lds_kernel<4, 4 or 8>"
+            launches = nlaunch
         mean_us = us_per_pass[M] / launches
         bpl = pass_bytes[M] / launches
         achieved = bpl / (mean_us * 1e-6) / 1e9
@@ -996,13 +1118,13 @@ def main():
     roofline = {"bound": "hbm", "achieved": dk["achieved_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dk["achieved_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
                 "per_launch": ("alg_bytes_per_launch = 0.51953125 N K + 2 M K + 2 M N (bf16 output) summed over "
-                               "the launch's linears: the 561 linears of the pass for the persistent pass kernel, "
-                               "one linear (averaged over the pass) for per-linear launches; achieved = that / "
-                               "the launch's mean duration from the graph replays")}
+                               "the launch's linears: the 321 (fused) linears of the pass for the persistent pass "
+                               "kernel, one linear (averaged over the pass) for per-linear launches; achieved = "
+                               "that / the launch's mean duration from the graph replays")}
 
     fused = acceptance = tree = None
     if not args.no_extras:
-        fused = fused_sweep(torch, w4, packed, xs, specs, host, check_layers, args)
+        fused = fused_sweep(torch, w4, fpk, xs, host, check_layers, args)
         acceptance = acceptance_bench(torch, w4, args)
         tree = tree_attention_bench(torch, w4, args)
 
@@ -1017,7 +1139,7 @@ def main():
                 t.fill_(0x7FC0)  # bf16 NaN: an output left unwritten, or read early, shows up
             graphs[M].replay()  # the captured pass, on a changed input
             w4.w4_pass_check(handle)
-            worst[str(M)] = dependent_pass_parity(torch, w4, host, pdescs, check_layers, n0, M)
+            worst[str(M)] = fused_dependent_parity(w4, host, pdescs, check_layers, n0)
         parity = {"layers": check_layers, "lm_head_cols": [n0, n0 + 512], "columns": "all (lm_head: the slice)",
                   "worst_err_over_bound": worst}
     cpu = None if args.no_cpu_baseline else cpu_baseline(host)
@@ -1037,13 +1159,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian weights quantised to uint4 g=128, Gaussian bf16 activations)",
-        "config": {"workload": "llama3-70b-w4a16-verify-sweep", "layers": 80, "linears_per_pass": len(specs),
+        "config": {"workload": "llama3-70b-w4a16-verify-sweep", "layers": 80, "weight_matrices": len(specs),
+                   "linears_per_pass": nlaunch,
+                   "projections": "q|k|v and gate|up fused (the layer's weights concatenated: N = 10240, 57344)",
                    "passes_per_step": list(PASS_M), "group": 128, "weight_bytes": int(sum(
                        s["N"] * s["K"] * 0.51953125 for s in specs)), "graph": True,
-                   "dependencies": "each linear reads its producer's bf16 output", "output": "bf16",
-                   "launches_per_pass": {str(M): (1 if info[M]["persistent"] else nlin) for M in PASS_M}},
+                   "dependencies": "each linear reads its producer's bf16 output (o: the q columns of qkv's, "
+                                   "down: the gate columns of gate_up's)", "output": "bf16",
+                   "launches_per_pass": {str(M): (1 if info[M]["persistent"] else nlaunch) for M in PASS_M}},
         "us_per_pass": {str(M): round(us_per_pass[M], 1) for M in PASS_M},
         "us_per_pass_eager": {str(M): round(us_eager[M], 1) for M in PASS_M},
+        "unfused_dependent": {"linears_per_pass": len(specs),
+                              "us_per_pass": {str(M): unfused[M]["us"] for M in PASS_M},
+                              "roofline_frac_per_pass": {str(M): unfused[M]["roofline_frac"] for M in PASS_M},
+                              "launches_per_pass": {str(M): unfused[M]["launches"] for M in PASS_M},
+                              "worst_err_over_bound": {str(M): unfused[M].get("worst_err_over_bound")
+                                                       for M in PASS_M}},
         "separate_launches": {"us_per_pass": {str(M): round(us_separate[M], 1) for M in PASS_M},
                               "roofline_frac_per_pass": {str(M): round(max(
                                   sep_bytes[M] / (HBM_PEAK_GBS * 1e9),
