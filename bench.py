@@ -10,27 +10,31 @@ W ~ N(0, 0.02) quantised round-to-nearest; layer L's linear idx uses seed
 resident in HBM.  One *step* is three verify passes, at M = 1 (plain decode),
 M = 5 (a sequence draft) and M = 64 (a flattened tree draft).
 
-A pass keeps the model's data dependencies: layer L's q, k and v read the
-layer input (layer L-1's down output; layer 0: a seeded input), o reads q's
-output (standing in for the attention output, which has q's shape) and waits
-for q, k and v, gate and up read o's output, down reads gate's output and
-waits for gate and up, and the lm_head reads the last down output.  Every
-linear writes its result as bf16 (the next layer's activation type), scaled
-by a power of two (1/2 for K = 8192, 1/4 for K = 28672) that keeps the
-activations near unit scale over 80 layers.  A pass is one pass object
-(include/w4_pass.h): at M = 1 and 5 one persistent launch, at M = 64 the 561
-linears as their own launches; each captured once in a HIP graph and
+A pass keeps the model's data dependencies, with the projections that share
+an input fused (the layer's weights concatenated): layer L's qkv (q|k|v,
+N = 10240) reads the layer input (layer L-1's down output; layer 0: a seeded
+input), o reads the q columns of qkv's output (standing in for the attention
+output, which has q's shape), gate_up (gate|up, N = 57344) reads o's output,
+down reads the gate columns of gate_up's output, and the lm_head reads the
+last down output: 321 linears.  Every linear writes its result as bf16 (the
+next layer's activation type), scaled by a power of two (1/2 for K = 8192,
+1/4 for K = 28672) that keeps the activations near unit scale over 80
+layers.  A pass is one pass object (include/w4_pass.h) in the form the
+library chooses -- for this pass, one linear per dependency class,
+per-linear launches at every M -- captured once in a HIP graph and
 replayed.  Algorithmic bytes per linear: 0.51953125 N K (codes, scales,
 zeros) + 2 M K (x) + 2 M N (the bf16 output).
 
 Printed JSON line: `value` is the step's effective HBM throughput (algorithmic
 bytes of the three passes / step time, TB/s); per-M microseconds per pass,
-t(M)/t(1), roofline fractions, the same passes as 561 independent launches
-(no dependencies, fp32 outputs) for comparison, the measured HBM read
-ceiling, the oracle's host throughput on a bounded sample and the oracle
-checks (every output column of three seeded-random layers and a 512-column
-slice of the lm_head, against the oracle on the inputs each linear read)
-ride along.
+t(M)/t(1), roofline fractions; for comparison the same pass in the
+persistent-kernel form (M = 1, 5), the unfused pass (561 linears, in the
+library's choice of form: the persistent kernel at M = 1 and 5) and the 561
+linears as independent launches (no dependencies, fp32 outputs); the
+measured HBM read ceiling, the oracle's host throughput on a bounded sample
+and the oracle checks (every output column of three seeded-random layers and
+a 512-column slice of the lm_head, against the oracle on the inputs each
+linear read) ride along.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3]
 """
@@ -80,6 +84,9 @@ def parse():
     p.add_argument("--no-parity", action="store_true", help="skip the oracle spot checks")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the fused-projection and acceptance measurements (profiling runs of the sweep)")
+    p.add_argument("--headline-only", action="store_true",
+                   help="only the measured passes (profiling runs): no comparison passes, extras, parity or CPU "
+                        "baseline")
     p.add_argument("--shapes", action="store_true",
                    help="per-linear report instead of the sweep: each decoder shape and the lm_head at every M of "
                         "--m, graph-replayed over rotating weight copies (>= --rotate-gib) so HBM, not the 256 MB "
@@ -369,7 +376,7 @@ def dependent_pass(torch, w4, packed, M, input_seed=2000):
     return handle, outs, h0, descs
 
 
-def fused_dependent_pass(torch, w4, fpk, M, input_seed=2000):
+def fused_dependent_pass(torch, w4, fpk, M, input_seed=2000, mode=None):
     """The dependent pass over the fused projections: per layer qkv (N =
     10240) reads the layer input; o reads the q part of qkv's output (its
     first 8192 columns, ldx = 10240); gate_up (N = 57344) reads o's output;
@@ -402,7 +409,7 @@ def fused_dependent_pass(torch, w4, fpk, M, input_seed=2000):
         h = add(L, "down", gu, [(L, "gate_up")], F, ldx=gu.shape[1])
         hdeps = [(L, "down")]
     add(None, "lm_head", h, hdeps, H)
-    handle = w4.w4_pass_create(descs, M)
+    handle = w4.w4_pass_create(descs, M) if mode is None else w4.w4_pass_create_mode(descs, M, mode)
     return handle, outs, h0, descs
 
 
@@ -744,13 +751,14 @@ def copy_calibration(torch, w4, mib):
 
 def traffic_from_pmc(fetch_dir, write_dir, copy_mib, out_path):
     """HBM bytes per launch of each sweep pass from two rocprofv3 --pmc runs
-    of the sweep (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
-    by what the counter reads for w4_bench_copy of copy_mib MiB.  M = 1 and 5:
-    a launch is one dispatch of the persistent pass kernel (GEMV form: M = 1,
-    MFMA form: M = 5), the whole pass.  M = 64: a launch is one linear, the
-    LDS-ring MFMA kernel plus the split-K reduction dispatched right after it
-    when K is split.  Writes profiles/traffic.json (tagged with the
-    kernel-source digest) and returns it."""
+    of the sweep (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch; taken with
+    --headline-only so that only the measured passes run), each scaled by
+    what the counter reads for w4_bench_copy of copy_mib MiB.  A launch is
+    one dispatch of the persistent pass kernel (the whole pass; GEMV form at
+    M = 1, MFMA form at M = 5) or one linear (its kernel plus the split-K
+    reduction dispatched right after it when K is split).  Writes
+    profiles/traffic.json (tagged with the kernel-source digest) and returns
+    it."""
     import csv
     import glob
 
@@ -766,16 +774,16 @@ def traffic_from_pmc(fetch_dir, write_dir, copy_mib, out_path):
         return vals, names
 
     def pass_of(name):
-        if "w4_pass_kernel<0" in name:
-            return "1"
-        if "w4_pass_kernel<1" in name:
-            return "5"
-        if "w4a16_mfma_lds_kernel" in name:
-            return "64"
-        return None
+        # (M, what a launch is): the persistent pass kernel is a whole pass,
+        # the per-linear kernels one linear each
+        for key, m, kind in (("w4_pass_kernel<0", "1", "pass"), ("w4_pass_kernel<1", "5", "pass"),
+                             ("w4a16_gemv_kernel", "1", "linear"), ("w4a16_mfma_direct_kernel", "5", "linear"),
+                             ("w4a16_mfma_lds_kernel", "64", "linear")):
+            if key in name:
+                return m, kind
+        return None, None
 
-    out = {"source_digest": source_digest(), "copy_calibration_mib": copy_mib,
-           "launch": {"1": "pass", "5": "pass", "64": "linear"}, "passes": {}}
+    out = {"source_digest": source_digest(), "copy_calibration_mib": copy_mib, "launch": {}, "passes": {}}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals, names = per_dispatch(d, counter)
         copies = [vals[i] for i in vals if "bench_copy" in names[i]]
@@ -785,11 +793,12 @@ def traffic_from_pmc(fetch_dir, write_dir, copy_mib, out_path):
         for i in sorted(vals):
             n = names[i]
             if "splitk_reduce" in n:
-                if cur == "64":
+                if cur is not None:  # the reduction of the linear launched just before
                     sums[cur] += vals[i] * factor * 1024
                 continue
-            cur = pass_of(n)
+            cur, kind = pass_of(n)
             if cur is not None:
+                out["launch"][cur] = kind
                 sums[cur] = sums.get(cur, 0.0) + vals[i] * factor * 1024
                 counts[cur] = counts.get(cur, 0) + 1
         for m in sums:
@@ -1031,77 +1040,108 @@ def main():
         torch.cuda.synchronize()
         us_eager[M] = s0.elapsed_time(s1) * 1e3
 
-    # the same dependent pass over the seven unfused linears of each layer
-    # (561 linears), for comparison
-    unfused = {}
-    for M in PASS_M:
-        handle, uouts, uh0, udescs = dependent_pass(torch, w4, packed, M)
-        w4.w4_pass_run(handle)
+    # the persistent pass kernel on the same fused pass where the library
+    # chose per-linear launches (M <= 16), for comparison
+    def pass_entry(handle, descs, outs, h0, g, seed):
+        Mh = h0.shape[0]
+        eb = sum(alg_bytes(Mh, d["N"], d["K"], 2) for d in descs)
+        ef = sum(alg_flops(Mh, d["N"], d["K"]) for d in descs)
+        eus = replay_us(g, max(3, args.steps))
         w4.w4_pass_check(handle)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            w4.w4_pass_run(handle)
-        g.replay()
-        torch.cuda.synchronize()
-        ub = sum(alg_bytes(M, d["N"], d["K"], 2) for d in udescs)
-        uf = sum(alg_flops(M, d["N"], d["K"]) for d in udescs)
-        uus = replay_us(g, max(3, args.steps))
-        w4.w4_pass_check(handle)
-        ent = {"us": round(uus, 1), "roofline_frac": round(max(ub / (HBM_PEAK_GBS * 1e9),
-                                                               uf / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6 / uus, 4),
-               "launches": 1 if w4.w4_pass_info(handle)["persistent"] else len(udescs)}
+        ent = {"us": round(eus, 1), "roofline_frac": round(max(eb / (HBM_PEAK_GBS * 1e9),
+                                                               ef / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6 / eus, 4),
+               "launches": 1 if w4.w4_pass_info(handle)["persistent"] else len(descs)}
         if not args.no_parity:
-            uh0.copy_(torch.from_numpy(synth.gen_x(M, uh0.shape[1], seed_base=2700).view(np.int16)))
-            for t in uouts.values():
+            h0.copy_(torch.from_numpy(synth.gen_x(h0.shape[0], h0.shape[1], seed_base=seed).view(np.int16)))
+            for t in outs.values():
                 t.fill_(0x7FC0)
             g.replay()
             w4.w4_pass_check(handle)
-            ent["worst_err_over_bound"] = dependent_pass_parity(torch, w4, host, udescs, check_layers, n0, M)
-        torch.cuda.synchronize()
-        del g
-        w4.w4_pass_destroy(handle)
-        del uouts, udescs, uh0
-        unfused[M] = ent
+        return ent
 
-    # the same linears as 561 independent launches (no dependencies, one input
-    # per K, fp32 outputs): the structure of a launch per linear, for comparison
-    xs = {K: torch.from_numpy(synth.gen_x(64, K).view(np.int16)).to(dev) for K in (8192, 28672)}
-    ys = {N: torch.empty((64, N), dtype=torch.float32, device=dev) for N in (1024, 8192, 28672, 128256)}
+    persistent_form, unfused, us_separate, sep_bytes = {}, {}, {}, {}
+    if not args.headline_only:
+        for M in PASS_M:
+            if M > 16 or info[M]["persistent"]:
+                continue
+            handle, pouts, ph0, pdescs = fused_dependent_pass(torch, w4, fpk, M, mode=w4.W4_PASS_PERSISTENT)
+            w4.w4_pass_run(handle)
+            w4.w4_pass_check(handle)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                w4.w4_pass_run(handle)
+            g.replay()
+            torch.cuda.synchronize()
+            ent = pass_entry(handle, pdescs, pouts, ph0, g, 2600)
+            if not args.no_parity:
+                ent["worst_err_over_bound"] = fused_dependent_parity(w4, host, pdescs, check_layers, n0)
+            torch.cuda.synchronize()
+            del g
+            w4.w4_pass_destroy(handle)
+            del pouts, pdescs, ph0
+            persistent_form[M] = ent
 
-    def descs_for(M):
-        out = []
-        for sp in specs:
-            pk = packed[(sp["layer"], sp["name"])]
-            out.append(dict(x=xs[sp["K"]][:M], qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t,
-                            y=ys[sp["N"]][:M], N=sp["N"], K=sp["K"]))
-        return out
+        # the same dependent pass over the seven unfused linears of each layer
+        # (561 linears), for comparison
+        for M in PASS_M:
+            handle, uouts, uh0, udescs = dependent_pass(torch, w4, packed, M)
+            w4.w4_pass_run(handle)
+            w4.w4_pass_check(handle)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                w4.w4_pass_run(handle)
+            g.replay()
+            torch.cuda.synchronize()
+            ent = pass_entry(handle, udescs, uouts, uh0, g, 2700)
+            if not args.no_parity:
+                ent["worst_err_over_bound"] = dependent_pass_parity(torch, w4, host, udescs, check_layers, n0, M)
+            torch.cuda.synchronize()
+            del g
+            w4.w4_pass_destroy(handle)
+            del uouts, udescs, uh0
+            unfused[M] = ent
 
-    sep_descs = {M: descs_for(M) for M in PASS_M}
-    us_separate = {}
-    for M in PASS_M:
-        w4.w4a16_verify_pass(sep_descs[M], M)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
+        # the same linears as 561 independent launches (no dependencies, one input
+        # per K, fp32 outputs): the structure of a launch per linear, for comparison
+        xs = {K: torch.from_numpy(synth.gen_x(64, K).view(np.int16)).to(dev) for K in (8192, 28672)}
+        ys = {N: torch.empty((64, N), dtype=torch.float32, device=dev) for N in (1024, 8192, 28672, 128256)}
+
+        def descs_for(M):
+            out = []
+            for sp in specs:
+                pk = packed[(sp["layer"], sp["name"])]
+                out.append(dict(x=xs[sp["K"]][:M], qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t,
+                                y=ys[sp["N"]][:M], N=sp["N"], K=sp["K"]))
+            return out
+
+        sep_descs = {M: descs_for(M) for M in PASS_M}
+        for M in PASS_M:
             w4.w4a16_verify_pass(sep_descs[M], M)
-        g.replay()
-        torch.cuda.synchronize()
-        us_separate[M] = replay_us(g, max(3, args.steps))
-        del g
-    sep_bytes = {M: sum(alg_bytes(M, sp["N"], sp["K"]) for sp in specs) for M in PASS_M}
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                w4.w4a16_verify_pass(sep_descs[M], M)
+            g.replay()
+            torch.cuda.synchronize()
+            us_separate[M] = replay_us(g, max(3, args.steps))
+            del g
+        sep_bytes = {M: sum(alg_bytes(M, sp["N"], sp["K"]) for sp in specs) for M in PASS_M}
 
-    # per-kernel roofline.  M = 1 and 5: the whole pass is one launch of the
-    # persistent pass kernel (GEMV and MFMA form); M = 64: 321 launches of the
-    # LDS-ring MFMA kernel, each with its split-K reduction when K is split --
-    # there the unit is the (fused) linear.  Durations come from the graph
-    # replays (events on the replay stream).
+    # per-kernel roofline.  A pass in the persistent form is one launch of the
+    # pass kernel (GEMV form at M = 1, MFMA form above); in the launch form
+    # it is one launch per (fused) linear -- the GEMV at M = 1, the streaming
+    # MFMA kernel at M = 2..14, the LDS-ring MFMA kernel above -- each with
+    # its split-K reduction when K is split, and the unit is the linear
+    # (averaged over the pass).  Durations come from the graph replays
+    # (events on the replay stream).
     kernels = {}
     for M in PASS_M:
         if info[M]["persistent"]:
             name = "w4_pass_kernel<GEMV>" if M == 1 else "w4_pass_kernel<MFMA 16 rows>"
             launches = 1
         else:
-            name = "w4a16_mfma_lds_kernel<4, 4 or 8>"
+            name = ("w4a16_gemv_kernel" if M == 1 else "w4a16_mfma_direct_kernel" if M <= 14
+                    else "w4a16_mfma_lds_kernel<4, 4 or 8>")
             launches = nlaunch
         mean_us = us_per_pass[M] / launches
         bpl = pass_bytes[M] / launches
@@ -1119,18 +1159,19 @@ def main():
                 "frac": round(dk["achieved_GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
                 "per_launch": ("alg_bytes_per_launch = 0.51953125 N K + 2 M K + 2 M N (bf16 output) summed over "
                                "the launch's linears: the 321 (fused) linears of the pass for the persistent pass "
-                               "kernel, one linear (averaged over the pass) for per-linear launches; achieved = "
-                               "that / the launch's mean duration from the graph replays")}
+                               "kernel, one linear (averaged over the pass, with its split-K reduction) for "
+                               "per-linear launches; achieved = that / the launch's mean duration from the graph "
+                               "replays")}
 
     fused = acceptance = tree = None
-    if not args.no_extras:
+    if not args.no_extras and not args.headline_only:
         fused = fused_sweep(torch, w4, fpk, xs, host, check_layers, args)
         acceptance = acceptance_bench(torch, w4, args)
         tree = tree_attention_bench(torch, w4, args)
 
     ceiling = hbm_read_ceiling(torch, w4)
     parity = None
-    if not args.no_parity:
+    if not args.no_parity and not args.headline_only:
         worst = {}
         for M in PASS_M:
             handle, outs, h0, pdescs = passes[M]
@@ -1142,7 +1183,7 @@ def main():
             worst[str(M)] = fused_dependent_parity(w4, host, pdescs, check_layers, n0)
         parity = {"layers": check_layers, "lm_head_cols": [n0, n0 + 512], "columns": "all (lm_head: the slice)",
                   "worst_err_over_bound": worst}
-    cpu = None if args.no_cpu_baseline else cpu_baseline(host)
+    cpu = None if args.no_cpu_baseline or args.headline_only else cpu_baseline(host)
 
     t_roof = {M: max(pass_bytes[M] / (HBM_PEAK_GBS * 1e9), pass_flops[M] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
               for M in PASS_M}
@@ -1169,17 +1210,22 @@ def main():
                    "launches_per_pass": {str(M): (1 if info[M]["persistent"] else nlaunch) for M in PASS_M}},
         "us_per_pass": {str(M): round(us_per_pass[M], 1) for M in PASS_M},
         "us_per_pass_eager": {str(M): round(us_eager[M], 1) for M in PASS_M},
+        "persistent_form": {"linears_per_pass": nlaunch,
+                            "us_per_pass": {str(M): e["us"] for M, e in persistent_form.items()},
+                            "roofline_frac_per_pass": {str(M): e["roofline_frac"] for M, e in persistent_form.items()},
+                            "worst_err_over_bound": {str(M): e.get("worst_err_over_bound")
+                                                     for M, e in persistent_form.items()}} if persistent_form else None,
         "unfused_dependent": {"linears_per_pass": len(specs),
                               "us_per_pass": {str(M): unfused[M]["us"] for M in PASS_M},
                               "roofline_frac_per_pass": {str(M): unfused[M]["roofline_frac"] for M in PASS_M},
                               "launches_per_pass": {str(M): unfused[M]["launches"] for M in PASS_M},
                               "worst_err_over_bound": {str(M): unfused[M].get("worst_err_over_bound")
-                                                       for M in PASS_M}},
+                                                       for M in PASS_M}} if unfused else None,
         "separate_launches": {"us_per_pass": {str(M): round(us_separate[M], 1) for M in PASS_M},
                               "roofline_frac_per_pass": {str(M): round(max(
                                   sep_bytes[M] / (HBM_PEAK_GBS * 1e9),
                                   pass_flops[M] / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6 / us_separate[M], 4)
-                                  for M in PASS_M}},
+                                  for M in PASS_M}} if us_separate else None,
         "tbps_per_pass": {str(M): round(pass_bytes[M] / (us_per_pass[M] * 1e-6) / 1e12, 4) for M in PASS_M},
         "roofline_frac_per_pass": {str(M): round(t_roof[M] / us_per_pass[M], 4) for M in PASS_M},
         "t_over_t1": {str(M): round(us_per_pass[M] / us_per_pass[1], 4) for M in PASS_M},

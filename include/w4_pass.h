@@ -16,10 +16,13 @@
  * producers, listed in `deps`): its multiply-adds start only once every
  * producer's output is stored, while its weights are already being read.
  *
- * At M <= 16 the pass runs as one persistent kernel (one workgroup per CU)
- * that streams the weights of successive linears without a gap between
- * them.  At M = 17..64 it runs each linear as its own launch, in order, on
- * the stream (the same kernels and results as w4a16_linear_out).
+ * A pass runs in one of two forms.  At M <= 16 it can run as one persistent
+ * kernel (one workgroup per CU) that streams the weights of successive
+ * linears without a gap between them and runs the linears that share their
+ * producers side by side.  At any M it can run each linear as its own
+ * launch, in order, on the stream (the same kernels and results as
+ * w4a16_linear_out).  w4_pass_create_mode chooses the form (w4_pass_create
+ * leaves the choice to the library); w4_pass_info reports it.
  *
  * Conventions are those of include/w4a16.h: device pointers owned by the
  * caller, `stream` a hipStream_t as void*, validation before any HIP call,
@@ -82,6 +85,20 @@ typedef struct w4_pass w4_pass;
  * shapes, M > 64, more than W4_PASS_MAX_DEPS producers) or W4_ERR_HIP. */
 int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pass** out);
 
+/* The form of a pass (w4_pass_create_mode). */
+#define W4_PASS_AUTO 0       /* the library's choice: the persistent kernel at M <= 16 when the linears that share
+                                their producers (dependency classes; the linears without producers are one class)
+                                number at least 1.25 per class on average, else per-linear launches */
+#define W4_PASS_PERSISTENT 1 /* the persistent kernel (M <= 16; W4_ERR_UNSUPPORTED above) */
+#define W4_PASS_LAUNCHES 2   /* one launch per linear, in order */
+
+/* w4_pass_create with the form chosen by the caller: `mode` is one of the
+ * W4_PASS_* values above (else W4_ERR_INVALID).  Both forms compute the same
+ * outputs within the accumulation contract (they may differ in the last
+ * bits: the persistent kernel sums a chunk's K range in its own order).
+ * Otherwise as w4_pass_create. */
+int w4_pass_create_mode(const w4_pass_linear* linears, int n, int M, int group, int mode, w4_pass** out);
+
 /* Launch the whole pass on `stream` (asynchronous).  Allocates nothing and
  * writes no memset: the launch can be captured in a HIP graph and replayed
  * (replays of one pass object on one device must not overlap in time: they
@@ -97,8 +114,9 @@ int w4_pass_run(w4_pass* pass, void* stream);
 int w4_pass_check(w4_pass* pass, void* stream);
 
 /* How a pass runs (host outputs, any may be NULL): 1 if it is one persistent
- * launch (M <= 16), else 0; that launch's workgroups; its units (64-column
- * chunks of all its linears). */
+ * launch, else 0 (per-linear launches); that launch's workgroups (0 for
+ * launches); its units (the 64-column chunks of all its linears, a chunk
+ * that the persistent kernel splits into K slices counting once per slice). */
 int w4_pass_info(const w4_pass* pass, int* persistent, int* grid, int* units);
 
 /* Test hook: the number of polls (about 50 ns apart) a dependency wait makes

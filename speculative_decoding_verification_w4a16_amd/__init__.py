@@ -22,6 +22,7 @@ LIB_PATH = os.environ.get("W4A16_LIB") or os.path.join(HERE, "libw4a16.so")
 
 W4_OK, W4_ERR_INVALID, W4_ERR_UNSUPPORTED, W4_ERR_HIP, W4_ERR_TIMEOUT = 0, 1, 2, 3, 4
 W4_PASS_MAX_DEPS = 4
+W4_PASS_AUTO, W4_PASS_PERSISTENT, W4_PASS_LAUNCHES = 0, 1, 2
 W4_KERNEL_AUTO, W4_KERNEL_GEMV, W4_KERNEL_MFMA = 0, 1, 2
 W4_OUT_F32, W4_OUT_BF16 = 0, 1
 GROUP = 128
@@ -78,6 +79,8 @@ _c = {
     "w4a16_verify_pass": _sig("w4a16_verify_pass", [ctypes.POINTER(W4LinearDesc), _i, _i, _i, _vp]),
     "w4_unpack": _sig("w4_unpack", [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     "w4_pass_create": _sig("w4_pass_create", [ctypes.POINTER(W4PassLinear), _i, _i, _i, ctypes.POINTER(_vp)]),
+    "w4_pass_create_mode": _sig("w4_pass_create_mode",
+                                [ctypes.POINTER(W4PassLinear), _i, _i, _i, _i, ctypes.POINTER(_vp)]),
     "w4_pass_run": _sig("w4_pass_run", [_vp, _vp]),
     "w4_pass_check": _sig("w4_pass_check", [_vp, _vp]),
     "w4_pass_info": _sig("w4_pass_info", [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
@@ -211,11 +214,7 @@ def w4a16_verify_pass(linears, M, group=GROUP, stream=None):
     _check(_c["w4a16_verify_pass"](arr, len(linears), M, group, st), "w4a16_verify_pass")
 
 
-def w4_pass_create(linears, M, group=GROUP):
-    """`linears`: sequence of dicts with x, qweight_t, scales_t, zeros_t, y
-    (or None), y_bf16 (or None), N, K, and optionally alpha (1.0), deps
-    (indices of earlier entries) and ldx (elements between rows of x; 0, the
-    default, means K).  Returns the pass handle (an int)."""
+def _pass_array(linears):
     n = len(linears)
     arr = (W4PassLinear * max(1, n))()
     for i, d in enumerate(linears):
@@ -223,8 +222,27 @@ def w4_pass_create(linears, M, group=GROUP):
         arr[i] = W4PassLinear(_ptr(d["x"]), _ptr(d["qweight_t"]), _ptr(d["scales_t"]), _ptr(d["zeros_t"]),
                               _ptr(d.get("y")), _ptr(d.get("y_bf16")), float(d.get("alpha", 1.0)), d["N"], d["K"],
                               len(deps), (_i * 4)(*(deps + [0] * (4 - len(deps)))[:4]), int(d.get("ldx", 0)))
+    return arr, n
+
+
+def w4_pass_create(linears, M, group=GROUP):
+    """`linears`: sequence of dicts with x, qweight_t, scales_t, zeros_t, y
+    (or None), y_bf16 (or None), N, K, and optionally alpha (1.0), deps
+    (indices of earlier entries) and ldx (elements between rows of x; 0, the
+    default, means K).  The library chooses the form.  Returns the pass
+    handle (an int)."""
+    arr, n = _pass_array(linears)
     out = _vp()
     _check(_c["w4_pass_create"](arr, n, M, group, ctypes.byref(out)), "w4_pass_create")
+    return out.value
+
+
+def w4_pass_create_mode(linears, M, mode, group=GROUP):
+    """w4_pass_create with the form chosen: `mode` is W4_PASS_AUTO,
+    W4_PASS_PERSISTENT or W4_PASS_LAUNCHES."""
+    arr, n = _pass_array(linears)
+    out = _vp()
+    _check(_c["w4_pass_create_mode"](arr, n, M, group, mode, ctypes.byref(out)), "w4_pass_create_mode")
     return out.value
 
 

@@ -81,6 +81,17 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 l (the LDS line address travels in M0, wave-uniform).  Issued
+// from inline asm so the compiler's wait-count pass does not see it; callers
+// wait for it with an explicit s_waitcnt vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory", "m0");
+}
+
 // Split-K partial sums travel through device memory with agent-scope (sc1)
 // stores and loads, which are made visible at, and read from, the device
 // coherence point directly.  No L2 write-back or invalidate is needed; those

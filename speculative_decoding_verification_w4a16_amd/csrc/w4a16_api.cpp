@@ -548,10 +548,16 @@ void pass_free(w4_pass* p) {
 extern "C" {
 
 int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pass** out) {
+    return w4_pass_create_mode(linears, n, M, group, W4_PASS_AUTO, out);
+}
+
+int w4_pass_create_mode(const w4_pass_linear* linears, int n, int M, int group, int mode, w4_pass** out) {
     if (!out) return W4_ERR_INVALID;
     *out = nullptr;
     if (n < 0 || M < 0 || (n > 0 && !linears)) return W4_ERR_INVALID;
+    if (mode != W4_PASS_AUTO && mode != W4_PASS_PERSISTENT && mode != W4_PASS_LAUNCHES) return W4_ERR_INVALID;
     if (group != w4::kGroup || M > W4_MAX_M || n > W4_PASS_MAX_LINEARS) return W4_ERR_UNSUPPORTED;
+    if (mode == W4_PASS_PERSISTENT && M > w4::kPassMaxM) return W4_ERR_UNSUPPORTED;
     for (int i = 0; i < n; ++i) {
         int rc = check_pass_linear(linears[i], i, M, group);
         if (rc != W4_OK) return rc;
@@ -565,7 +571,9 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
     p->n = n;
     p->M = M;
     p->lin.assign(linears, linears + n);
-    p->persistent = M >= 1 && M <= w4::kPassMaxM;
+    // the persistent kernel is possible at M <= kPassMaxM; whether it is
+    // chosen is decided once the dependency classes are known
+    p->persistent = M >= 1 && M <= w4::kPassMaxM && mode != W4_PASS_LAUNCHES;
     hipError_t e = hipGetDevice(&p->device);
     if (e != hipSuccess) {
         pass_free(p);
@@ -613,6 +621,26 @@ int w4_pass_create(const w4_pass_linear* linears, int n, int M, int group, w4_pa
             for (int j = 0; j <= i && t.dep_class < 0; ++j)
                 if (linears[j].ndeps == d.ndeps && sorted_deps(linears[j]) == mine) t.dep_class = j;
         }
+    }
+    // Which form (W4_PASS_AUTO).  The persistent kernel pays, at each
+    // dependency class, the wait for its producers' last units and a memory
+    // round trip before the first multiply-add; per-linear launches pay a
+    // launch gap per linear and run the linears of a class one after the
+    // other.  Measured on MI355X over the 80-layer Llama-3-70B pass (M = 1 /
+    // M = 5): with q, k, v and gate, up as separate linears (561 linears in
+    // 321 classes) the persistent kernel takes 7.6 / 8.6 ms against 8.9 /
+    // 9.8 for launches; with q|k|v and gate|up fused (321 linears, one per
+    // class) 7.6 / 8.6 against 7.1 / 7.8.  So the persistent kernel is chosen
+    // when the classes hold at least 1.25 linears on average.
+    if (p->persistent && mode == W4_PASS_AUTO) {
+        long classes = 0;
+        bool free_class = false;  // linears without producers form one class
+        for (int i = 0; i < n; ++i) {
+            if (tab[i].dep_class < 0) free_class = true;
+            else if (tab[i].dep_class == i) ++classes;
+        }
+        classes += free_class ? 1 : 0;
+        p->persistent = 4L * n >= 5L * classes;
     }
     // K slices.  The linears of one dependency class run side by side, and
     // their consumers wait for all of them; when together they have fewer

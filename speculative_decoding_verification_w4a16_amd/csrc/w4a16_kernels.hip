@@ -545,17 +545,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds + 16 l (the LDS line address travels in M0, wave-uniform).  Issued
-// from inline asm so the compiler's wait-count pass does not see it; callers
-// wait for it with wait_vmcnt.
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
-    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory", "m0");
-}
-
 template <int MB, int WV>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2))) void w4a16_mfma_lds_kernel(LinearArgs a) {
     static_assert(WV == 4 || WV == 8, "four or eight chunks per workgroup");

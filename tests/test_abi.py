@@ -335,5 +335,16 @@ def test_pass_validation_before_any_hip_call():
     arr = (w4.W4PassLinear * 1)(_pl(X0, Y0, **wt(0)))
     assert w4._c["w4_pass_create"](arr, 1, 4, 64, ctypes.byref(out)) == w4.W4_ERR_UNSUPPORTED
     assert w4._c["w4_pass_create"](arr, 1, 4, 128, None) == w4.W4_ERR_INVALID
+    # the form: an unknown mode is invalid, the persistent kernel above M = 16
+    # unsupported, and both are checked before any HIP call
+    for mode in (-1, 3):
+        assert w4._c["w4_pass_create_mode"](arr, 1, 4, 128, mode, ctypes.byref(out)) == w4.W4_ERR_INVALID, mode
+    assert w4._c["w4_pass_create_mode"](arr, 1, 17, 128, w4.W4_PASS_PERSISTENT,
+                                        ctypes.byref(out)) == w4.W4_ERR_UNSUPPORTED
+    assert w4._c["w4_pass_create_mode"](arr, 1, 4, 128, w4.W4_PASS_PERSISTENT, None) == w4.W4_ERR_INVALID
+    bad_mode = [_pl(X0, Y0, **wt(0)), _pl(Y0, Y1, K=256, **wt(1))]  # an unlisted dependency, any mode
+    arr2 = (w4.W4PassLinear * 2)(*bad_mode)
+    for mode in (w4.W4_PASS_AUTO, w4.W4_PASS_PERSISTENT, w4.W4_PASS_LAUNCHES):
+        assert w4._c["w4_pass_create_mode"](arr2, 2, 4, 128, mode, ctypes.byref(out)) == w4.W4_ERR_INVALID, mode
     assert w4._c["w4_pass_run"](None, None) == w4.W4_ERR_INVALID
     assert w4._c["w4_pass_destroy"](None) == w4.W4_OK

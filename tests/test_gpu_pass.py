@@ -8,13 +8,18 @@ layer's q, k and v read down's output; the lm_head reads the last down's.
 Every linear writes its bf16 output (the next activation) and some also fp32,
 scaled by a power-of-two alpha that keeps magnitudes near 1.
 
+The same chain with q|k|v and gate|up fused (o and down reading column
+slices of the fused outputs through a row stride) runs in both forms of a
+pass: the library chooses per-linear launches for it (one linear per
+dependency class), the persistent kernel when asked.
+
 Each output is checked against the oracle applied to the input the linear
 actually read (its producer's output buffer after the run), so a consumer
 that read its input before the producer finished would not match.  Between
 runs the external input changes and every output is filled with NaN first:
 a stale or early read shows up as a mismatch or a NaN.  Cases: the
 persistent kernel at M = 1 (GEMV) and 2, 5, 8, 16 (MFMA), the per-linear
-launches at M = 17 and 64, a HIP graph replayed with eager changes between
+launches at M = 1, 5, 16 (asked for), 17 and 64, a HIP graph replayed with eager changes between
 replays, a forced dependency-wait timeout (spin limit 0) and recovery, a
 producer split into K slices across workgroups (the last slice of a chunk
 adds the partial tiles) read by its consumer, a consumer reading a column
@@ -48,14 +53,15 @@ def _alpha(K):
 class Chain:
     """Weights, buffers and the pass descriptors of a layered chain."""
 
-    def __init__(self, M, H, KV, F, layers, vocab, seed=7000, fp32_leaves=True):
+    def __init__(self, M, H, KV, F, layers, vocab, seed=7000, fp32_leaves=True, fused=False,
+                 mode=None):
         self.M = M
         self.lins, self.descs, self.names = [], [], []
         self.x0 = torch.empty((M, H), dtype=torch.int16, device=DEV)
         self.bufs = []
         idx = {}
 
-        def add(name, N, K, x, deps, fp32):
+        def add(name, N, K, x, deps, fp32, ldx=0):
             lin = synth.gen_linear(seed + len(self.lins), N, K)
             pk = w4.repack(to_dev(lin["qweight"]), to_dev(lin["scales"]), to_dev(lin["zeros"]), N, K)
             yb = torch.empty((M, N), dtype=torch.int16, device=DEV)
@@ -65,11 +71,19 @@ class Chain:
             self.lins.append((lin, pk))
             self.names.append(name)
             self.descs.append(dict(x=x, qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t, y=y,
-                                   y_bf16=yb, N=N, K=K, alpha=_alpha(K), deps=[idx[d] for d in deps]))
+                                   y_bf16=yb, N=N, K=K, ldx=ldx, alpha=_alpha(K), deps=[idx[d] for d in deps]))
             return yb
 
         h, hdeps = self.x0, []
-        for L in range(layers):
+        for L in range(layers if fused else 0):
+            # q|k|v and gate|up as single linears: o reads the q columns of
+            # qkv's output, down the gate columns of gate_up's
+            qkv = add(f"qkv{L}", H + 2 * KV, H, h, hdeps, fp32_leaves)
+            o = add(f"o{L}", H, H, qkv, [f"qkv{L}"], False, ldx=H + 2 * KV)
+            gu = add(f"gate_up{L}", 2 * F, H, o, [f"o{L}"], fp32_leaves)
+            h = add(f"down{L}", H, F, gu, [f"gate_up{L}"], True, ldx=2 * F)
+            hdeps = [f"down{L}"]
+        for L in range(0 if fused else layers):
             q = add(f"q{L}", H, H, h, hdeps, False)
             add(f"k{L}", KV, H, h, hdeps, fp32_leaves)
             add(f"v{L}", KV, H, h, hdeps, fp32_leaves)
@@ -80,7 +94,8 @@ class Chain:
             hdeps = [f"down{L}"]
         if vocab:
             add("lm_head", vocab, H, h, hdeps, True)
-        self.handle = w4.w4_pass_create(self.descs, M)
+        self.handle = (w4.w4_pass_create(self.descs, M) if mode is None
+                       else w4.w4_pass_create_mode(self.descs, M, mode))
 
     def close(self):
         w4.w4_pass_destroy(self.handle)
@@ -101,7 +116,7 @@ class Chain:
         torch.cuda.synchronize()
         worst = 0.0
         for (lin, pk), d, name in zip(self.lins, self.descs, self.names):
-            x = d["x"].cpu().numpy().view(np.uint16)
+            x = d["x"].cpu().numpy().view(np.uint16)[:, :d["K"]].copy()  # the columns the linear reads
             assert np.all(np.isfinite(bf16_bits_to_f64(x))), (what, name, "input not finite")
             Y, A = linear64_gemm(x, lin["qweight"], lin["scales"], lin["zeros"], 128, 0, d["N"])
             al = d["alpha"]
@@ -120,11 +135,17 @@ class Chain:
 SMALL = dict(H=1024, KV=128, F=2816, layers=2, vocab=4096)
 
 
-@pytest.mark.parametrize("M", [1, 2, 5, 8, 16, 17, 64])
-def test_chain_against_the_oracle_with_changing_inputs(M):
-    ch = Chain(M, **SMALL)
+AUTO, PERSISTENT, LAUNCHES = w4.W4_PASS_AUTO, w4.W4_PASS_PERSISTENT, w4.W4_PASS_LAUNCHES
+
+
+@pytest.mark.parametrize("M,mode", [(1, AUTO), (2, AUTO), (5, AUTO), (8, AUTO), (16, AUTO), (17, AUTO), (64, AUTO),
+                                    (1, LAUNCHES), (5, LAUNCHES), (16, LAUNCHES)])
+def test_chain_against_the_oracle_with_changing_inputs(M, mode):
+    # q, k, v share their producers, as do gate and up: 14 linears in 8
+    # classes, so the library's choice at M <= 16 is the persistent kernel
+    ch = Chain(M, **SMALL, mode=mode)
     info = w4.w4_pass_info(ch.handle)
-    assert info["persistent"] == (1 if M <= 16 else 0), info
+    assert info["persistent"] == (1 if M <= 16 and mode != LAUNCHES else 0), info
     assert info["units"] == 2 * (16 + 2 + 2 + 16 + 44 + 44 + 16) + 64
     try:
         for run, seed in enumerate((8100, 8200, 8300)):
@@ -134,6 +155,26 @@ def test_chain_against_the_oracle_with_changing_inputs(M):
             w4.w4_pass_check(ch.handle)
             worst = ch.check((M, run))
         print(f"M={M}: {info}, worst err/bound of the fp32 outputs {worst:.2e}")
+    finally:
+        ch.close()
+
+
+@pytest.mark.parametrize("M,mode", [(1, AUTO), (5, AUTO), (1, PERSISTENT), (5, PERSISTENT), (16, PERSISTENT),
+                                    (33, AUTO)])
+def test_fused_chain_in_both_forms(M, mode):
+    # q|k|v and gate|up fused: one linear per dependency class, so the
+    # library's choice is per-linear launches; the persistent kernel, asked
+    # for, computes the same chain (strided reads of the fused outputs)
+    ch = Chain(M, **SMALL, fused=True, mode=mode)
+    info = w4.w4_pass_info(ch.handle)
+    assert info["persistent"] == (1 if mode == PERSISTENT else 0), info
+    try:
+        for run, seed in enumerate((8150, 8250)):
+            ch.set_input(seed)
+            ch.poison()
+            w4.w4_pass_run(ch.handle)
+            w4.w4_pass_check(ch.handle)
+            ch.check(("fused", M, mode, run))
     finally:
         ch.close()
 
@@ -167,7 +208,7 @@ def test_forced_wait_timeout_is_reported_and_recovered():
     # spin limit 0: every dependency wait not already satisfied gives up at
     # once (the launch still runs to its end); the check reports it, and the
     # next run with the default limit is correct again
-    ch = Chain(1, **SMALL)
+    ch = Chain(1, **SMALL, mode=PERSISTENT)
     try:
         ch.set_input(8800)
         w4.w4_pass_set_spin_limit(ch.handle, 0)
@@ -203,7 +244,7 @@ def test_k_split_producer_against_the_oracle(M):
                   N=N1, K=K1, alpha=a1, deps=[]),
              dict(x=h, qweight_t=pk2.qweight_t, scales_t=pk2.scales_t, zeros_t=pk2.zeros_t, y=y2, y_bf16=None,
                   N=N2, K=N1, alpha=1.0, deps=[0])]
-    hd = w4.w4_pass_create(descs, M)
+    hd = w4.w4_pass_create_mode(descs, M, PERSISTENT)
     try:
         info = w4.w4_pass_info(hd)
         assert info["persistent"] == 1 and info["units"] > (N1 // 64) + (N2 // 64), info  # the producer is split
@@ -228,12 +269,13 @@ def test_k_split_producer_against_the_oracle(M):
         w4.w4_pass_destroy(hd)
 
 
-@pytest.mark.parametrize("M", [1, 5, 17, 64])
-def test_consumer_reads_a_column_slice_of_a_fused_output(M):
+@pytest.mark.parametrize("M,mode", [(1, PERSISTENT), (5, PERSISTENT), (1, LAUNCHES), (5, LAUNCHES), (17, AUTO),
+                                    (64, AUTO)])
+def test_consumer_reads_a_column_slice_of_a_fused_output(M, mode):
     # a fused producer (q|k|v-like: N = 1024 + 256 + 256) writes [M, 1536];
     # its consumer reads the first 1024 columns of each row (ldx = 1536), as
-    # o reads the q part of a fused q|k|v output -- the persistent kernel at
-    # M <= 16, the per-linear launches above
+    # o reads the q part of a fused q|k|v output -- in the persistent kernel
+    # and in per-linear launches
     H, NF, N2 = 1024, 1536, 512
     lin1, lin2 = synth.gen_linear(9400, NF, H), synth.gen_linear(9401, N2, H)
     pk1 = w4.repack(to_dev(lin1["qweight"]), to_dev(lin1["scales"]), to_dev(lin1["zeros"]), NF, H)
@@ -245,7 +287,8 @@ def test_consumer_reads_a_column_slice_of_a_fused_output(M):
                   N=NF, K=H, alpha=_alpha(H), deps=[]),
              dict(x=f, qweight_t=pk2.qweight_t, scales_t=pk2.scales_t, zeros_t=pk2.zeros_t, y=y2, y_bf16=None,
                   N=N2, K=H, ldx=NF, alpha=1.0, deps=[0])]
-    hd = w4.w4_pass_create(descs, M)
+    hd = w4.w4_pass_create_mode(descs, M, mode)
+    assert w4.w4_pass_info(hd)["persistent"] == (1 if mode == PERSISTENT else 0)
     try:
         for seed in (9500, 9600):
             x0.copy_(to_dev(synth.gen_x(M, H, seed_base=seed)))
