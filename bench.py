@@ -84,6 +84,8 @@ def parse():
     p.add_argument("--no-parity", action="store_true", help="skip the oracle spot checks")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the fused-projection and acceptance measurements (profiling runs of the sweep)")
+    p.add_argument("--pass-mode", choices=("auto", "persistent", "launches"), default="auto",
+                   help="the form of the measured passes at M <= 16 (default: the library's choice)")
     p.add_argument("--headline-only", action="store_true",
                    help="only the measured passes (profiling runs): no comparison passes, extras, parity or CPU "
                         "baseline")
@@ -105,6 +107,9 @@ def parse():
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="instead of running: turn two rocprofv3 --pmc runs of the sweep (FETCH_SIZE, WRITE_SIZE; "
                         "taken with --copy-calib) into profiles/traffic.json")
+    p.add_argument("--trace-summary", metavar="TRACE_DIR",
+                   help="instead of running: per-linear kernel time of each measured pass from a rocprofv3 "
+                        "--kernel-trace run of --headline-only (run_kernel_trace.csv)")
     p.add_argument("--copy-calib", type=int, default=0,
                    help="with --shapes: also run w4_bench_copy over this many MiB (HBM counter calibration)")
     return p.parse_args()
@@ -812,6 +817,45 @@ def traffic_from_pmc(fetch_dir, write_dir, copy_mib, out_path):
     return out
 
 
+def trace_summary(trace_dir):
+    """Per-linear kernel time of the measured passes from a rocprofv3
+    --kernel-trace run of `bench.py --headline-only`: every dispatch of a
+    per-linear kernel, plus the split-K reduction dispatched right after it,
+    is one linear of the pass at the M that kernel serves (as in
+    traffic_from_pmc); a persistent pass kernel dispatch is a whole pass.
+    Returns {M: {kernel, linears (dispatches), mean_us (kernel + its
+    reduction), kernel_mean_us (kernel alone)}}."""
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    keys = (("w4_pass_kernel<0", "1"), ("w4_pass_kernel<1", "5"), ("w4a16_gemv_kernel", "1"),
+            ("w4a16_mfma_direct_kernel", "5"), ("w4a16_mfma_lds_kernel", "64"))
+    out, cur = {}, None
+    for r in rows:
+        name = r["Kernel_Name"]
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if "splitk_reduce" in name:
+            if cur is not None:
+                out[cur]["total_us"] += dur
+            continue
+        cur = next((m for k, m in keys if k in name), None)
+        if cur is None:
+            continue
+        e = out.setdefault(cur, {"kernels": set(), "linears": 0, "total_us": 0.0, "kernel_us": 0.0})
+        short = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        e["kernels"].add(short[:short.index(">(") + 1] if ">(" in short else short.split("(")[0])
+        e["linears"] += 1
+        e["total_us"] += dur
+        e["kernel_us"] += dur
+    return {m: {"kernels": sorted(e["kernels"]), "dispatches": e["linears"],
+                "mean_us": round(e["total_us"] / e["linears"], 3),
+                "kernel_mean_us": round(e["kernel_us"] / e["linears"], 3)} for m, e in sorted(out.items())}
+
+
 def shapes_report(args):
     """Per-linear microseconds and effective TB/s (the tiny, plain-decode,
     sequence-draft and tree-draft configurations' shapes)."""
@@ -950,6 +994,9 @@ def main():
     if args.floor:
         floor_report(args)
         return
+    if args.trace_summary:
+        print(json.dumps(trace_summary(args.trace_summary)))
+        return
     if args.traffic_from:
         out = traffic_from_pmc(args.traffic_from[0], args.traffic_from[1], args.copy_calib or 1024,
                                os.path.join(ROOT, "profiles", "traffic.json"))
@@ -984,7 +1031,8 @@ def main():
     # that share an input fused (q|k|v, gate|up), each linear reading its
     # producer's output
     fpk = fuse_projections(w4, packed)
-    passes = {M: fused_dependent_pass(torch, w4, fpk, M) for M in PASS_M}
+    forced = {"auto": None, "persistent": w4.W4_PASS_PERSISTENT, "launches": w4.W4_PASS_LAUNCHES}[args.pass_mode]
+    passes = {M: fused_dependent_pass(torch, w4, fpk, M, mode=forced if M <= 16 else None) for M in PASS_M}
     pass_bytes = {M: sum(alg_bytes(M, d["N"], d["K"], 2) for d in passes[M][3]) for M in PASS_M}
     pass_flops = {M: sum(alg_flops(M, d["N"], d["K"]) for d in passes[M][3]) for M in PASS_M}
     nlaunch = len(passes[PASS_M[0]][3])
@@ -1207,7 +1255,8 @@ def main():
                        s["N"] * s["K"] * 0.51953125 for s in specs)), "graph": True,
                    "dependencies": "each linear reads its producer's bf16 output (o: the q columns of qkv's, "
                                    "down: the gate columns of gate_up's)", "output": "bf16",
-                   "launches_per_pass": {str(M): (1 if info[M]["persistent"] else nlaunch) for M in PASS_M}},
+                   "launches_per_pass": {str(M): (1 if info[M]["persistent"] else nlaunch) for M in PASS_M},
+                   "pass_mode": args.pass_mode},
         "us_per_pass": {str(M): round(us_per_pass[M], 1) for M in PASS_M},
         "us_per_pass_eager": {str(M): round(us_eager[M], 1) for M in PASS_M},
         "persistent_form": {"linears_per_pass": nlaunch,
