@@ -107,6 +107,9 @@ def parse():
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="instead of running: turn two rocprofv3 --pmc runs of the sweep (FETCH_SIZE, WRITE_SIZE; "
                         "taken with --copy-calib) into profiles/traffic.json")
+    p.add_argument("--curve-from", metavar="SHAPES_JSONL",
+                   help="instead of running: the markdown tables of a --shapes run's JSON lines (us per call, "
+                        "t(M)/t(1) with one layer's sum, TB/s, roofline fraction)")
     p.add_argument("--trace-summary", metavar="TRACE_DIR",
                    help="instead of running: per-linear kernel time of each measured pass from a rocprofv3 "
                         "--kernel-trace run of --headline-only (run_kernel_trace.csv)")
@@ -817,6 +820,45 @@ def traffic_from_pmc(fetch_dir, write_dir, copy_mib, out_path):
     return out
 
 
+def curve_tables(path):
+    """Markdown tables of a --shapes run (its JSON lines in `path`): us per
+    call, t(M)/t(1) (with one decoder layer summed, separate and fused),
+    effective TB/s and the roofline fraction, per linear and M."""
+    d = {}
+    for line in open(path):
+        if line.startswith("{"):
+            r = json.loads(line)
+            if "linear" in r and "M" in r:
+                d[(r["linear"], r["M"])] = r
+    names = [n for n in ("q", "k", "v", "o", "gate", "up", "down", "lm_head", "qkv", "gate_up")
+             if any(k[0] == n for k in d)]
+    ms = sorted({k[1] for k in d})
+    head = "| linear | " + " | ".join(f"M = {m}" for m in ms) + " |\n|---|" + "---|" * len(ms)
+    layers = [("one layer, 7 launches", ("q", "k", "v", "o", "gate", "up", "down")),
+              ("one layer, fused (4 launches)", ("qkv", "o", "gate_up", "down"))]
+    out = []
+
+    def table(title, value, fmt, sums=False):
+        out.append(f"## {title}\n\n{head}")
+        for n in names:
+            out.append(f"| {n} | " + " | ".join(fmt % value(n, m) for m in ms) + " |")
+        for label, parts in (layers if sums else ()):
+            if all((p_, m) in d for p_ in parts for m in ms):
+                t1 = sum(d[(p_, ms[0])]["us"] for p_ in parts)
+                out.append(f"| {label} | " + " | ".join("%.2f" % (sum(d[(p_, m)]["us"] for p_ in parts) / t1)
+                                                        for m in ms) + " |")
+        out.append("")
+
+    table("us per call (median)", lambda n, m: d[(n, m)]["us"], "%.1f")
+    table("t(M) / t(1)", lambda n, m: d[(n, m)]["us"] / d[(n, ms[0])]["us"], "%.2f", sums=True)
+    table("Effective TB/s (algorithmic bytes / t)", lambda n, m: d[(n, m)]["tbps"], "%.2f")
+    table("Fraction of the roofline, max(bytes / 8 TB/s, flops / 2.5 PFLOP/s) / t",
+          lambda n, m: d[(n, m)]["roofline_frac"], "%.2f")
+    table("Spread: (max - min) / median of the repeats",
+          lambda n, m: (d[(n, m)]["us_max"] - d[(n, m)]["us_min"]) / d[(n, m)]["us"], "%.3f")
+    return "\n".join(out)
+
+
 def trace_summary(trace_dir):
     """Per-linear kernel time of the measured passes from a rocprofv3
     --kernel-trace run of `bench.py --headline-only`: every dispatch of a
@@ -923,9 +965,10 @@ def shapes_report(args):
 def floor_report(args):
     """Separate-launch floor: a plain 128-bit streaming read (w4_bench_read,
     graph-replayed over rotating buffers past the MALL) of each linear's packed
-    bytes, an empty launch, and the sum of those reads over the 561 linears of
-    a pass -- the least time any design that keeps one launch per linear can
-    take, against the 8 TB/s roofline of the same bytes."""
+    bytes, an empty launch, and the sum of those reads over the linears of a
+    pass -- the 561 separate linears, and the 321 with q|k|v and gate|up fused
+    -- the least time any design that keeps one launch per linear can take,
+    against the 8 TB/s roofline of the same bytes."""
     import torch
 
     import speculative_decoding_verification_w4a16_amd as w4
@@ -959,7 +1002,9 @@ def floor_report(args):
     us_empty = timed(16, tiny)
     del tiny
     print(json.dumps({"launch": "w4_bench_read of 16 bytes", "us": round(us_empty, 3)}), flush=True)
-    shapes = list(synth.LAYER_LINEARS) + [synth.LM_HEAD]
+    dims = {name: (N, K) for name, N, K in synth.LAYER_LINEARS}
+    fused = [(f, sum(dims[n][0] for n in names), dims[names[0]][1]) for f, names in FUSED_GROUPS if len(names) > 1]
+    shapes = list(synth.LAYER_LINEARS) + fused + [synth.LM_HEAD]
     floors = {}
     for name, N, K in shapes:
         nbytes = (int(N * K * 0.51953125) + 15) // 16 * 16
@@ -976,9 +1021,15 @@ def floor_report(args):
     pass_us = synth.N_LAYERS * sum(floors[n] for n, _, _ in synth.LAYER_LINEARS) + floors["lm_head"]
     pass_bytes = synth.N_LAYERS * sum(N * K * 0.51953125 for _, N, K in synth.LAYER_LINEARS) + \
         synth.LM_HEAD[1] * synth.LM_HEAD[2] * 0.51953125
-    print(json.dumps({"pass_floor_us": round(pass_us, 1), "pass_bytes": int(pass_bytes),
+    print(json.dumps({"pass": "561 linears", "pass_floor_us": round(pass_us, 1), "pass_bytes": int(pass_bytes),
                       "floor_tbps": round(pass_bytes / (pass_us * 1e-6) / 1e12, 4),
                       "floor_roofline_frac": round(pass_bytes / (HBM_PEAK_GBS * 1e9) * 1e6 / pass_us, 4)}),
+          flush=True)
+    fused_us = synth.N_LAYERS * sum(floors[f] for f, _ in FUSED_GROUPS) + floors["lm_head"]
+    print(json.dumps({"pass": "321 linears (q|k|v and gate|up fused)", "pass_floor_us": round(fused_us, 1),
+                      "pass_bytes": int(pass_bytes),
+                      "floor_tbps": round(pass_bytes / (fused_us * 1e-6) / 1e12, 4),
+                      "floor_roofline_frac": round(pass_bytes / (HBM_PEAK_GBS * 1e9) * 1e6 / fused_us, 4)}),
           flush=True)
 
 
@@ -993,6 +1044,9 @@ def main():
         return
     if args.floor:
         floor_report(args)
+        return
+    if args.curve_from:
+        print(curve_tables(args.curve_from))
         return
     if args.trace_summary:
         print(json.dumps(trace_summary(args.trace_summary)))
