@@ -181,7 +181,6 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
     if (u < a.U) {
         const int o = lane >> 4, t = lane & 15;
         const uint32_t mask = a.mask, magic = to_vgpr(a.magic);
-        const bool xvalid = MB == 0 || t < a.M;
         const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2});
 
         // Completion of a producer: its chunk c counts on sub-counter c % 64,
@@ -283,8 +282,8 @@ __global__ __launch_bounds__(64 * W) void w4_pass_kernel(const PassLinear* __res
                 f32x4 acc[4], accx;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const u32x4 raw = xvalid ? rx[d][kk] : u32x4{0, 0, 0, 0};
-                    const bf16x8 av = __builtin_bit_cast(bf16x8, raw);
+                    // rows past M hold row M - 1 again (their sums are never stored)
+                    const bf16x8 av = __builtin_bit_cast(bf16x8, rx[d][kk]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const bf16x8 bv = __builtin_bit_cast(bf16x8, unpack_biased(rw[d][kk][j], mask, magic));

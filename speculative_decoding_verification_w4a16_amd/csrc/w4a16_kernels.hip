@@ -361,9 +361,11 @@ __global__ __launch_bounds__(kMaxThreads) void w4a16_gemv_kernel(LinearArgs a) {
 // For small M the activation rows are tiny and L1/L2-resident, so each lane
 // loads its own A operand (row 16mb + l%16, k-octet l/16 of each k-block)
 // from global memory in the same ring as the weights: no LDS, no barriers.
-// Rows past M are zeroed in registers.  One extra MFMA per k-block against an
-// all-ones B operand yields the per-(row, group) sums of x that the
-// zero-point term needs, already in the result layout (rows 4(l/16) + r).
+// Rows past M load row M - 1 again: an MFMA output row depends on its own A
+// row only, and rows past M are never stored, so they need no zeroing.  One
+// extra MFMA per k-block against an all-ones B operand yields the
+// per-(row, group) sums of x that the zero-point term needs, already in the
+// result layout (rows 4(l/16) + r).
 
 template <int MB, int R>
 __global__ __launch_bounds__(kMaxThreads) void w4a16_mfma_direct_kernel(LinearArgs a) {
@@ -375,11 +377,9 @@ __global__ __launch_bounds__(kMaxThreads) void w4a16_mfma_direct_kernel(LinearAr
     const uint32_t mask = a.mask, magic = to_vgpr(a.magic);
     const WaveStream ws = wave_stream(a, min(c, a.NC - 1), g0, lane);
     const u32x4* xp[MB];
-    bool xvalid[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int row = 16 * mb + t;
-        xvalid[mb] = row < a.M;
         xp[mb] = (const u32x4*)(a.x + (size_t)min(row, a.M - 1) * a.ldx + (size_t)g0 * kGroup + 8 * o);
     }
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2});
@@ -405,6 +405,29 @@ __global__ __launch_bounds__(kMaxThreads) void w4a16_mfma_direct_kernel(LinearAr
 #pragma unroll
         for (int j = 0; j < 4; ++j) yv[mb][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // A group's scale epilogue runs after the next group's MFMAs are issued:
+    // the VALU reads an MFMA result only once the MFMA has finished, which
+    // takes far longer than forwarding it to a dependent MFMA, so reading a
+    // group's accumulators right after its last MFMA stalled the wave every
+    // group.  Two sets of accumulators (and of the group's scales and zeros)
+    // alternate with the group's parity, which is the ring slot's (R even).
+    // The epilogues still add into yv in group order.
+    static_assert(R % 2 == 0, "accumulator sets alternate with the ring slot");
+    f32x4 acc[2][MB][4], accx[2][MB];
+    float sjh[2][4];
+    uint32_t zwh[2];
+    auto epilogue = [&](int b) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float cz = biased_zero(zwh[b], j);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    yv[mb][j][r] = fmaf(sjh[b][j], fmaf(-cz, accx[b][mb][r], acc[b][mb][j][r]), yv[mb][j][r]);
+            }
+    };
+
 #pragma unroll
     for (int d = 0; d < R; ++d) load(d, min(d, ng - 1));
     for (int gb = 0; gb < ng; gb += R) {
@@ -412,44 +435,38 @@ __global__ __launch_bounds__(kMaxThreads) void w4a16_mfma_direct_kernel(LinearAr
         for (int d = 0; d < R; ++d) {
             const int gl = gb + d;
             if (gl < ng) {
-                f32x4 acc[MB][4], accx[MB];
+                const int b = d & 1;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     bf16x8 av[MB];
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        const u32x4 raw = xvalid[mb] ? rx[d][kk][mb] : u32x4{0, 0, 0, 0};
-                        av[mb] = __builtin_bit_cast(bf16x8, raw);
-                    }
+                    for (int mb = 0; mb < MB; ++mb) av[mb] = __builtin_bit_cast(bf16x8, rx[d][kk][mb]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const u32x4 braw = unpack_biased(rw[d][kk][j], mask, magic);
                         const bf16x8 bv = __builtin_bit_cast(bf16x8, braw);
 #pragma unroll
                         for (int mb = 0; mb < MB; ++mb)
-                            acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                av[mb], bv, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[mb][j], 0, 0, 0);
+                            acc[b][mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                av[mb], bv, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[b][mb][j], 0, 0, 0);
                     }
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
-                        accx[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            av[mb], ones, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : accx[mb], 0, 0, 0);
+                        accx[b][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            av[mb], ones, kk == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : accx[b][mb], 0, 0, 0);
                 }
-                float sj[4];
-                decode_scales(rs[d], sj);
-                const uint32_t zw = rz[d];
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float cz = biased_zero(zw, j);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            yv[mb][j][r] = fmaf(sj[j], fmaf(-cz, accx[mb][r], acc[mb][j][r]), yv[mb][j][r]);
-                    }
+                decode_scales(rs[d], sjh[b]);
+                zwh[b] = rz[d];
+                if (gl > 0) epilogue(b ^ 1);  // the previous group's
             }
             load(d, min(gl + R, ng - 1));
         }
+    }
+    if (ng > 0) {  // the last group's epilogue
+        if ((ng - 1) & 1)
+            epilogue(1);
+        else
+            epilogue(0);
     }
 
     if (a.kw > 1) {
