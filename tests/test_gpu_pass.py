@@ -24,7 +24,8 @@ replays, a forced dependency-wait timeout (spin limit 0) and recovery, a
 producer split into K slices across workgroups (the last slice of a chunk
 adds the partial tiles) read by its consumer, a consumer reading a column
 slice of a fused output through a row stride, and one full-size
-Llama-3-70B layer at M = 1 and 5 (its down projection is K-split).
+Llama-3-70B layer at M = 1 and 5 (its down projection is K-split), separate
+and fused (the fused one in both forms).
 """
 import math
 
@@ -118,17 +119,21 @@ class Chain:
         for (lin, pk), d, name in zip(self.lins, self.descs, self.names):
             x = d["x"].cpu().numpy().view(np.uint16)[:, :d["K"]].copy()  # the columns the linear reads
             assert np.all(np.isfinite(bf16_bits_to_f64(x))), (what, name, "input not finite")
-            Y, A = linear64_gemm(x, lin["qweight"], lin["scales"], lin["zeros"], 128, 0, d["N"])
+            yb_all = bf16_bits_to_f64(d["y_bf16"].cpu().numpy().view(np.uint16))
+            y_all = d["y"].cpu().numpy().astype(np.float64) if d["y"] is not None else None
             al = d["alpha"]
-            Y, A = Y * al, A * al
-            yb = bf16_bits_to_f64(d["y_bf16"].cpu().numpy().view(np.uint16))
-            err = np.abs(yb - Y)
-            bound = 4e-3 * A * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(Y)
-            assert np.all(err <= bound), (what, name, float(np.nanmax(err / bound)))
-            if d["y"] is not None:
-                y = d["y"].cpu().numpy().astype(np.float64)
-                assert np.all(np.abs(y - Y) <= 4e-3 * A), (what, name)
-                worst = max(worst, float(np.max(np.abs(y - Y) / np.maximum(4e-3 * A, 1e-300))))
+            # column blocks keep the float64 weights of a full-size linear small
+            for n0 in range(0, d["N"], 8192):
+                n1 = min(d["N"], n0 + 8192)
+                Y, A = linear64_gemm(x, lin["qweight"], lin["scales"], lin["zeros"], 128, n0, n1)
+                Y, A = Y * al, A * al
+                err = np.abs(yb_all[:, n0:n1] - Y)
+                bound = 4e-3 * A * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(Y)
+                assert np.all(err <= bound), (what, name, n0, float(np.nanmax(err / bound)))
+                if y_all is not None:
+                    y = y_all[:, n0:n1]
+                    assert np.all(np.abs(y - Y) <= 4e-3 * A), (what, name, n0)
+                    worst = max(worst, float(np.max(np.abs(y - Y) / np.maximum(4e-3 * A, 1e-300))))
         return worst
 
 
@@ -321,3 +326,23 @@ def test_full_size_llama_layer(M):
         print(f"Llama-3-70B layer M={M}: worst err/bound {worst:.2e}")
     finally:
         ch.close()
+
+
+@pytest.mark.parametrize("M,mode", [(1, AUTO), (5, AUTO), (5, PERSISTENT)])
+def test_full_size_fused_llama_layer(M, mode):
+    # one Llama-3-70B decoder layer with q|k|v and gate|up fused (qkv N = 10240,
+    # gate_up N = 57344; o and down read column slices of them), in the
+    # library's choice of form (per-linear launches) and in the persistent
+    # kernel, every column of every output against the oracle
+    ch = Chain(M, H=8192, KV=1024, F=28672, layers=1, vocab=0, seed=1100, fp32_leaves=True, fused=True, mode=mode)
+    try:
+        assert w4.w4_pass_info(ch.handle)["persistent"] == (1 if mode == PERSISTENT else 0)
+        ch.set_input(2100)
+        ch.poison()
+        w4.w4_pass_run(ch.handle)
+        w4.w4_pass_check(ch.handle)
+        worst = ch.check(("fused llama layer", M, mode))
+        print(f"fused Llama-3-70B layer M={M} mode={mode}: worst err/bound {worst:.2e}")
+    finally:
+        ch.close()
+
