@@ -105,6 +105,20 @@ def test_tiny_config_all_kernels_and_splits(M):
 RAGGED_M = [1, 2, 3, 5, 8, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64]
 
 
+@pytest.mark.parametrize("N,K", [(320, 1024), (4096, 256)])
+def test_every_m_through_the_planner(N, K):
+    # every M from 1 to 64 through the planner's kernel choice: the GEMV
+    # (M = 1), the streaming MFMA kernel (rows past M repeat row M - 1 and
+    # must never reach y), the LDS kernel with one row block (M = 15, 16 on
+    # N >= 4096) and with two to four (M = 17..64)
+    lin = synth.gen_linear(70 + N, N, K)
+    x = synth.gen_x(64, K, seed_base=1700)
+    Y, A = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+    pk = packed(lin, N, K)
+    for M in range(1, 65):
+        _check(run_linear(x[:M], pk, w4.W4_KERNEL_AUTO, 0), Y[:M], A[:M], (N, K, M))
+
+
 @pytest.mark.parametrize("N,K", [(200, 384), (8, 128), (1000, 1152), (264, 256)])
 def test_ragged_shapes_every_m_block_boundary(N, K):
     lin = synth.gen_linear(50 + N + K, N, K)
