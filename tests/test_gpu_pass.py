@@ -346,3 +346,36 @@ def test_full_size_fused_llama_layer(M, mode):
     finally:
         ch.close()
 
+
+def test_every_m_in_the_persistent_kernel():
+    # a producer and its consumer at every M the persistent kernel takes
+    # (rows past M repeat row M - 1 in its MFMA form and must never reach an
+    # output), against the oracle on the input the consumer read
+    N1, K1, N2 = 512, 1024, 256
+    lin1, lin2 = synth.gen_linear(9900, N1, K1), synth.gen_linear(9901, N2, N1)
+    pk1 = w4.repack(to_dev(lin1["qweight"]), to_dev(lin1["scales"]), to_dev(lin1["zeros"]), N1, K1)
+    pk2 = w4.repack(to_dev(lin2["qweight"]), to_dev(lin2["scales"]), to_dev(lin2["zeros"]), N2, N1)
+    for M in range(1, 17):
+        x = synth.gen_x(M, K1, seed_base=9950)
+        x0 = to_dev(x)
+        h = torch.full((M, N1), 0x7FC0, dtype=torch.int16, device=DEV)
+        y2 = torch.full((M, N2), float("nan"), dtype=torch.float32, device=DEV)
+        descs = [dict(x=x0, qweight_t=pk1.qweight_t, scales_t=pk1.scales_t, zeros_t=pk1.zeros_t, y=None, y_bf16=h,
+                      N=N1, K=K1, alpha=_alpha(K1), deps=[]),
+                 dict(x=h, qweight_t=pk2.qweight_t, scales_t=pk2.scales_t, zeros_t=pk2.zeros_t, y=y2, y_bf16=None,
+                      N=N2, K=N1, alpha=1.0, deps=[0])]
+        hd = w4.w4_pass_create_mode(descs, M, PERSISTENT)
+        try:
+            w4.w4_pass_run(hd)
+            w4.w4_pass_check(hd)
+            torch.cuda.synchronize()
+        finally:
+            w4.w4_pass_destroy(hd)
+        a1 = _alpha(K1)
+        Y1, A1 = linear64_gemm(x, lin1["qweight"], lin1["scales"], lin1["zeros"], 128, 0, N1)
+        hb = h.cpu().numpy().view(np.uint16)
+        err1 = np.abs(bf16_bits_to_f64(hb) - a1 * Y1)
+        assert np.all(err1 <= 4e-3 * a1 * A1 * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(a1 * Y1)), (M, "producer")
+        Y2, A2 = linear64_gemm(hb, lin2["qweight"], lin2["scales"], lin2["zeros"], 128, 0, N2)
+        assert np.all(np.abs(y2.cpu().numpy().astype(np.float64) - Y2) <= 4e-3 * A2), (M, "consumer")
+
