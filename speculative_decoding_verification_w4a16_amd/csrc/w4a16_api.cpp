@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <map>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -495,42 +496,61 @@ int check_pass_linear(const w4_pass_linear& d, int i, int M, int group) {
 }
 
 // Hazards between the linears of a pass (see w4_pass_create).
+// The ranges of a pass, swept in address order: every pair of ranges whose
+// 128-byte lines meet is classified (outputs against outputs, weights and
+// inputs; inputs and weights may share lines with each other), so the check
+// takes O(n log n) plus the pairs that do meet, not a comparison of every
+// output with every other range.
 int check_pass_hazards(const w4_pass_linear* L, int n, int M) {
-    std::vector<Range> xs(n), ws;
-    struct Out {
-        Range r;
-        int owner;
+    enum Kind { kOut, kWeight, kIn };
+    struct Item {
+        Range r, lines;  // exact bytes, and rounded out to whole 128-byte lines
+        Kind kind;
+        int owner;       // the linear
     };
-    std::vector<Out> outs;
+    std::vector<Item> items;
+    items.reserve((size_t)n * 6);
+    auto add = [&](Range r, Kind k, int i) {
+        if (r.lo < r.hi) items.push_back(Item{r, lines_of(r), k, i});
+    };
     for (int i = 0; i < n; ++i) {
         const w4_pass_linear& d = L[i];
         size_t qb, sb, zb;
         tile_sizes(d.N, d.K, &qb, &sb, &zb);
-        xs[i] = range_of(d.x, pass_x_bytes(d, M));
-        ws.push_back(range_of(d.qweight_t, qb));
-        ws.push_back(range_of(d.scales_t, sb));
-        ws.push_back(range_of(d.zeros_t, zb));
-        if (d.y) outs.push_back(Out{range_of(d.y, (size_t)M * d.N * 4), i});
-        if (d.y_bf16) outs.push_back(Out{range_of(d.y_bf16, (size_t)M * d.N * 2), i});
+        add(range_of(d.x, pass_x_bytes(d, M)), kIn, i);
+        add(range_of(d.qweight_t, qb), kWeight, i);
+        add(range_of(d.scales_t, sb), kWeight, i);
+        add(range_of(d.zeros_t, zb), kWeight, i);
+        if (d.y) add(range_of(d.y, (size_t)M * d.N * 4), kOut, i);
+        if (d.y_bf16) add(range_of(d.y_bf16, (size_t)M * d.N * 2), kOut, i);
     }
-    for (size_t a = 0; a < outs.size(); ++a) {
-        const Range oa = outs[a].r, la = lines_of(oa);
-        const int j = outs[a].owner;
-        for (size_t b = a + 1; b < outs.size(); ++b)
-            if (meets(la, lines_of(outs[b].r))) return W4_ERR_INVALID;
-        for (const Range& w : ws)
-            if (meets(la, lines_of(w))) return W4_ERR_INVALID;
-        for (int i = 0; i < n; ++i) {
-            if (meets(oa, xs[i])) {
-                // linear i reads linear j's output: j must be earlier and a listed producer
-                if (i <= j) return W4_ERR_INVALID;
-                bool listed = false;
-                for (int k = 0; k < L[i].ndeps; ++k) listed = listed || L[i].deps[k] == j;
-                if (!listed) return W4_ERR_INVALID;
-            } else if (meets(la, lines_of(xs[i]))) {
-                return W4_ERR_INVALID;  // an unrelated input shares a cache line with the output
-            }
+    std::sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.lines.lo < b.lines.lo; });
+    // a pair whose lines meet: an output may meet only the inputs of its
+    // consumers (exactly, listed, later), never another output, weights or a
+    // line of any other input
+    auto pair_ok = [&](const Item& a, const Item& b) {
+        if (a.kind != kOut && b.kind != kOut) return true;
+        if (a.kind == kOut && b.kind == kOut) return false;
+        const Item& o = a.kind == kOut ? a : b;
+        const Item& x = a.kind == kOut ? b : a;
+        if (x.kind == kWeight) return false;
+        if (!meets(o.r, x.r)) return false;  // an unrelated input shares a cache line with the output
+        const int i = x.owner, j = o.owner;  // linear i reads linear j's output
+        if (i <= j) return false;
+        for (int k = 0; k < L[i].ndeps; ++k)
+            if (L[i].deps[k] == j) return true;
+        return false;
+    };
+    std::vector<size_t> active;  // items whose lines may still meet later ones
+    for (size_t b = 0; b < items.size(); ++b) {
+        size_t keep = 0;
+        for (size_t a : active) {
+            if (items[a].lines.hi <= items[b].lines.lo) continue;  // ends before b starts: done
+            if (!pair_ok(items[a], items[b])) return W4_ERR_INVALID;
+            active[keep++] = a;
         }
+        active.resize(keep);
+        active.push_back(b);
     }
     return W4_OK;
 }
@@ -588,6 +608,7 @@ int w4_pass_create_mode(const w4_pass_linear* linears, int n, int M, int group, 
         }
     }
     std::vector<w4::PassLinear> tab(n);
+    std::map<std::vector<int>, int> first_with;  // a set of producers -> the first linear that has it
     int U = 0, arrivals = 0;
     size_t tiles = 0;
     for (int i = 0; i < n; ++i) {
@@ -616,11 +637,7 @@ int w4_pass_create_mode(const w4_pass_linear* linears, int n, int M, int group, 
         // linears with the same set of producers share a class: once one
         // has seen its producers complete, the others need not wait
         t.dep_class = -1;
-        if (d.ndeps > 0) {
-            const std::vector<int> mine = sorted_deps(d);
-            for (int j = 0; j <= i && t.dep_class < 0; ++j)
-                if (linears[j].ndeps == d.ndeps && sorted_deps(linears[j]) == mine) t.dep_class = j;
-        }
+        if (d.ndeps > 0) t.dep_class = first_with.emplace(sorted_deps(d), i).first->second;
     }
     // Which form (W4_PASS_AUTO).  The persistent kernel pays, at each
     // dependency class, the wait for its producers' last units and a memory

@@ -348,3 +348,31 @@ def test_pass_validation_before_any_hip_call():
         assert w4._c["w4_pass_create_mode"](arr2, 2, 4, 128, mode, ctypes.byref(out)) == w4.W4_ERR_INVALID, mode
     assert w4._c["w4_pass_run"](None, None) == w4.W4_ERR_INVALID
     assert w4._c["w4_pass_destroy"](None) == w4.W4_OK
+
+
+def test_pass_validation_scales_to_large_passes():
+    # a chain of 100 000 linears (each reading its predecessor's bf16 output)
+    # validates in time that grows like n log n, and one unlisted read at the
+    # end of the chain is still found
+    import time
+
+    n, M, N, K = 100_000, 4, 256, 256
+    X0, OUT, W = 0x10_0000_0000, 0x20_0000_0000, 0x40_0000_0000
+    arr = (w4.W4PassLinear * n)()
+    for i in range(n):
+        wb = W + i * 0x10_0000
+        arr[i] = _pl(X0 if i == 0 else OUT + (i - 1) * 4096, 0, yb=OUT + i * 4096, N=N, K=K,
+                     deps=() if i == 0 else (i - 1,), qt=wb, st=wb + 0x8_0000, zt=wb + 0xC_0000)
+    out = ctypes.c_void_p()
+    t0 = time.time()
+    rc = w4._c["w4_pass_create"](arr, n, M, 128, ctypes.byref(out))
+    took = time.time() - t0
+    assert rc in (w4.W4_OK, w4.W4_ERR_HIP), rc
+    if rc == w4.W4_OK:
+        w4._c["w4_pass_destroy"](out)
+    assert took < 10.0, took
+    arr[n - 1] = _pl(OUT + (n - 2) * 4096, 0, yb=OUT + (n - 1) * 4096, N=N, K=K,
+                     qt=W + (n - 1) * 0x10_0000, st=W + (n - 1) * 0x10_0000 + 0x8_0000,
+                     zt=W + (n - 1) * 0x10_0000 + 0xC_0000)
+    assert w4._c["w4_pass_create"](arr, n, M, 128, ctypes.byref(out)) == w4.W4_ERR_INVALID
+
