@@ -93,7 +93,11 @@ int w4_repacked_sizes(int N, int K, int group, size_t* qweight_bytes, size_t* sc
  *     codes of column 64c + 16j + (l % 16), k = 32kb + 8(l / 16) + e,
  *     e = 0..7, code e at nibble e/2 (e even) or 4 + (e-1)/2 (e odd), the
  *     word then rotated left by 3 bits;
- *   scales_t uint16 [NC][G][16][4]: s[G][64c + 16j + t] at (c, G, t, j);
+ *   scales_t uint16 [NC][G][16][4]: s[G][64c + 16j + t] at (c, G, t, j),
+ *     or 0 where every code of that group and column equals its zero
+ *     point (all its weights are 0, so no weight changes; the kernels then
+ *     add exactly 0 for it, where the biased sums would leave a rounding
+ *     residue unless z = 0);
  *   zeros_t  uint16 [NC][G][16]: nibble j of (c, G, t) is z[G][64c + 16j + t].
  * Not in place; outputs must not overlap inputs.  Stateless. */
 int w4_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* zeros, int N, int K, int group,

@@ -73,9 +73,17 @@ __global__ void repack_qweight_kernel(const int32_t* __restrict__ qweight, int N
     }
 }
 
-__global__ void repack_scales_kernel(const uint16_t* __restrict__ scales, const int32_t* __restrict__ zeros, int N,
-                                     int K, uint16_t* __restrict__ s_out, uint16_t* __restrict__ z_out,
-                                     size_t total) {
+// A (group, column) whose every code equals its zero point holds only zero
+// weights, s (q - z) = 0 for any s; its scale is stored as 0.  The kernels
+// form s * (sum x (16 + q) - (16 + z) sum x), and the two sums of such a
+// group cancel exactly only when 16 + z is a power of two (z = 0): with the
+// scale 0 the group adds exactly 0 for every z, so a column of zero weights
+// gives exactly 0 as the contract requires (its bound is 0 there), also for
+// the z = 8 a symmetric quantiser writes.  Codes and zero points are stored
+// unchanged.
+__global__ void repack_scales_kernel(const int32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
+                                     const int32_t* __restrict__ zeros, int N, int K, uint16_t* __restrict__ s_out,
+                                     uint16_t* __restrict__ z_out, size_t total) {
     const int G = K / kGroup;
     // one thread per (c, G, t)
     for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -93,6 +101,10 @@ __global__ void repack_scales_kernel(const uint16_t* __restrict__ scales, const 
             if (n < (size_t)N) {
                 s = scales[(size_t)g * N + n];
                 z = ((uint32_t)zeros[(size_t)g * (N / 8) + n / 8] >> (4 * (n % 8))) & 15u;
+                bool flat = true;  // every code of the group equals z
+                for (int i = 0; i < kGroup / 8; ++i)
+                    flat &= (uint32_t)qweight[((size_t)g * (kGroup / 8) + i) * N + n] == z * 0x11111111u;
+                if (flat) s = 0;
             }
             s_out[idx * 4 + j] = s;
             zw |= z << (4 * j);
@@ -1047,8 +1059,8 @@ hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const i
                           qweight_t, words);
     if (e != hipSuccess) return e;
     const size_t sz = NC * (K / kGroup) * 16;
-    return launch(repack_scales_kernel, dim3(grid_for(sz, 256)), dim3(256), 0, stream, scales, zeros, N, K, scales_t,
-                  zeros_t, sz);
+    return launch(repack_scales_kernel, dim3(grid_for(sz, 256)), dim3(256), 0, stream, qweight, scales, zeros, N, K,
+                  scales_t, zeros_t, sz);
 }
 
 hipError_t launch_unpack(const uint32_t* qweight_t, const uint16_t* zeros_t, int N, int K, uint8_t* q_out,

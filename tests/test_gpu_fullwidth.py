@@ -148,6 +148,71 @@ def test_all_zero_columns_are_exact_zeros():
             _check(y, Y[:M], A[:M], ("zero columns", M, splits))
 
 
+def test_zero_columns_with_nonzero_zero_points_are_exact_zeros():
+    # a symmetric quantiser stores zero weights as q = z = 8: columns (and
+    # single groups) of such weights must still give exactly 0 (the contract
+    # leaves no room where sum_k |x w| = 0), and the other columns the
+    # contract; zero points 1..15 for the all-zero groups of one column
+    N, K, g = 256, 4096, 128
+    G = K // g
+    rng = np.random.default_rng(97531)
+    q = rng.integers(0, 16, size=(K, N))
+    z = rng.integers(0, 16, size=(G, N))
+    s = (np.float16(2.0 ** -7) * (0.5 + rng.random((G, N)))).astype(np.float16).view(np.uint16)
+    zero_cols = [1, 70, 129, 250]
+    z[:, zero_cols] = 8
+    q[:, zero_cols] = 8
+    z[:, 17] = (np.arange(G) % 15) + 1                 # zero point 1..15 per group
+    q[:, 17] = np.repeat(z[:, 17], g)
+    zero_cols.append(17)
+    for gi in (0, 5, G - 1):                           # single all-zero groups in live columns
+        q[gi * g:(gi + 1) * g, 40] = z[gi, 40]
+    lin = synth.pack_linear(q, z, s)
+    pk = packed(lin, N, K)
+    x = synth.gen_x(64, K, seed_base=8642)
+    x3 = synth.f32_to_bf16_bits(bf16_bits_to_f64(x).astype(np.float32) + 3.0)  # mean 3: large sum(x)
+    for label, xx in (("N(0,1)", x), ("N(3,1)", x3)):
+        Y, A = linear64(xx, lin["qweight"], lin["scales"], lin["zeros"])
+        assert np.all(A[:, zero_cols] == 0)
+        for M in FULL_M:
+            for splits in (0, 1, 3):
+                y = run_linear(xx[:M], pk, 0, splits)
+                assert np.all(y[:, zero_cols] == 0.0), (label, M, splits, np.abs(y[:, zero_cols]).max())
+                _check(y, Y[:M], A[:M], ("symmetric zeros", label, M, splits), fro_max=None)
+
+
+def test_zero_negative_and_extreme_group_scales():
+    # scales the quantiser never writes but a checkpoint may hold: +0 and -0
+    # in single groups and over whole columns (those columns must give exactly
+    # 0), negative scales, fp16 subnormals next to 65504 in the same column
+    # (consecutive group scales 2**-24 and 65504 apart), on every kernel
+    N, K, g = 256, 2048, 128
+    G = K // g
+    rng = np.random.default_rng(2468)
+    q = rng.integers(0, 16, size=(K, N))
+    z = rng.integers(0, 16, size=(G, N))
+    s = (np.float16(2.0 ** -7) * (0.5 + rng.random((G, N)))).astype(np.float16).view(np.uint16)
+    pick = rng.random((G, N))
+    s[pick < 0.10] = 0x0000                           # +0
+    s[(pick >= 0.10) & (pick < 0.15)] = 0x8000        # -0
+    s[(pick >= 0.15) & (pick < 0.25)] |= 0x8000       # negative
+    s[(pick >= 0.25) & (pick < 0.28)] = 0x0001        # smallest subnormal
+    s[(pick >= 0.28) & (pick < 0.30)] = 0x7BFF        # largest finite
+    zero_cols = [3, 64, 130, 255]
+    s[:, zero_cols] = 0x0000
+    s[::2, 200] = 0x8000                              # a column of alternating -0 and scale
+    lin = synth.pack_linear(q, z, s)
+    pk = packed(lin, N, K)
+    x = synth.gen_x(64, K, seed_base=4321)
+    Y, A = linear64(x, lin["qweight"], lin["scales"], lin["zeros"])
+    assert np.all(A[:, zero_cols] == 0)
+    for M in FULL_M:
+        for splits in (0, 1, 3):
+            y = run_linear(x[:M], pk, 0, splits)
+            assert np.all(y[:, zero_cols] == 0.0), (M, splits)
+            _check(y, Y[:M], A[:M], ("scales", M, splits), fro_max=None)
+
+
 GUARD = 256  # bytes of guard on each side of y (keeps y 16-byte aligned)
 PATTERN = 0xA5
 

@@ -54,10 +54,20 @@ def _layout_words(qweight, N, K):
 def test_repack_matches_documented_layout():
     N, K = 200, 256
     lin = synth.gen_linear(31, N, K)
+    # groups whose codes all equal their zero point (all weights 0), with
+    # zero points 0, 8 and 15, and one group one code short of that
+    q, z = unpack_qweight(lin["qweight"]), unpack_zeros(lin["zeros"])
+    z[0, 3], z[1, 77], z[0, 199], z[1, 5] = 0, 8, 15, 8
+    for g, n in ((0, 3), (1, 77), (0, 199), (1, 5)):
+        q[128 * g:128 * (g + 1), n] = z[g, n]
+    q[128 + 60, 5] = 7
+    lin = synth.pack_linear(q, z, lin["scales"])
+    flat = {(0, 3), (1, 77), (0, 199)}
     pk = packed(lin, N, K)
     got = pk.qweight_t.cpu().numpy().view(np.uint32)
     assert np.array_equal(got, _layout_words(lin["qweight"], N, K))
-    # scales: (c, G, t, j) -> s[G][64c + 16j + t]; zeros nibble j of (c, G, t)
+    # scales: (c, G, t, j) -> s[G][64c + 16j + t], 0 for a flat group;
+    # zeros nibble j of (c, G, t)
     NC, G = -(-N // 64), K // 128
     st = pk.scales_t.cpu().numpy().view(np.uint16).reshape(NC, G, 16, 4)
     zt = pk.zeros_t.cpu().numpy().view(np.uint16).reshape(NC, G, 16)
@@ -67,7 +77,7 @@ def test_repack_matches_documented_layout():
             for t in range(16):
                 for j in range(4):
                     n = 64 * c + 16 * j + t
-                    sv = lin["scales"][g, n] if n < N else 0
+                    sv = lin["scales"][g, n] if n < N and (g, n) not in flat else 0
                     zv = z[g, n] if n < N else 0
                     assert st[c, g, t, j] == sv
                     assert (int(zt[c, g, t]) >> (4 * j)) & 15 == zv
