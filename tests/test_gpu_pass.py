@@ -379,3 +379,51 @@ def test_every_m_in_the_persistent_kernel():
         Y2, A2 = linear64_gemm(hb, lin2["qweight"], lin2["scales"], lin2["zeros"], 128, 0, N2)
         assert np.all(np.abs(y2.cpu().numpy().astype(np.float64) - Y2) <= 4e-3 * A2), (M, "consumer")
 
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 16])
+def test_zero_weight_columns_through_the_persistent_kernel(M):
+    # columns of zero weights written with non-zero zero points (q = z = 8, and
+    # one column with z = 1..15 per group) give exactly 0 through the pass
+    # kernel's own epilogue, fp32 and bf16; a consumer reading that bf16
+    # output matches the oracle on what it read
+    N, K, g, N2 = 256, 4096, 128, 128
+    G = K // g
+    rng = np.random.default_rng(1357)
+    q = rng.integers(0, 16, size=(K, N))
+    z = rng.integers(0, 16, size=(G, N))
+    s = (np.float16(2.0 ** -7) * (0.5 + rng.random((G, N)))).astype(np.float16).view(np.uint16)
+    zero_cols = [2, 66, 131, 255]
+    z[:, zero_cols] = 8
+    q[:, zero_cols] = 8
+    z[:, 40] = (np.arange(G) % 15) + 1
+    q[:, 40] = np.repeat(z[:, 40], g)
+    zero_cols.append(40)
+    lin = synth.pack_linear(q, z, s)
+    lin2 = synth.gen_linear(4242, N2, N)
+    pk = w4.repack(to_dev(lin["qweight"]), to_dev(lin["scales"]), to_dev(lin["zeros"]), N, K)
+    pk2 = w4.repack(to_dev(lin2["qweight"]), to_dev(lin2["scales"]), to_dev(lin2["zeros"]), N2, N)
+    x = synth.gen_x(M, K, seed_base=2468)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    yb = torch.full((M, N), 0x7FC0, dtype=torch.int16, device=DEV)
+    y2 = torch.full((M, N2), float("nan"), dtype=torch.float32, device=DEV)
+    descs = [dict(x=to_dev(x), qweight_t=pk.qweight_t, scales_t=pk.scales_t, zeros_t=pk.zeros_t, y=y, y_bf16=yb,
+                  N=N, K=K, ldx=0, alpha=1.0, deps=[]),
+             dict(x=yb, qweight_t=pk2.qweight_t, scales_t=pk2.scales_t, zeros_t=pk2.zeros_t, y=y2, y_bf16=None,
+                  N=N2, K=N, ldx=0, alpha=1.0, deps=[0])]
+    h = w4.w4_pass_create_mode(descs, M, PERSISTENT)
+    try:
+        assert w4.w4_pass_info(h)["persistent"] == 1
+        w4.w4_pass_run(h)
+        w4.w4_pass_check(h)
+    finally:
+        w4.w4_pass_destroy(h)
+    torch.cuda.synchronize()
+    y_h = y.cpu().numpy().astype(np.float64)
+    yb_h = yb.cpu().numpy().view(np.uint16)
+    assert np.all(y_h[:, zero_cols] == 0.0) and np.all((yb_h[:, zero_cols] & 0x7FFF) == 0), M
+    Y, A = linear64_gemm(x, lin["qweight"], lin["scales"], lin["zeros"], 128, 0, N)
+    assert np.all(A[:, zero_cols] == 0)
+    assert np.all(np.abs(y_h - Y) <= 4e-3 * A), M
+    Y2, A2 = linear64_gemm(yb_h.copy(), lin2["qweight"], lin2["scales"], lin2["zeros"], 128, 0, N2)
+    assert np.all(np.abs(y2.cpu().numpy().astype(np.float64) - Y2) <= 4e-3 * A2), M
