@@ -165,6 +165,57 @@ def test_plans_fit_the_hardware(M, N, K):
     assert p["splits"] == 1 or p["splits"] * M * (-(-N // 64) * 64) * 4 <= 64 << 20
 
 
+def test_random_plans_keep_their_invariants():
+    # A seeded sweep over shapes and forced decompositions the model never
+    # uses (tiny and ragged N, odd group counts, splits past the group count,
+    # every waves-per-chunk choice): every plan fits the hardware, splits K
+    # into non-empty runs of whole groups, gives every wave of a K-splitting
+    # workgroup a group of its own, covers every chunk, and keeps its partial
+    # sums inside the 64 MiB split-K workspace.
+    import numpy as np
+
+    rng = np.random.default_rng(2024)
+    checked = 0
+    for _ in range(4000):
+        M = 1 if rng.random() < 0.2 else int(rng.integers(2, 65))  # the GEMV path too
+        N = 8 * int(rng.integers(1, 4000 if rng.random() < 0.8 else 20000))
+        G = int(rng.integers(1, 300))
+        K = 128 * G
+        splits = 0 if rng.random() < 0.5 else int(rng.integers(1, G + 8))
+        kwaves = int(rng.choice([1, 2, 4, 8])) if M <= 16 and rng.random() < 0.3 else 0
+        kernel = w4.W4_KERNEL_MFMA if M == 1 and rng.random() < 0.3 else w4.W4_KERNEL_AUTO
+        p = w4.w4a16_plan(M, N, K, kernel=kernel, splits=splits, kwaves=kwaves)
+        what = (M, N, K, splits, kwaves, kernel, p)
+        chunks, mb = -(-N // 64), -(-M // 16)
+        assert p["kernel"] == (w4.W4_KERNEL_GEMV if M == 1 and kernel == w4.W4_KERNEL_AUTO else w4.W4_KERNEL_MFMA), what
+        S = p["splits"]
+        assert 1 <= S <= G, what
+        if splits:
+            assert S <= splits, what
+        gps = -(-G // S)
+        assert -(-G // gps) == S, what  # no split is empty
+        assert 0 <= p["lds"] <= 160 * 1024 - 256, what
+        lds_kernel = p["lds"] > 0
+        assert not lds_kernel or (M > 16 or (M >= 15 and N >= 4096 and kwaves == 0)), what
+        kw = p["kwaves"]
+        if kwaves:
+            assert kw == kwaves or (kw < kwaves and G - (S - 1) * gps < kwaves), what
+        if kw > 1:
+            assert not lds_kernel and p["block"] == 64 * kw and p["grid"] == chunks * S, what
+            assert G - (S - 1) * gps >= kw, what  # every wave of the workgroup has a group
+        else:
+            wv = p["block"] // 64
+            assert wv == 4 or (lds_kernel and wv == 8), what
+            tiles = -(-chunks // wv) * S
+            assert p["grid"] % tiles == 0, what
+            rs = p["grid"] // tiles
+            assert rs == 1 or (lds_kernel and 1 < rs <= min(4, mb)), what
+        assert 1 <= p["grid"] and p["grid"] * p["block"] < 2 ** 31, what
+        assert S == 1 or S * M * chunks * 64 * 4 <= 64 << 20, what
+        checked += 1
+    assert checked == 4000
+
+
 def test_forced_plans():
     p = w4.w4a16_plan(1, 8192, 8192, kernel=w4.W4_KERNEL_MFMA, splits=3)
     assert p["kernel"] == w4.W4_KERNEL_MFMA and p["splits"] == 3
