@@ -103,3 +103,16 @@ def test_curve_tables_ratios_and_layer_sums(tmp_path):
     assert rows["one layer, 7 launches"].split("|")[3].strip() == "%.2f" % ((90 * 1.2 + 6) / 90)
     assert "one layer, fused (4 launches)" not in text  # no fused shapes in this run
     assert "| q | 0.020 | 0.020 |" in text  # spread (max - min) / median
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    # the bench measures one GPU's throughput; --gpus N > 1 exits before any
+    # device work, saying so
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300, cwd=root)
+    assert r.returncode == 2, (r.returncode, r.stderr[-500:])
+    assert "one GPU" in r.stderr and r.stdout == ""
