@@ -98,6 +98,9 @@ def parse():
                         "each), an empty launch, and their sum over a pass")
     p.add_argument("--tree", action="store_true",
                    help="instead of the sweep: only the tree-draft verify attention measurement (one JSON line)")
+    p.add_argument("--tree-merge-sweep", action="store_true",
+                   help="instead of the sweep: tree attention with each merge of the key splits forced, over "
+                        "prefix lengths and draft sizes (one JSON line per case)")
     p.add_argument("--m", default="1,2,4,5,8,16,32,48,64", help="M grid for --shapes")
     p.add_argument("--names", default="q,k,v,o,gate,up,down,lm_head", help="linears for --shapes")
     p.add_argument("--splits", type=int, default=0, help="force the K split count in --shapes (0 = planner)")
@@ -666,7 +669,8 @@ def tree_attention_bench(torch, w4, args):
     """Tree-draft verify attention of one layer (64 query heads over 8
     key/value heads, head dim 128) over a 4096-position KV prefix, for the
     pass M = 1, a 5-token chain (sequence draft) and a 64-token random tree
-    (tree draft): microseconds per call (graph-replayed, 20 calls per replay),
+    (tree draft): microseconds per call (graph-replayed, 20 calls per replay;
+    with the default merge of the key splits, and with each merge forced),
     the KV bytes it must read, the flops it must do (q.k and p.v over every
     visible key), and the rates against the 8 TB/s and 2.5 PFLOP/s rooflines.
     Synthetic bf16 inputs N(0, 1); outputs checked against the oracle."""
@@ -695,25 +699,32 @@ def tree_attention_bench(torch, w4, args):
         qd, kdd, vdd = td(qb), td(kdb), td(vdb)
         md = torch.from_numpy(masks.view(np.int64)).to(dev)
         o = torch.empty((M, Hq, D), dtype=torch.float32, device=dev)
-        w4.tree_attention(qd, kcd, vcd, kdd, vdd, md, out=o)
-        torch.cuda.synchronize()
         args_o = (q, kc, vc, kd, vd, masks)
         ref, mass = tree_attention(*args_o), attention_weight_mass(*args_o)
-        worst = float(np.max(np.abs(o.cpu().numpy() - ref) / (1e-2 * mass + 1e-6)))
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
-            for _ in range(20):
-                w4.tree_attention(qd, kcd, vcd, kdd, vdd, md, out=o)
-        g.replay()
-        torch.cuda.synchronize()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(3, args.steps)
-        s0.record()
-        for _ in range(reps):
+
+        def timed(merge):
+            w4.tree_attention(qd, kcd, vcd, kdd, vdd, md, out=o, merge=merge)
+            torch.cuda.synchronize()
+            worst = float(np.max(np.abs(o.cpu().numpy() - ref) / (1e-2 * mass + 1e-6)))
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                for _ in range(20):
+                    w4.tree_attention(qd, kcd, vcd, kdd, vdd, md, out=o, merge=merge)
             g.replay()
-        s1.record()
-        torch.cuda.synchronize()
-        us = s0.elapsed_time(s1) * 1e3 / (reps * 20)
+            torch.cuda.synchronize()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(3, args.steps)
+            s0.record()
+            for _ in range(reps):
+                g.replay()
+            s1.record()
+            torch.cuda.synchronize()
+            del g
+            return s0.elapsed_time(s1) * 1e3 / (reps * 20), worst
+
+        by_merge = {name_m: timed(m) for name_m, m in (("launch", w4.TREE_MERGE_LAUNCH), ("last", w4.TREE_MERGE_LAST))}
+        us, worst = timed(w4.TREE_MERGE_AUTO)
+        splits, used = w4.w4_tree_attention_plan(M, L, Hq, Hkv)
         visible = sum(bin(int(m)).count("1") for m in masks)
         nbytes = 2 * L * Hkv * D * 2 + 2 * M * Hkv * D * 2 + M * Hq * D * 2 + M * Hq * D * 4
         flops = 4.0 * Hq * D * (M * L + visible)
@@ -721,9 +732,57 @@ def tree_attention_bench(torch, w4, args):
                      "TBps": round(nbytes / (us * 1e-6) / 1e12, 3), "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
                      "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "frac_mfma": round(flops / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
-                     "worst_err_over_bound": round(worst, 5)}
-        del g
+                     "worst_err_over_bound": round(max([worst] + [w for _, w in by_merge.values()]), 5),
+                     "splits": splits, "merge": {0: "none", 1: "launch", 2: "last"}[used],
+                     "us_by_merge": {k: round(t, 2) for k, (t, _) in by_merge.items()}}
     return out
+
+
+def tree_merge_sweep(torch, w4):
+    """Microseconds per tree attention call (64 query heads over 8 key/value
+    heads; chain drafts; N(0, 1) bf16 inputs; graph-replayed, 20 calls per
+    replay, best of 3 x 10 replays) with the key splits merged by a second
+    launch and by the last workgroup of each tile, for M = 1..64 over
+    prefixes of 128..8192 positions; the merge the default takes; and the
+    largest difference between the two outputs."""
+    dev = "cuda:0"
+    Hq, Hkv, D = 64, 8, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    bf = lambda *shape: torch.randn(*shape, device=dev, generator=gen).to(torch.bfloat16)
+    for L in (128, 256, 512, 1024, 2048, 4096, 8192):
+        kc, vc = bf(L, Hkv, D), bf(L, Hkv, D)
+        for M in (1, 2, 5, 8, 16, 64):
+            q, kd, vd = bf(M, Hq, D), bf(M, Hkv, D), bf(M, Hkv, D)
+            masks = torch.tensor([((1 << (i + 1)) - 1) - (1 << 64 if i == 63 else 0) for i in range(M)],
+                                 dtype=torch.int64, device=dev)
+            o = torch.empty(M, Hq, D, device=dev)
+            splits, used = w4.w4_tree_attention_plan(M, L, Hq, Hkv)
+            row = {"M": M, "L": L, "splits": splits, "default": {0: "none", 1: "launch", 2: "last"}[used]}
+            outs = {}
+            for name, merge in (("launch", w4.TREE_MERGE_LAUNCH), ("last", w4.TREE_MERGE_LAST)):
+                w4.tree_attention(q, kc, vc, kd, vd, masks, out=o, merge=merge)
+                torch.cuda.synchronize()
+                outs[name] = o.clone()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+                    for _ in range(20):
+                        w4.tree_attention(q, kc, vc, kd, vd, masks, out=o, merge=merge)
+                g.replay()
+                torch.cuda.synchronize()
+                best = float("inf")
+                for _ in range(3):
+                    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    s0.record()
+                    for _ in range(10):
+                        g.replay()
+                    s1.record()
+                    torch.cuda.synchronize()
+                    best = min(best, s0.elapsed_time(s1) * 1e3 / 200)
+                row[name + "_us"] = round(best, 2)
+                del g
+            row["max_abs_diff"] = float((outs["launch"] - outs["last"]).abs().max())
+            print(json.dumps(row), flush=True)
 
 
 def oracle_round_bf16(y):
@@ -1065,6 +1124,10 @@ def main():
     if args.tree:
         w4.w4_init()
         print(json.dumps(tree_attention_bench(torch, w4, args)))
+        return
+    if args.tree_merge_sweep:
+        w4.w4_init()
+        tree_merge_sweep(torch, w4)
         return
     t_start = time.time()
     w4.w4_init()

@@ -93,6 +93,10 @@ _c = {
     "w4_accept_sample": _sig("w4_accept_sample", [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "w4_tree_attention": _sig("w4_tree_attention",
                               [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _vp, _vp]),
+    "w4_tree_attention_ex": _sig("w4_tree_attention_ex",
+                                 [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, _i, _vp, _vp]),
+    "w4_tree_attention_plan": _sig("w4_tree_attention_plan",
+                                   [_i, _i, _i, _i, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]),
 }
 
 
@@ -352,10 +356,33 @@ def w4_tree_attention(q, k_cache, v_cache, k_draft, v_draft, masks, M, L, num_he
            "w4_tree_attention")
 
 
-def tree_attention(q, k_cache, v_cache, k_draft, v_draft, masks, scale=0.0, out=None, stream=None):
+def w4_tree_attention_ex(q, k_cache, v_cache, k_draft, v_draft, masks, M, L, num_heads, num_kv_heads, head_dim,
+                         scale, merge, out, stream=None):
+    st = _stream(stream, q, out)
+    _check(_c["w4_tree_attention_ex"](_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft), _ptr(v_draft),
+                                      _ptr(masks), M, L, num_heads, num_kv_heads, head_dim, scale, merge, _ptr(out),
+                                      st),
+           "w4_tree_attention_ex")
+
+
+TREE_MERGE_AUTO, TREE_MERGE_LAUNCH, TREE_MERGE_LAST = 0, 1, 2
+
+
+def w4_tree_attention_plan(M, L, num_heads, num_kv_heads, merge=TREE_MERGE_AUTO):
+    """(key splits, merge used) of a tree attention call of that shape."""
+    splits, used = ctypes.c_int(0), ctypes.c_int(0)
+    _check(_c["w4_tree_attention_plan"](M, L, num_heads, num_kv_heads, merge, ctypes.byref(splits),
+                                        ctypes.byref(used)),
+           "w4_tree_attention_plan")
+    return splits.value, used.value
+
+
+def tree_attention(q, k_cache, v_cache, k_draft, v_draft, masks, scale=0.0, out=None, stream=None,
+                   merge=TREE_MERGE_AUTO):
     """Tree-draft verify attention on device tensors: q [M, Hq, 128], caches
     [L, Hkv, 128] and draft keys/values [M, Hkv, 128] as bf16 (or int16 bf16
-    bits), masks [M] int64 (uint64 bit patterns).  Returns fp32 [M, Hq, 128]."""
+    bits), masks [M] int64 (uint64 bit patterns).  Returns fp32 [M, Hq, 128].
+    merge: how the key splits are merged (TREE_MERGE_AUTO, _LAUNCH, _LAST)."""
     import torch
 
     if q.dim() != 3 or k_cache.dim() != 3 or k_draft.dim() != 3:
@@ -377,8 +404,8 @@ def tree_attention(q, k_cache, v_cache, k_draft, v_draft, masks, scale=0.0, out=
     _on_device(dev, q=q, k_cache=k_cache, v_cache=v_cache, k_draft=k_draft, v_draft=v_draft, masks=masks)
     if out is None:
         out = torch.empty((M, Hq, D), dtype=torch.float32, device=dev)
-    w4_tree_attention(q, k_cache if L else None, v_cache if L else None, k_draft, v_draft, masks, M, L, Hq, Hkv, D,
-                      scale, out, stream)
+    w4_tree_attention_ex(q, k_cache if L else None, v_cache if L else None, k_draft, v_draft, masks, M, L, Hq, Hkv,
+                         D, scale, merge, out, stream)
     return out
 
 

@@ -40,8 +40,15 @@
 // The softmax runs in base 2: scores are scaled by scale * log2(e) and
 // exponentiated with the hardware exp2.  With one key split a workgroup
 // writes its normalised rows; otherwise each writes its unnormalised output
-// with the running max and sum of every row, and tree_attn_combine_kernel
-// merges the splits (log-sum-exp), one workgroup per row.
+// with the running max and sum of every row, and the splits are merged
+// (log-sum-exp) either by tree_attn_combine_kernel, a second launch, or by
+// the last workgroup of each tile to finish (merge_tile): the partial results
+// then go out as device-coherent stores, every thread's stores retire, one
+// thread counts the workgroup in on the tile's arrival counter, and the
+// workgroup that brings the count to the number of splits reads the others'
+// results back with device-coherent loads, merges them and sets the counter
+// to zero again for the next call (so no clearing launch, and a captured
+// call replays).  Nothing ever waits for another workgroup.
 #include "w4_aux.h"
 
 #include <algorithm>
@@ -75,8 +82,10 @@ struct TreeArgs {
     float* mpart;        // [S][Hkv][R]
     float* lpart;        // [S][Hkv][R]
     float* out;          // [M][Hq][128]
+    uint32_t* arrive;    // [nrt][Hkv] arrival counters (fused merge)
     int M, L, Hq, Hkv, G, R, T, nrt;
-    int nchunks, nsplit, cng;  // cng: thread groups per row in the merge
+    int nchunks, nsplit, cng;  // cng: thread groups per row in the merge launch
+    int fused;                 // the last workgroup of a tile merges its splits
     float c;  // scale * log2(e)
 };
 
@@ -90,6 +99,97 @@ __device__ __forceinline__ u32x4 kv_load(const uint16_t* cache, const uint16_t* 
 }
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Device-coherent (agent scope) stores and loads of the fused merge: they
+// reach or read the level that every XCD shares, past the XCD's own L2.
+typedef __attribute__((address_space(1))) uint32_t gu32;
+typedef __attribute__((address_space(1))) uint64_t gu64;
+__device__ __forceinline__ void store_agent(float* p, float v) {
+    __hip_atomic_store((gu32*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(float* p, f32x4 v) {  // as two 8-byte halves
+    __hip_atomic_store((gu64*)p, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((gu64*)(p + 2), (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// (a uniform base and a 32-bit byte offset: the workspace is below 4 GB)
+__device__ __forceinline__ float load_agent(const float* base, uint32_t off) {
+    return __uint_as_float(__hip_atomic_load((const gu32*)((const char*)base + off), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+// two float pairs, 256 bytes apart
+__device__ __forceinline__ f32x4 load_agent2x2(const float* base, uint32_t off) {
+    const char* p = (const char*)base + off;
+    const uint64_t lo = __hip_atomic_load((const gu64*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load((const gu64*)(p + 256), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)), __uint_as_float((uint32_t)hi),
+                 __uint_as_float((uint32_t)(hi >> 32))};
+}
+
+// The fused merge of rows [r0, r0 + 16W) of key/value head g (the tile's
+// real rows): out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s over the
+// splits s.  Thread (rg, c) = (tid / 32, tid % 32) takes head-dim values 2c,
+// 2c + 1, 64 + 2c and 65 + 2c of rows r0 + rg + 2W p (so each 8-byte load of
+// the 32 threads of a row reads 256 contiguous bytes); its (row, split)
+// items run row-major, kB of them in flight at once, merged online (running
+// max, rescaled sums); a row is written when its last split is in.
+template <int W>
+__device__ void merge_tile(const TreeArgs& a, int g, int r0, int tid) {
+    constexpr int kB = 24;
+    const int rg = tid >> 5, c = tid & 31;
+    const int nr = min(16 * W, a.R - r0);
+    const int S = a.nsplit;
+    const int npair = rg < nr ? (nr - rg + 2 * W - 1) / (2 * W) : 0;
+    const int n = npair * S;
+    const uint32_t plane = (uint32_t)a.Hkv * a.R;
+    const uint32_t row0 = (uint32_t)g * a.R + r0 + rg;  // (head, row) index of pair 0
+    int p = 0, s = 0;  // the next item merged
+    float mx = -INFINITY, den = 0.0f;
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < n; k0 += kB) {
+        float mv[kB], lv[kB];
+        f32x4 ov[kB];
+        int pp = p, ss = s;
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            if (k0 + b < n) {
+                const uint32_t idx = ss * plane + row0 + 2 * W * pp;
+                mv[b] = load_agent(a.mpart, 4 * idx);
+                lv[b] = load_agent(a.lpart, 4 * idx);
+                ov[b] = load_agent2x2(a.opart, 4 * (idx * kHd + 2 * c));
+            }
+            if (++ss == S) {
+                ss = 0;
+                ++pp;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            if (k0 + b >= n) continue;
+            const float nm = fmaxf(mx, mv[b]);
+            if (nm != -INFINITY) {
+                const float f = exp2_hw(mx - nm), w = exp2_hw(mv[b] - nm);
+                acc = acc * f + ov[b] * w;
+                den = den * f + lv[b] * w;
+                mx = nm;
+            }
+            if (++s == S) {
+                const int r = r0 + rg + 2 * W * p;
+                const int tok = r / a.G, head = g * a.G + r % a.G;
+                const f32x4 v = den > 0.0f ? acc * (1.0f / den) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                float* const op = a.out + ((size_t)tok * a.Hq + head) * kHd + 2 * c;
+                *(float2*)op = make_float2(v[0], v[1]);
+                *(float2*)(op + 64) = make_float2(v[2], v[3]);
+                s = 0;
+                ++p;
+                mx = -INFINITY;
+                den = 0.0f;
+                acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+    }
+}
 
 template <int W>
 __global__ __launch_bounds__(64 * W) void tree_attn_kernel(TreeArgs a) {
@@ -300,16 +400,40 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(TreeArgs a) {
         return;
     }
     const size_t plane = (size_t)a.Hkv * a.R;
-    if (row_ok) {
-        const size_t base = (size_t)split * plane + (size_t)g * a.R + row;
-        float* op = a.opart + base * kHd + 4 * o;
+    const size_t base = (size_t)split * plane + (size_t)g * a.R + row;
+    float* op = a.opart + base * kHd + 4 * o;
+    if (!a.fused) {
+        if (row_ok) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *(f32x4*)(op + 16 * dt) = oacc[dt];
+            for (int dt = 0; dt < 8; ++dt) *(f32x4*)(op + 16 * dt) = oacc[dt];
+            if (o == 0) {
+                a.mpart[base] = m_run;
+                a.lpart[base] = l_run;
+            }
+        }
+        return;
+    }
+    if (row_ok) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) store_agent(op + 16 * dt, oacc[dt]);
         if (o == 0) {
-            a.mpart[base] = m_run;
-            a.lpart[base] = l_run;
+            store_agent(a.mpart + base, m_run);
+            store_agent(a.lpart + base, l_run);
         }
     }
+    // every thread's partial results retire before the workgroup counts in
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __shared__ uint32_t last;
+    uint32_t* const cnt = a.arrive + (size_t)rt * a.Hkv + g;
+    if (tid == 0)
+        last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)a.nsplit - 1;
+    __syncthreads();
+    if (!last) return;
+    asm volatile("" ::: "memory");
+    // every split of the tile has counted in: merge, and clear the counter
+    if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_tile<W>(a, g, rt * kRowsWg, tid);
 }
 
 // out[tok][head][:] = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s over the
@@ -395,9 +519,11 @@ size_t partial_bytes(int nsplit, int Hkv, int R) { return (size_t)nsplit * Hkv *
 // wave, else 8 (128 rows).
 int tree_waves(int R) { return R > 16 ? 8 : 4; }
 
+constexpr size_t kFusedMergeBytes = 72 << 10;  // default limit of a tile's partials for the in-kernel merge
+
 }  // namespace
 
-int tree_attn_plan(int M, int L, int Hq, int Hkv, int* nsplit_out, size_t* ws_bytes) {
+int tree_attn_plan(int M, int L, int Hq, int Hkv, int merge, int* nsplit_out, int* merge_used, size_t* ws_bytes) {
     const int G = Hq / Hkv, R = M * G, T = L + M;
     const int nchunks = (T + kChunk - 1) / kChunk;
     const int W = tree_waves(R), rows_wg = 16 * W;
@@ -411,15 +537,33 @@ int tree_attn_plan(int M, int L, int Hq, int Hkv, int* nsplit_out, size_t* ws_by
     const long long slots = W == 4 ? 512 : 256;
     const int cps = std::max(2, (int)(((long long)nchunks * tiles + slots - 1) / slots));
     int nsplit = std::max(1, std::min(kTreeMaxSplits, (nchunks + cps - 1) / cps));
-    while (nsplit > 1 && partial_bytes(nsplit, Hkv, R) > kTreeWorkspaceBytes) --nsplit;
+    while (nsplit > 1 && kTreeCounterBytes + partial_bytes(nsplit, Hkv, R) > kTreeWorkspaceBytes) --nsplit;
+    if ((size_t)tiles * sizeof(uint32_t) > kTreeCounterBytes) return -1;
+    // The merge in the last workgroup of a tile costs a chain of
+    // device-coherent round trips (every split's stores acknowledged, the
+    // count, the loads of the partials: about 4 us with almost nothing to
+    // merge) and then pulls every split's partial rows of the tile through
+    // one CU, at 20-30 GB/s; a second launch costs 4.5-7 us but spreads the
+    // merge over the chip.  By default the last workgroup merges only
+    // four-wave tiles (at most 16 rows) whose partials come to 72 KiB at
+    // most (measured with 64 query heads over 8: M = 1 and L up to 2048, M = 2
+    // and L up to 512: 0.2-1.4 us per call faster, slower everywhere else).
+    int used = kTreeMergeAuto;
+    if (nsplit > 1) {
+        const size_t tile_bytes = (size_t)nsplit * std::min(R, rows_wg) * (kHd + 2) * sizeof(float);
+        used = merge == kTreeMergeLaunch || merge == kTreeMergeLast ? merge
+               : W == 4 && tile_bytes <= kFusedMergeBytes       ? kTreeMergeLast
+                                                                 : kTreeMergeLaunch;
+    }
     if (nsplit_out) *nsplit_out = nsplit;
-    if (ws_bytes) *ws_bytes = nsplit > 1 ? partial_bytes(nsplit, Hkv, R) : 0;
+    if (merge_used) *merge_used = used;
+    if (ws_bytes) *ws_bytes = nsplit > 1 ? kTreeCounterBytes + partial_bytes(nsplit, Hkv, R) : 0;
     return 0;
 }
 
 hipError_t launch_tree_attn(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const uint16_t* kd,
                             const uint16_t* vd, const uint64_t* masks, int M, int L, int Hq, int Hkv, float scale,
-                            float* out, void* ws, hipStream_t stream) {
+                            int merge, float* out, void* ws, hipStream_t stream) {
     TreeArgs a;
     a.q = q;
     a.kc = kc;
@@ -437,16 +581,19 @@ hipError_t launch_tree_attn(const uint16_t* q, const uint16_t* kc, const uint16_
     const int W = tree_waves(a.R);
     a.nrt = (a.R + 16 * W - 1) / (16 * W);
     a.nchunks = (a.T + kChunk - 1) / kChunk;
-    if (tree_attn_plan(M, L, Hq, Hkv, &a.nsplit, nullptr) != 0) return hipErrorInvalidValue;
+    int used = 0;
+    if (tree_attn_plan(M, L, Hq, Hkv, merge, &a.nsplit, &used, nullptr) != 0) return hipErrorInvalidValue;
+    a.fused = used == kTreeMergeLast;
     a.c = scale * kLog2e;
     const size_t plane = (size_t)a.nsplit * Hkv * a.R;
-    a.opart = (float*)ws;
+    a.arrive = (uint32_t*)ws;
+    a.opart = (float*)((char*)ws + kTreeCounterBytes);
     a.mpart = a.opart + plane * kHd;
     a.lpart = a.mpart + plane;
     a.out = out;
     hipError_t e = W == 4 ? launch(tree_attn_kernel<4>, dim3(a.nsplit, a.nrt, Hkv), dim3(256), stream, a)
                           : launch(tree_attn_kernel<8>, dim3(a.nsplit, a.nrt, Hkv), dim3(512), stream, a);
-    if (e != hipSuccess || a.nsplit == 1) return e;
+    if (e != hipSuccess || a.nsplit == 1 || a.fused) return e;
     a.cng = 1;
     while (a.cng < 8 && a.cng * 8 < a.nsplit) a.cng *= 2;
     const int rows_wg = 8 / a.cng;

@@ -72,9 +72,17 @@ int device_state(w4::Workspace* out, void** accept = nullptr, float** tree = nul
             what = "hipMalloc(tree attention workspace)";
             e = hipMalloc(&tree, w4::kTreeWorkspaceBytes);
         }
+        if (e == hipSuccess) {
+            // the tree attention's arrival counters start at zero; each call
+            // leaves them at zero
+            what = "hipMemset(tree attention counters)";
+            e = hipMemset(tree, 0, w4::kTreeCounterBytes);
+            if (e == hipSuccess) e = hipDeviceSynchronize();
+        }
         if (e != hipSuccess) {
             if (part) (void)hipFree(part);
             if (acc) (void)hipFree(acc);
+            if (tree) (void)hipFree(tree);
             return hip_fail(what, e);
         }
         st.ws.partial = (float*)part;
@@ -388,11 +396,37 @@ int w4_accept_sample(const float* logits, const float* draft_logits, const int32
 
 }
 
+static_assert(W4_TREE_MERGE_AUTO == w4::kTreeMergeAuto && W4_TREE_MERGE_LAUNCH == w4::kTreeMergeLaunch &&
+                  W4_TREE_MERGE_LAST == w4::kTreeMergeLast,
+              "merge choices");
+
+extern "C" int w4_tree_attention_plan(int M, int L, int num_heads, int num_kv_heads, int merge, int* splits,
+                                      int* merge_used) {
+    if (M < 1 || L < 0 || num_heads <= 0 || num_kv_heads <= 0) return W4_ERR_INVALID;
+    if (merge < W4_TREE_MERGE_AUTO || merge > W4_TREE_MERGE_LAST) return W4_ERR_INVALID;
+    if (M > W4_TREE_MAX_M || L > W4_TREE_MAX_L || num_heads % num_kv_heads != 0 || num_heads > 256)
+        return W4_ERR_UNSUPPORTED;
+    int s = 0, used = 0;
+    if (w4::tree_attn_plan(M, L, num_heads, num_kv_heads, merge, &s, &used, nullptr) != 0) return W4_ERR_UNSUPPORTED;
+    if (splits) *splits = s;
+    if (merge_used) *merge_used = used;
+    return W4_OK;
+}
+
 extern "C" int w4_tree_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                                  const uint16_t* k_draft, const uint16_t* v_draft, const uint64_t* masks, int M,
                                  int L, int num_heads, int num_kv_heads, int head_dim, float scale, float* out,
                                  void* stream) {
+    return w4_tree_attention_ex(q, k_cache, v_cache, k_draft, v_draft, masks, M, L, num_heads, num_kv_heads,
+                                head_dim, scale, W4_TREE_MERGE_AUTO, out, stream);
+}
+
+extern "C" int w4_tree_attention_ex(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                                    const uint16_t* k_draft, const uint16_t* v_draft, const uint64_t* masks, int M,
+                                    int L, int num_heads, int num_kv_heads, int head_dim, float scale, int merge,
+                                    float* out, void* stream) {
     if (M < 0 || L < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return W4_ERR_INVALID;
+    if (merge < W4_TREE_MERGE_AUTO || merge > W4_TREE_MERGE_LAST) return W4_ERR_INVALID;
     if (!(scale >= 0.0f) || scale > 1e30f) return W4_ERR_INVALID;  // rejects NaN
     if (head_dim != w4::kTreeHeadDim || M > W4_TREE_MAX_M || L > W4_TREE_MAX_L || num_heads % num_kv_heads != 0 ||
         num_heads > 256)
@@ -408,14 +442,15 @@ extern "C" int w4_tree_attention(const uint16_t* q, const uint16_t* k_cache, con
     if (overlap(out, ob, q, qb) || overlap(out, ob, k_cache, cb) || overlap(out, ob, v_cache, cb) ||
         overlap(out, ob, k_draft, db) || overlap(out, ob, v_draft, db) || overlap(out, ob, masks, (size_t)M * 8))
         return W4_ERR_INVALID;
-    if (w4::tree_attn_plan(M, L, num_heads, num_kv_heads, nullptr, nullptr) != 0) return W4_ERR_UNSUPPORTED;
+    if (w4::tree_attn_plan(M, L, num_heads, num_kv_heads, merge, nullptr, nullptr, nullptr) != 0)
+        return W4_ERR_UNSUPPORTED;
     float* ws = nullptr;
     int rc = device_state(nullptr, nullptr, &ws);
     if (rc != W4_OK) return rc;
     const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)head_dim);
     return hip_status("tree attention launch",
                       w4::launch_tree_attn(q, k_cache, v_cache, k_draft, v_draft, masks, M, L, num_heads,
-                                           num_kv_heads, sc, out, ws, (hipStream_t)stream));
+                                           num_kv_heads, sc, merge, out, ws, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------

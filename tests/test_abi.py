@@ -294,6 +294,54 @@ def test_tree_attention_argument_errors():
             call(**kw)
         assert e.value.status == code, kw
     assert call(M=0) is None  # nothing to do: no launch, no error
+    # the merge choice of the _ex form: anything but AUTO, LAUNCH or LAST is
+    # refused (also when there is nothing to do)
+    for merge in (-1, 3, 1 << 20):
+        with pytest.raises(w4.W4Error) as e:
+            w4.w4_tree_attention_ex(a["q"], a["kc"], a["vc"], a["kd"], a["vd"], a["m"], 0, 64, 64, 8, 128, 0.0, merge,
+                                    a["out"], stream=0)
+        assert e.value.status == w4.W4_ERR_INVALID, merge
+    assert w4.w4_tree_attention_ex(a["q"], a["kc"], a["vc"], a["kd"], a["vd"], a["m"], 0, 64, 64, 8, 128, 0.0,
+                                   w4.TREE_MERGE_LAST, a["out"], stream=0) is None
+
+
+def test_tree_attention_plan():
+    # Llama-3-70B heads over a 4096-position prefix: the key splits each
+    # draft size uses, merged by a second launch by default; either merge can
+    # be asked for
+    for M, splits in ((1, 33), (5, 22), (64, 8)):
+        assert w4.w4_tree_attention_plan(M, 4096, 64, 8) == (splits, w4.TREE_MERGE_LAUNCH), M
+        for merge in (w4.TREE_MERGE_LAUNCH, w4.TREE_MERGE_LAST):
+            assert w4.w4_tree_attention_plan(M, 4096, 64, 8, merge) == (splits, merge)
+    # the default merges in the last workgroup where a tile (at most 16 rows)
+    # holds at most 72 KiB of partial rows (130 floats each per split)
+    for M, L, Hq, Hkv in ((1, 128, 64, 8), (1, 1024, 64, 8), (1, 2048, 64, 8), (2, 512, 64, 8), (2, 1024, 64, 8),
+                          (3, 512, 64, 8), (16, 300, 16, 16), (16, 1000, 16, 16), (1, 100000, 8, 8)):
+        splits, used = w4.w4_tree_attention_plan(M, L, Hq, Hkv)
+        rows = M * Hq // Hkv
+        small = rows <= 16 and splits * rows * 130 * 4 <= 72 << 10
+        assert splits > 1 and used == (w4.TREE_MERGE_LAST if small else w4.TREE_MERGE_LAUNCH), (M, L, splits, used)
+    assert w4.w4_tree_attention_plan(1, 2048, 64, 8)[1] == w4.TREE_MERGE_LAST
+    assert w4.w4_tree_attention_plan(2, 1024, 64, 8)[1] == w4.TREE_MERGE_LAUNCH
+    assert w4.w4_tree_attention_plan(1, 4096, 64, 8)[1] == w4.TREE_MERGE_LAUNCH
+    # a single 64-key chunk: one split, nothing to merge
+    for merge in (w4.TREE_MERGE_AUTO, w4.TREE_MERGE_LAUNCH, w4.TREE_MERGE_LAST):
+        assert w4.w4_tree_attention_plan(3, 20, 64, 8, merge) == (1, w4.TREE_MERGE_AUTO)
+    # the extremes of the limits plan (at most 64 splits; every tile has its
+    # arrival counter)
+    for M, L, Hq, Hkv in ((64, 1 << 20, 256, 1), (64, 1 << 20, 256, 256), (1, 1 << 20, 256, 256),
+                          (64, 0, 256, 1), (1, 1, 1, 1), (17, 100000, 64, 8)):
+        splits, used = w4.w4_tree_attention_plan(M, L, Hq, Hkv)
+        assert 1 <= splits <= 64 and (used != w4.TREE_MERGE_AUTO) == (splits > 1)
+    for args, code in (((0, 64, 64, 8), w4.W4_ERR_INVALID), ((65, 64, 64, 8), w4.W4_ERR_UNSUPPORTED),
+                       ((1, (1 << 20) + 1, 64, 8), w4.W4_ERR_UNSUPPORTED), ((1, 64, 60, 8), w4.W4_ERR_UNSUPPORTED),
+                       ((1, 64, 512, 8), w4.W4_ERR_UNSUPPORTED), ((1, -1, 64, 8), w4.W4_ERR_INVALID)):
+        with pytest.raises(w4.W4Error) as e:
+            w4.w4_tree_attention_plan(*args)
+        assert e.value.status == code, args
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_tree_attention_plan(1, 64, 64, 8, 7)
+    assert e.value.status == w4.W4_ERR_INVALID
 
 
 def test_size_limits():

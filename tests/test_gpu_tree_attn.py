@@ -9,9 +9,11 @@ probabilities to bf16 for the value product, so each output must lie within
 the page's A -> B, C, D tree; prefixes that end inside a 64-key chunk and on
 its edge; the Llama-3-70B grouping (64 query heads over 8 key/value heads)
 and other groupings; a token that sees nothing; one key split and the most
-splits (M = 1 over 4096 and 12288 keys); repeatability, also with calls of
-other shapes in between (the key splits' partial results share one
-workspace, merged by a second launch), and under HIP graph replays.
+splits (M = 1 over 4096 and 12288 keys); both ways of merging the key
+splits (a second launch; the last workgroup of each row tile, counted in on
+an arrival counter that it sets back to zero); repeatability, also with
+calls of other shapes and the other merge in between (the partial results
+and the counters share one workspace), and under HIP graph replays.
 """
 import numpy as np
 import pytest
@@ -35,7 +37,10 @@ def _bf16(rng, shape, sigma=1.0):
     return bits, (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def _case(seed, M, L, Hq, Hkv, parents, sigma_q=1.0):
+MERGES = (w4.TREE_MERGE_LAUNCH, w4.TREE_MERGE_LAST)
+
+
+def _case(seed, M, L, Hq, Hkv, parents, sigma_q=1.0, merge=w4.TREE_MERGE_AUTO):
     rng = np.random.default_rng(seed)
     D = 128
     qb, q = _bf16(rng, (M, Hq, D), sigma_q)
@@ -46,7 +51,7 @@ def _case(seed, M, L, Hq, Hkv, parents, sigma_q=1.0):
     masks = ancestor_masks(parents) if parents is not None else np.zeros(M, np.uint64)
     dev = lambda b: torch.from_numpy(b.view(np.int16)).to(DEV)
     out = w4.tree_attention(dev(qb), dev(kcb), dev(vcb), dev(kdb), dev(vdb),
-                            torch.from_numpy(masks.view(np.int64)).to(DEV))
+                            torch.from_numpy(masks.view(np.int64)).to(DEV), merge=merge)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), (q, kc, vc, kd, vd, masks)
 
@@ -64,23 +69,40 @@ def _random_tree(rng, M):
     return [-1] + [int(rng.integers(-1, i)) for i in range(1, M)]
 
 
+@pytest.mark.parametrize("merge", MERGES)
 @pytest.mark.parametrize("M,L,kind", [(1, 0, "chain"), (1, 200, "chain"), (5, 100, "chain"), (5, 128, "star"),
                                       (4, 61, "page"), (16, 1000, "tree"), (64, 64, "chain"), (64, 1000, "tree"),
                                       (64, 4096, "tree"), (1, 4096, "chain"), (8, 2047, "tree"),
-                                      (2, 64 * 64 * 3, "chain"), (1, 1500, "chain")])
-def test_tree_attention_matches_the_oracle(M, L, kind):
+                                      (2, 64 * 64 * 3, "chain"), (1, 1500, "chain"), (17, 3000, "tree"),
+                                      (5, 4096, "chain")])
+def test_tree_attention_matches_the_oracle(M, L, kind, merge):
     rng = np.random.default_rng(M * 1000 + L)
     parents = {"chain": list(range(-1, M - 1)), "star": [-1] * M, "page": [-1, 0, 0, 0],
                "tree": _random_tree(rng, M)}[kind]
-    got, args = _case(M + L, M, L, 64, 8, parents)
-    _check(got, args, (M, L, kind))
+    got, args = _case(M + L, M, L, 64, 8, parents, merge=merge)
+    _check(got, args, (M, L, kind, merge))
 
 
+@pytest.mark.parametrize("merge", MERGES)
 @pytest.mark.parametrize("Hq,Hkv", [(16, 16), (32, 4), (8, 1)])
-def test_other_head_groupings(Hq, Hkv):
+def test_other_head_groupings(Hq, Hkv, merge):
     rng = np.random.default_rng(Hq + Hkv)
-    got, args = _case(7, 9, 150, Hq, Hkv, _random_tree(rng, 9))
-    _check(got, args, (Hq, Hkv))
+    got, args = _case(7, 9, 150, Hq, Hkv, _random_tree(rng, 9), merge=merge)
+    _check(got, args, (Hq, Hkv, merge))
+
+
+@pytest.mark.parametrize("M,L", [(1, 1024), (1, 4096), (2, 500), (5, 4096)])
+def test_the_default_merge_matches_the_forced_one(M, L):
+    # the default takes the merge the plan names (the last workgroup for
+    # small tiles, a second launch otherwise): bit for bit the same output
+    splits, used = w4.w4_tree_attention_plan(M, L, 64, 8)
+    assert splits > 1 and used in MERGES
+    a, args = _case(30 + M, M, L, 64, 8, list(range(-1, M - 1)))
+    b, _ = _case(30 + M, M, L, 64, 8, list(range(-1, M - 1)), merge=used)
+    assert np.array_equal(a, b), (M, L, used)
+    _check(a, args, (M, L, "default"))
+    # one split: nothing to merge
+    assert w4.w4_tree_attention_plan(1, 0, 64, 8) == (1, w4.TREE_MERGE_AUTO)
 
 
 def test_peaked_scores_and_unseen_tokens():
@@ -98,21 +120,28 @@ def test_repeatable():
     assert np.array_equal(a, b)
 
 
-def test_repeatable_across_shapes():
-    # the key splits' partial results go through one shared workspace and
-    # are merged by a second launch; calls of other shapes in between (other
-    # split counts and workspace extents) must not change the next result
-    a, _ = _case(11, 1, 4096, 64, 8, [-1])
-    _case(12, 64, 1000, 64, 8, list(range(-1, 63)))
-    _case(13, 3, 30, 64, 8, [-1, 0, 1])
-    b, args = _case(11, 1, 4096, 64, 8, [-1])
+@pytest.mark.parametrize("merge", MERGES)
+def test_repeatable_across_shapes(merge):
+    # the key splits' partial results and the arrival counters go through
+    # one shared workspace; calls of other shapes and of the other merge in
+    # between (other split counts, tile counts and workspace extents) must
+    # not change the next result: every call leaves the counters at zero
+    other = MERGES[1 - MERGES.index(merge)]
+    a, _ = _case(11, 1, 4096, 64, 8, [-1], merge=merge)
+    _case(12, 64, 1000, 64, 8, list(range(-1, 63)), merge=other)
+    _case(13, 3, 30, 64, 8, [-1, 0, 1], merge=merge)
+    _case(14, 64, 4096, 64, 8, list(range(-1, 63)), merge=merge)
+    _case(15, 17, 3000, 64, 8, list(range(-1, 16)), merge=other)
+    b, args = _case(11, 1, 4096, 64, 8, [-1], merge=merge)
     assert np.array_equal(a, b)
-    _check(b, args, "after other shapes")
+    _check(b, args, ("after other shapes", merge))
 
 
-def test_graph_replays_merge_every_time():
-    # a captured call (the split kernel, then the merge launch) replays
-    # correctly, also with the query changed between replays
+@pytest.mark.parametrize("merge", MERGES)
+def test_graph_replays_merge_every_time(merge):
+    # a captured call (the split kernel and the merge launch, or the split
+    # kernel alone with its arrival counters) replays correctly, also with
+    # the query changed between replays
     M, L, Hq, Hkv = 1, 4096, 64, 8
     rng = np.random.default_rng(4242)
     D = 128
@@ -130,16 +159,18 @@ def test_graph_replays_merge_every_time():
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        w4.tree_attention(qd, *tens, out=out, stream=s)
+        w4.tree_attention(qd, *tens, out=out, stream=s, merge=merge)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        w4.tree_attention(qd, *tens, out=out)
+        w4.tree_attention(qd, *tens, out=out, merge=merge)
     for rep in range(3):
         qb, q = _bf16(rng, (M, Hq, D))
         qd.copy_(dev(qb))
         out.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
-        _check(out.cpu().numpy().astype(np.float64), (q, kc, vc, kd, vd, masks), ("graph replay", rep))
+        _check(out.cpu().numpy().astype(np.float64), (q, kc, vc, kd, vd, masks), ("graph replay", rep, merge))
+        # an eager call of another shape between replays
+        _case(20 + rep, 5, 700, 64, 8, list(range(-1, 4)), merge=merge)
