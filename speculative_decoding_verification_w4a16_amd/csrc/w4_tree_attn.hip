@@ -64,6 +64,8 @@ namespace {
 
 constexpr int kHd = kTreeHeadDim;              // 128
 constexpr int kChunk = 64;                     // keys per chunk
+constexpr int kKT = kChunk / 16;               // 16-key score tiles per chunk
+constexpr int kKP = kChunk / 32;               // 32-key value-product steps per chunk
 constexpr int kKPitch = kHd * 2 + 16;          // bytes per key row of the K copy
 constexpr int kKBytes = kChunk * kKPitch;      // one chunk's K copy
 constexpr int kVtPitch = kChunk * 2 + 8;       // bytes per head-dim column of the V copy
@@ -218,10 +220,10 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(TreeArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     // Chunk loads: thread (lt, lq) = (tid / 16, tid % 16) fetches head-dim octet
-    // lq of keys lt + 4W r (r < 16/W) and of the value key pairs lt + 4W i
-    // (i < 8/W).
+    // lq of keys lt + 4W r (r < kChunk/4W) and of the value key pairs lt + 4W i
+    // (i < kChunk/8W).
     static_assert(W == 4 || W == 8, "4 or 8 waves per workgroup");
-    constexpr int KI = 16 / W, VI = 8 / W, TS = 4 * W;  // TS: thread rows (lt) per workgroup
+    constexpr int KI = kChunk / (4 * W), VI = kChunk / (8 * W), TS = 4 * W;  // TS: thread rows (lt) per workgroup
     const int lt = tid >> 4, lq = tid & 15;
     struct ChunkRegs {
         u32x4 k[KI], v[2 * VI];  // v[2i], v[2i+1]: keys 2(lt + TS i) and 2(lt + TS i) + 1
@@ -294,10 +296,10 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(TreeArgs a) {
     auto compute = [&](int b, int c) {
         const char* buf = smem + b * kBufBytes;
         const int key0 = c * kChunk;
-        // scores of the chunk's four 16-key tiles
-        f32x4 s[4];
+        // scores of the chunk's 16-key tiles
+        f32x4 s[kKT];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < kKT; ++kt) {
             f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -312,19 +314,19 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(TreeArgs a) {
             // every key is a prefix position: all visible, all finite
             float cm = s[0][0];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) cm = fmaxf(cm, s[kt][r]);
             m_new = fmaxf(m_run, row_max(cm) * a.c);
             alpha = exp2_hw(m_run - m_new);
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) s[kt][r] = exp2_hw(fmaf(s[kt][r], a.c, -m_new));
         } else {
             float cm = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = key0 + 16 * kt + 4 * o + r;
@@ -338,14 +340,14 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(TreeArgs a) {
             const bool none = m_new == -INFINITY;  // nothing visible to this row yet
             alpha = none ? 1.0f : exp2_hw(m_run - m_new);
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) s[kt][r] = none ? 0.0f : exp2_hw(s[kt][r] - m_new);
         }
         // the lane's share of the row sum (the four shares are added at the end)
         float ls = 0.0f;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) ls += s[kt][r];
         l_run = l_run * alpha + ls;
@@ -354,9 +356,9 @@ __global__ __launch_bounds__(64 * W) void tree_attn_kernel(TreeArgs a) {
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
         }
-        // O^T += V^T P^T over the chunk's two 32-key halves
+        // O^T += V^T P^T over the chunk's 32-key steps
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
+        for (int kp = 0; kp < kKP; ++kp) {
             bf16x8 pb;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
