@@ -1,7 +1,8 @@
 """The boundary is a C ABI: a C99 program that includes every public header
 compiles with -Wall -Wextra -Werror, links against the in-tree libw4a16.so
-and runs the calls that need no GPU (byte sizes, launch plans, status
-strings, argument errors returned before any HIP call).  The same headers
+and runs the calls that need no GPU (byte sizes, launch plans of the linear
+and of tree attention, status strings, argument errors returned before any
+HIP call).  The same headers
 also compile as C++ (-std=c++17)."""
 import os
 import shutil
@@ -49,6 +50,18 @@ int main(void) {
     if (w4a16_linear(NULL, qt, st, zt, 4, 256, 512, 128, y, NULL) != W4_ERR_INVALID) return 9;
     if (w4a16_linear(x, qt, st, zt, 0, 256, 512, 128, y, NULL) != W4_OK) return 10; /* nothing to do */
     if (strlen(w4_status_str(W4_ERR_INVALID)) == 0 || strlen(w4_status_str(W4_ERR_HIP)) == 0) return 11;
+    /* tree attention: the split count and merge a shape uses, host only */
+    int tsplits = 0, tmerge = -1;
+    if (w4_tree_attention_plan(1, 4096, 64, 8, W4_TREE_MERGE_AUTO, &tsplits, &tmerge) != W4_OK || tsplits < 2 ||
+        tmerge != W4_TREE_MERGE_LAUNCH)
+        return 12;
+    if (w4_tree_attention_plan(1, 512, 64, 8, W4_TREE_MERGE_AUTO, NULL, &tmerge) != W4_OK ||
+        tmerge != W4_TREE_MERGE_LAST)
+        return 13;
+    if (w4_tree_attention_plan(1, 64, 64, 8, 3, NULL, NULL) != W4_ERR_INVALID) return 14;
+    if (w4_tree_attention_ex(NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 64, 8, 128, 0.0f, -1, NULL, NULL) !=
+        W4_ERR_INVALID)
+        return 15;
     printf("ok %zu %d %d %d\n", qb, splits, grid, block);
     return 0;
 }
