@@ -174,3 +174,46 @@ def test_graph_replays_merge_every_time(merge):
         _check(out.cpu().numpy().astype(np.float64), (q, kc, vc, kd, vd, masks), ("graph replay", rep, merge))
         # an eager call of another shape between replays
         _case(20 + rep, 5, 700, 64, 8, list(range(-1, 4)), merge=merge)
+
+
+def test_interleaved_graph_replays_of_shapes_sharing_the_counters():
+    # three captured calls of different shapes -- two merged in the last
+    # workgroup of each tile (different tile and split counts), one by a
+    # second launch -- replayed interleaved: each replay must match the
+    # oracle, so no call leaves an arrival counter another one reads
+    shapes = [(1, 1024), (2, 500), (64, 1000)]
+    D, Hq, Hkv = 128, 64, 8
+    rng = np.random.default_rng(777)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).to(DEV)
+    cases = []
+    for M, L in shapes:
+        qb, q = _bf16(rng, (M, Hq, D))
+        kcb, kc = _bf16(rng, (L, Hkv, D))
+        vcb, vc = _bf16(rng, (L, Hkv, D))
+        kdb, kd = _bf16(rng, (M, Hkv, D))
+        vdb, vd = _bf16(rng, (M, Hkv, D))
+        masks = ancestor_masks(_random_tree(rng, M))
+        tens = [dev(qb), dev(kcb), dev(vcb), dev(kdb), dev(vdb), torch.from_numpy(masks.view(np.int64)).to(DEV)]
+        out = torch.empty((M, Hq, D), dtype=torch.float32, device=DEV)
+        cases.append((tens, out, (q, kc, vc, kd, vd, masks)))
+    used = [w4.w4_tree_attention_plan(M, L, Hq, Hkv)[1] for M, L in shapes]
+    assert used == [w4.TREE_MERGE_LAST, w4.TREE_MERGE_LAST, w4.TREE_MERGE_LAUNCH], used
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for tens, out, _ in cases:
+            w4.tree_attention(*tens, out=out, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for tens, out, _ in cases:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            w4.tree_attention(*tens, out=out)
+        graphs.append(g)
+    for step, i in enumerate([0, 1, 2, 0, 1, 0, 2, 1]):
+        tens, out, args = cases[i]
+        out.fill_(float("nan"))
+        graphs[i].replay()
+        torch.cuda.synchronize()
+        _check(out.cpu().numpy().astype(np.float64), args, ("interleaved replay", step, shapes[i]))
