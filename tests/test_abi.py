@@ -475,3 +475,32 @@ def test_pass_validation_scales_to_large_passes():
                      zt=W + (n - 1) * 0x10_0000 + 0xC_0000)
     assert w4._c["w4_pass_create"](arr, n, M, 128, ctypes.byref(out)) == w4.W4_ERR_INVALID
 
+
+
+def test_random_tree_plans_keep_their_invariants():
+    # seeded sweep over the limits: 1..64 splits, never more than the 64-key
+    # chunks, the partial results and arrival counters inside the 48 MiB
+    # workspace, and the merge the default picks follows its stated rule
+    # (last workgroup only for tiles of at most 16 rows and 72 KiB of partials)
+    rng = __import__("numpy").random.default_rng(2024)
+    for _ in range(3000):
+        M = int(rng.integers(1, 65))
+        L = int(rng.choice([0, 1, 63, 64, 65, 500, 4096, 100000, 1 << 20]) if rng.random() < 0.3
+                else rng.integers(0, 1 << 17))
+        Hkv = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256]))
+        Hq = Hkv * int(rng.choice([g for g in (1, 2, 4, 8, 16, 32, 64, 128, 256) if Hkv * g <= 256]))
+        splits, used = w4.w4_tree_attention_plan(M, L, Hq, Hkv)
+        chunks = -(-(L + M) // 64)
+        assert 1 <= splits <= min(64, chunks), (M, L, Hq, Hkv, splits)
+        R = M * Hq // Hkv
+        rows = 64 if R <= 16 else 128
+        tiles = -(-R // rows) * Hkv
+        assert tiles * 4 <= 4096, (M, Hq, Hkv)
+        if splits > 1:
+            assert 4096 + splits * Hkv * R * 130 * 4 <= 48 << 20, (M, L, Hq, Hkv, splits)
+            small = R <= 16 and splits * min(R, rows) * 130 * 4 <= 72 << 10
+            assert used == (w4.TREE_MERGE_LAST if small else w4.TREE_MERGE_LAUNCH), (M, L, Hq, Hkv, splits, used)
+            for m in (w4.TREE_MERGE_LAUNCH, w4.TREE_MERGE_LAST):
+                assert w4.w4_tree_attention_plan(M, L, Hq, Hkv, m) == (splits, m)
+        else:
+            assert used == w4.TREE_MERGE_AUTO
