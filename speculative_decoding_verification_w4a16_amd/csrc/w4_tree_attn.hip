@@ -522,6 +522,7 @@ size_t partial_bytes(int nsplit, int Hkv, int R) { return (size_t)nsplit * Hkv *
 int tree_waves(int R) { return R > 16 ? 8 : 4; }
 
 constexpr size_t kFusedMergeBytes = 72 << 10;  // default limit of a tile's partials for the in-kernel merge
+constexpr long long kOneChunkMaxWgs = 288;       // most workgroups of four-wave tiles at one chunk per split
 
 }  // namespace
 
@@ -535,9 +536,13 @@ int tree_attn_plan(int M, int L, int Hq, int Hkv, int merge, int* nsplit_out, in
     // (registers).  Chunks per split: at least two (a workgroup overlaps a
     // chunk's loads with the previous chunk's work), else the fewest that
     // keep to one such round; then at most kTreeMaxSplits splits and what
-    // the workspace holds
+    // the workspace holds.  Four-wave tiles take one chunk per split while
+    // that keeps to about one workgroup per CU (measured with 64 query heads
+    // over 8, M = 1 and 2: 0.5-0.9 us faster up to L = 2048, where it makes
+    // 264 workgroups; at L = 4096, 520 workgroups, 2 us slower).
     const long long slots = W == 4 ? 512 : 256;
-    const int cps = std::max(2, (int)(((long long)nchunks * tiles + slots - 1) / slots));
+    const int cps_min = W == 4 && (long long)nchunks * tiles <= kOneChunkMaxWgs ? 1 : 2;
+    const int cps = std::max(cps_min, (int)(((long long)nchunks * tiles + slots - 1) / slots));
     int nsplit = std::max(1, std::min(kTreeMaxSplits, (nchunks + cps - 1) / cps));
     while (nsplit > 1 && kTreeCounterBytes + partial_bytes(nsplit, Hkv, R) > kTreeWorkspaceBytes) --nsplit;
     if ((size_t)tiles * sizeof(uint32_t) > kTreeCounterBytes) return -1;
@@ -548,8 +553,9 @@ int tree_attn_plan(int M, int L, int Hq, int Hkv, int merge, int* nsplit_out, in
     // one CU, at 20-30 GB/s; a second launch costs 4.5-7 us but spreads the
     // merge over the chip.  By default the last workgroup merges only
     // four-wave tiles (at most 16 rows) whose partials come to 72 KiB at
-    // most (measured with 64 query heads over 8: M = 1 and L up to 2048, M = 2
-    // and L up to 512: 0.2-1.4 us per call faster, slower everywhere else).
+    // most (measured with 64 query heads over 8 on these plans: M = 1 and L up
+    // to 1024, M = 2 and L up to 256: 0.4-1.4 us per call faster, slower
+    // everywhere else).
     int used = kTreeMergeAuto;
     if (nsplit > 1) {
         const size_t tile_bytes = (size_t)nsplit * std::min(R, rows_wg) * (kHd + 2) * sizeof(float);

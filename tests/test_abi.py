@@ -321,7 +321,8 @@ def test_tree_attention_plan():
         rows = M * Hq // Hkv
         small = rows <= 16 and splits * rows * 130 * 4 <= 72 << 10
         assert splits > 1 and used == (w4.TREE_MERGE_LAST if small else w4.TREE_MERGE_LAUNCH), (M, L, splits, used)
-    assert w4.w4_tree_attention_plan(1, 2048, 64, 8)[1] == w4.TREE_MERGE_LAST
+    assert w4.w4_tree_attention_plan(1, 1024, 64, 8) == (17, w4.TREE_MERGE_LAST)
+    assert w4.w4_tree_attention_plan(1, 2048, 64, 8) == (33, w4.TREE_MERGE_LAUNCH)
     assert w4.w4_tree_attention_plan(2, 1024, 64, 8)[1] == w4.TREE_MERGE_LAUNCH
     assert w4.w4_tree_attention_plan(1, 4096, 64, 8)[1] == w4.TREE_MERGE_LAUNCH
     # a single 64-key chunk: one split, nothing to merge
@@ -496,6 +497,8 @@ def test_random_tree_plans_keep_their_invariants():
         rows = 64 if R <= 16 else 128
         tiles = -(-R // rows) * Hkv
         assert tiles * 4 <= 4096, (M, Hq, Hkv)
+        if R <= 16 and chunks * tiles <= 288 and 4096 + min(64, chunks) * Hkv * R * 520 <= 48 << 20:
+            assert splits == min(64, chunks), (M, L, Hq, Hkv, splits)  # one chunk per split
         if splits > 1:
             assert 4096 + splits * Hkv * R * 130 * 4 <= 48 << 20, (M, L, Hq, Hkv, splits)
             small = R <= 16 and splits * min(R, rows) * 130 * 4 <= 72 << 10
