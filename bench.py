@@ -104,6 +104,8 @@ def parse():
     p.add_argument("--m", default="1,2,4,5,8,16,32,48,64", help="M grid for --shapes")
     p.add_argument("--names", default="q,k,v,o,gate,up,down,lm_head", help="linears for --shapes")
     p.add_argument("--splits", type=int, default=0, help="force the K split count in --shapes (0 = planner)")
+    p.add_argument("--kernel", choices=("auto", "gemv", "mfma"), default="auto",
+                   help="force the kernel in --shapes (auto = planner; gemv only at M = 1)")
     p.add_argument("--kwaves", type=int, default=0,
                    help="force the waves splitting a chunk's K range in --shapes (0 = planner; M <= 16)")
     p.add_argument("--rotate-gib", type=float, default=2.0)
@@ -984,15 +986,16 @@ def shapes_report(args):
                            for _ in range(R - 1)]
         x = torch.from_numpy(synth.gen_x(max(Ms), K).view(np.int16)).to(dev)
         y = torch.empty((max(Ms), N), dtype=torch.float32, device=dev)
+        kern = {"auto": w4.W4_KERNEL_AUTO, "gemv": w4.W4_KERNEL_GEMV, "mfma": w4.W4_KERNEL_MFMA}[args.kernel]
         for M in Ms:
-            plan = w4.w4a16_plan(M, N, K, splits=args.splits, kwaves=args.kwaves)
+            plan = w4.w4a16_plan(M, N, K, kernel=kern, splits=args.splits, kwaves=args.kwaves)
             for pk in copies[:2]:
-                w4.linear(x[:M], pk, y=y[:M], splits=args.splits, kwaves=args.kwaves)
+                w4.linear(x[:M], pk, y=y[:M], kernel=kern, splits=args.splits, kwaves=args.kwaves)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for pk in copies:
-                    w4.linear(x[:M], pk, y=y[:M], splits=args.splits, kwaves=args.kwaves)
+                    w4.linear(x[:M], pk, y=y[:M], kernel=kern, splits=args.splits, kwaves=args.kwaves)
             g.replay()
             torch.cuda.synchronize()
             # 20 repeats of at least 200 calls each; the figure is the median
